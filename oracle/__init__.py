@@ -1,0 +1,160 @@
+"""CPU oracle for the fused GEMM + ReLU — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU product path
+(``dense_tiled_gemm_relu_amd``) never imports it, and the two share no code.
+
+The operation (page "TileLang：GPU/NPU 通用算子 DSL", §3.2 GPU minimal example;
+§3.3 for the (N,K)-stored B with transpose_B and the fp32 output):
+
+    ref[i, j] = max( sum_k a(i, k) * b(k, j), 0 )
+
+computed in binary64 from the exact values of the 16-bit inputs.  Two
+independent implementations live here:
+
+* ``gemm_relu_ref`` / ``gemm_relu_ref_at`` — a plain C triple loop
+  (``oracle.c``) with its own binary16 / bfloat16 decoders, OpenMP over rows;
+* ``gemm_relu_fraction`` — exact rational arithmetic in pure Python
+  (``fractions.Fraction``), for tiny shapes only; it decodes through numpy's
+  float16 and a bit shift for bfloat16, so it shares no decoder with the C code.
+
+Inputs are 16-bit storage patterns (numpy ``uint16`` arrays); outputs are
+binary64 numpy arrays.
+"""
+import ctypes
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from . import build as _build
+
+F16 = 0
+BF16 = 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB)
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    i64 = ctypes.c_int64
+    lib.oracle_dec_f16.argtypes = [ctypes.c_uint16]
+    lib.oracle_dec_f16.restype = ctypes.c_double
+    lib.oracle_dec_bf16.argtypes = [ctypes.c_uint16]
+    lib.oracle_dec_bf16.restype = ctypes.c_double
+    lib.oracle_decode.argtypes = [u16p, f64p, i64, ctypes.c_int]
+    lib.oracle_decode.restype = None
+    lib.oracle_gemm_relu_f64.argtypes = [u16p, u16p, f64p, i64, i64, i64,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.oracle_gemm_relu_f64.restype = ctypes.c_int
+    lib.oracle_gemm_relu_f64_at.argtypes = [u16p, u16p, i64p, i64p, i64, f64p, f64p,
+                                            i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int]
+    lib.oracle_gemm_relu_f64_at.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _u16(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError("oracle inputs are uint16 storage patterns, got %s" % x.dtype)
+    return x
+
+
+def _ptr(x, ctype):
+    return x.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def decode(bits, dtype):
+    """Exact binary64 values of 16-bit patterns (C decoder)."""
+    lib = _load()
+    bits = _u16(bits)
+    out = np.empty(bits.shape, dtype=np.float64)
+    lib.oracle_decode(_ptr(bits, ctypes.c_uint16), _ptr(out, ctypes.c_double),
+                      bits.size, dtype)
+    return out
+
+
+def gemm_relu_ref(A, B, M, N, K, dtype, transB=0, relu=True, threads=0,
+                  return_threads=False):
+    """ref = max(A·op(B), 0) in binary64, shape (M, N).
+
+    A holds M*K patterns (row-major (M,K)); B holds K*N patterns, row-major
+    (K,N) if transB == 0, (N,K) if transB == 1.
+    """
+    lib = _load()
+    A = _u16(A).reshape(-1)
+    B = _u16(B).reshape(-1)
+    if A.size != M * K or B.size != K * N:
+        raise ValueError("operand sizes do not match M, N, K")
+    C = np.empty((M, N), dtype=np.float64)
+    used = ctypes.c_int(0)
+    rc = lib.oracle_gemm_relu_f64(_ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16),
+                                  _ptr(C, ctypes.c_double), M, N, K, dtype, int(transB),
+                                  1 if relu else 0, threads, ctypes.byref(used))
+    if rc != 0:
+        raise ValueError("oracle_gemm_relu_f64 failed (%d)" % rc)
+    return (C, used.value) if return_threads else C
+
+
+def gemm_relu_ref_at(A, B, rows, cols, M, N, K, dtype, transB=0, relu=True):
+    """The same definition at positions (rows[t], cols[t]).
+
+    Returns (values, absum) where absum[t] = sum_k |a(i,k) b(k,j)|.
+    """
+    lib = _load()
+    A = _u16(A).reshape(-1)
+    B = _u16(B).reshape(-1)
+    if A.size != M * K or B.size != K * N:
+        raise ValueError("operand sizes do not match M, N, K")
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols differ in shape")
+    out = np.empty(rows.shape, dtype=np.float64)
+    absum = np.empty(rows.shape, dtype=np.float64)
+    rc = lib.oracle_gemm_relu_f64_at(_ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16),
+                                     _ptr(rows, ctypes.c_int64), _ptr(cols, ctypes.c_int64),
+                                     rows.size, _ptr(out, ctypes.c_double),
+                                     _ptr(absum, ctypes.c_double), M, N, K, dtype,
+                                     int(transB), 1 if relu else 0)
+    if rc != 0:
+        raise ValueError("oracle_gemm_relu_f64_at failed (%d)" % rc)
+    return out, absum
+
+
+def _exact(bits, dtype):
+    """Exact rational values of 16-bit patterns through numpy (not the C decoder)."""
+    bits = _u16(bits)
+    if dtype == F16:
+        vals = bits.view(np.float16).astype(np.float64)
+    else:
+        vals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return [Fraction(float(v)) for v in vals.reshape(-1)]
+
+
+def gemm_relu_fraction(A, B, M, N, K, dtype, transB=0, relu=True):
+    """Exact rational max(A·op(B), 0) as a nested list of Fractions (tiny shapes)."""
+    a = _exact(A, dtype)
+    b = _exact(B, dtype)
+    out = []
+    for i in range(M):
+        row = []
+        for j in range(N):
+            s = Fraction(0)
+            for k in range(K):
+                bk = b[j * K + k] if transB else b[k * N + j]
+                s += a[i * K + k] * bk
+            row.append(max(s, Fraction(0)) if relu else s)
+        out.append(row)
+    return out

@@ -1,0 +1,193 @@
+/*
+ * CPU oracle for the fused dense GEMM + ReLU — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of bench.py may
+ * load this library.  The GPU product path never calls it and shares no code,
+ * header, table or helper with it.
+ *
+ * What it computes (page "TileLang：GPU/NPU 通用算子 DSL", §3.2 GPU minimal
+ * example and §3.3 Ascend 950 version): an output tile accumulator is cleared,
+ * A·B (or A·Bᵀ when B is stored (N,K) and the gemm is told transpose_B) is
+ * accumulated over the whole K range, and every accumulator element is then
+ * replaced by max(x, 0) before it is written out.  The tiling, the pipelined
+ * K-loop and the layouts on those pages only reorder that sum, so this file
+ * writes the plain definition:
+ *
+ *     ref[i][j] = max( sum_{k<K} a(i,k) * b(k,j), 0 )
+ *
+ * in IEEE binary64, with a(i,k) = dec(A[i*K+k]) and b(k,j) = dec(B[k*N+j]),
+ * or dec(B[j*K+k]) when transB = 1.  The result stays binary64: no rounding to
+ * the storage type of C happens here.
+ *
+ * dec() turns a 16-bit storage pattern into its exact value.  binary16 and
+ * bfloat16 are decoded from their field definitions (sign, biased exponent,
+ * fraction; bfloat16 is the upper half of a binary32 pattern: 8 exponent bits,
+ * 7 fraction bits), not by reinterpreting bits through a hardware type.
+ *
+ * Readings where the pages are silent (listed with the others in the design
+ * notes): a negative sum maps to +0.0; K = 0 gives an empty sum, so every
+ * output is +0.0; M = 0 or N = 0 is a no-op.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F16 = 0, ORACLE_BF16 = 1 };
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_dec_f16(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);              /* subnormal: f * 2^-10 * 2^-14 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);  /* (1 + f/2^10) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits. */
+double oracle_dec_bf16(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 7) & 0xff;
+    int f = h & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);             /* subnormal: f * 2^-7 * 2^-126 */
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + f), e - 134);  /* (1 + f/2^7) * 2^(e-127) */
+    return sign ? -v : v;
+}
+
+static double dec(uint16_t h, int dtype)
+{
+    return dtype == ORACLE_F16 ? oracle_dec_f16(h) : oracle_dec_bf16(h);
+}
+
+void oracle_decode(const uint16_t* x, double* out, int64_t n, int dtype)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = dec(x[i], dtype);
+}
+
+static int bad_args(const void* A, const void* B, const void* C,
+                    int64_t M, int64_t N, int64_t K, int dtype, int transB)
+{
+    if (M < 0 || N < 0 || K < 0) return 1;
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return 1;
+    if (transB != 0 && transB != 1) return 1;
+    if ((M > 0 && K > 0 && !A) || (N > 0 && K > 0 && !B) || (M > 0 && N > 0 && !C)) return 1;
+    return 0;
+}
+
+/* b(k, j) as the definition indexes it. */
+static int64_t b_index(int64_t k, int64_t j, int64_t N, int64_t K, int transB)
+{
+    return transB ? j * K + k : k * N + j;
+}
+
+/*
+ * Full product.  C is (M, N) row-major binary64.  relu = 0 skips the max (a test
+ * mode used to pin the ReLU on its own).  threads = 0 lets OpenMP choose.
+ * Returns 0, or -1 on bad arguments.  *threads_used (if not NULL) receives the
+ * number of threads the row loop ran on.
+ */
+int oracle_gemm_relu_f64(const uint16_t* A, const uint16_t* B, double* C,
+                         int64_t M, int64_t N, int64_t K,
+                         int dtype, int transB, int relu, int threads,
+                         int* threads_used)
+{
+    if (bad_args(A, B, C, M, N, K, dtype, transB)) return -1;
+    if (threads_used) *threads_used = 1;
+    if (M == 0 || N == 0) return 0;
+
+    /* Decode both operands once: a(i,k) and b(k,j) are exact in binary64. */
+    double* Ad = (double*)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
+    double* Bd = (double*)malloc(sizeof(double) * (size_t)(K * N > 0 ? K * N : 1));
+    if (!Ad || !Bd) { free(Ad); free(Bd); return -2; }
+    oracle_decode(A, Ad, M * K, dtype);
+    oracle_decode(B, Bd, K * N, dtype);
+
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#endif
+    int used = 1;
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+        double* acc = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < M; ++i) {
+            for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
+            if (!transB) {
+                /* i-k-j: add a(i,k) * row k of B into the row accumulator. */
+                for (int64_t k = 0; k < K; ++k) {
+                    double a = Ad[i * K + k];
+                    const double* brow = Bd + k * N;
+                    for (int64_t j = 0; j < N; ++j) acc[j] += a * brow[j];
+                }
+            } else {
+                /* i-j: dot product of row i of A with row j of the (N,K) B. */
+                for (int64_t j = 0; j < N; ++j) {
+                    double s = 0.0;
+                    for (int64_t k = 0; k < K; ++k) s += Ad[i * K + k] * Bd[j * K + k];
+                    acc[j] = s;
+                }
+            }
+            for (int64_t j = 0; j < N; ++j) {
+                double x = acc[j];
+                C[i * N + j] = relu ? (x > 0.0 ? x : 0.0) : x;
+            }
+        }
+        free(acc);
+    }
+    if (threads_used) *threads_used = used;
+    free(Ad);
+    free(Bd);
+    return 0;
+}
+
+/*
+ * The same definition at n chosen output positions (rows[t], cols[t]), one dot
+ * product each, for full-size problems where the whole product is too slow.
+ * If absum is not NULL it also receives S = sum_k |a(i,k) * b(k,j)|, the scale
+ * of the floating-point summation error bound.
+ */
+int oracle_gemm_relu_f64_at(const uint16_t* A, const uint16_t* B,
+                            const int64_t* rows, const int64_t* cols, int64_t n,
+                            double* out, double* absum,
+                            int64_t M, int64_t N, int64_t K,
+                            int dtype, int transB, int relu)
+{
+    if (bad_args(A, B, out, M, N, K, dtype, transB) || n < 0 || (n > 0 && (!rows || !cols)))
+        return -1;
+    for (int64_t t = 0; t < n; ++t)
+        if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t i = rows[t], j = cols[t];
+        double s = 0.0, sa = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = dec(A[i * K + k], dtype) * dec(B[b_index(k, j, N, K, transB)], dtype);
+            s += p;
+            sa += fabs(p);
+        }
+        out[t] = relu ? (s > 0.0 ? s : 0.0) : s;
+        if (absum) absum[t] = sa;
+    }
+    return 0;
+}

@@ -1,0 +1,265 @@
+"""Pins of the CPU oracle against facts fixed outside it (no GPU).
+
+Every check here compares the oracle with something it does not compute
+itself: hand-worked fixtures, exact rational brute force, closed forms,
+algebraic identities and exhaustive decoder tables from numpy.  The operation
+is the fused GEMM + ReLU of page "TileLang：GPU/NPU 通用算子 DSL", §3.2 (GPU
+minimal example) and §3.3 (Ascend 950 version: B stored (N,K), transpose_B).
+"""
+import itertools
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests.helpers import read_golden
+
+F16, BF16 = oracle.F16, oracle.BF16
+
+
+def enc(vals, dtype):
+    return wl.encode(np.asarray(vals, dtype=np.float64), dtype)
+
+
+# ---------------------------------------------------------------- P1 decoders
+def test_decode_f16_exhaustive():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode(bits, F16)
+    want = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    # signs of zero survive decoding
+    assert np.signbit(got[0x8000]) and not np.signbit(got[0])
+
+
+def test_decode_bf16_exhaustive():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode(bits, BF16)
+    want = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+# ---------------------------------------------------------- hand-worked golden
+@pytest.mark.parametrize("name", ["handworked_f16_2x2x3.txt",
+                                  "handworked_bf16_transB_2x3x2.txt",
+                                  "handworked_f16_extremes_2x1x2.txt",
+                                  "handworked_f16_zero_k.txt"])
+def test_golden_handworked(name):
+    g = read_golden(name)
+    dtype = {"f16": F16, "bf16": BF16}[g["dtype"]]
+    M, N, K = g["M"], g["N"], g["K"]
+    A = enc([float(x) for r in g["A"] for x in r], dtype) if K else np.zeros(0, np.uint16)
+    B = enc([float(x) for r in g["B"] for x in r], dtype) if K else np.zeros(0, np.uint16)
+    # inputs must be exact in the 16-bit format, else the fixture is wrong
+    assert [Fraction(float(v)) for v in oracle.decode(A, dtype)] == \
+        [x for r in g["A"] for x in r]
+    C = oracle.gemm_relu_ref(A, B, M, N, K, dtype, g["transB"])
+    assert [[Fraction(float(v)) for v in row] for row in C] == g["C"]
+    Cf = oracle.gemm_relu_fraction(A, B, M, N, K, dtype, g["transB"])
+    assert Cf == g["C"]
+
+
+# -------------------------------------------------------------- P2 identities
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("transB", [0, 1])
+def test_identity_right(dtype, transB):
+    M, K = 5, 7
+    A = wl.uniform((M, K), 11, dtype)
+    I = enc(np.eye(K), dtype)            # symmetric, so (K,N) and (N,K) agree
+    C = oracle.gemm_relu_ref(A, I, M, K, K, dtype, transB)
+    a = oracle.decode(A, dtype)
+    assert np.array_equal(C, np.maximum(a, 0.0))
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_identity_left(dtype):
+    M, N = 6, 9
+    B = wl.uniform((M, N), 12, dtype)    # (K,N) with K = M
+    I = enc(np.eye(M), dtype)
+    C = oracle.gemm_relu_ref(I, B, M, N, M, dtype, 0)
+    assert np.array_equal(C, np.maximum(oracle.decode(B, dtype), 0.0))
+    # with B stored (N,K), A = I gives relu of B read column-wise
+    Bt = wl.uniform((N, M), 13, dtype)
+    C = oracle.gemm_relu_ref(I, Bt, M, N, M, dtype, 1)
+    assert np.array_equal(C, np.maximum(oracle.decode(Bt, dtype).T, 0.0))
+
+
+# ------------------------------------------------------------- P3 permutation
+@pytest.mark.parametrize("transB", [0, 1])
+def test_permutation(transB):
+    M, K = 4, 11
+    rng = np.random.default_rng(5)
+    pi = rng.permutation(K)
+    P = np.zeros((K, K))
+    P[np.arange(K), pi] = 1.0            # P[k, pi(k)] = 1: column pi(k) of C is column k of A
+    A = wl.uniform((M, K), 14, F16)
+    Bm = P.T if transB else P
+    C = oracle.gemm_relu_ref(A, enc(Bm, F16), M, K, K, F16, transB)
+    a = np.maximum(oracle.decode(A, F16), 0.0)
+    for k in range(K):
+        assert np.array_equal(C[:, pi[k]], a[:, k])
+
+
+# ------------------------------------------------------------ P4 closed forms
+@pytest.mark.parametrize("transB", [0, 1])
+def test_rank_one_closed_form(transB):
+    # A = u p^T, B = q v^T  =>  ref_ij = max((p.q) u_i v_j, 0)
+    u = [1, -2, 0.5, 3, -0.25]
+    p = [1, 2, -1, 0.5, 4, -3, 1.5]
+    q = [2, -1, 1, 0.25, -0.5, 1, 2]
+    v = [-1, 0.5, 2, -4, 1, 3]
+    M, K, N = len(u), len(p), len(v)
+    A = np.outer(u, p)
+    Bkn = np.outer(q, v)
+    B = Bkn.T if transB else Bkn
+    C = oracle.gemm_relu_ref(enc(A, F16), enc(B, F16), M, N, K, F16, transB)
+    pq = sum(Fraction(a) * Fraction(b) for a, b in zip(p, q))
+    for i in range(M):
+        for j in range(N):
+            want = max(pq * Fraction(u[i]) * Fraction(v[j]), Fraction(0))
+            assert Fraction(float(C[i, j])) == want
+
+
+@pytest.mark.parametrize("K", [1, 255, 256, 4096, 8192])
+def test_all_ones_gives_K(K):
+    M, N = 3, 5
+    A = enc(np.ones((M, K)), F16)
+    B = enc(np.ones((K, N)), F16)
+    C = oracle.gemm_relu_ref(A, B, M, N, K, F16, 0)
+    assert np.all(C == K)
+    Cn = oracle.gemm_relu_ref(enc(-np.ones((M, K)), F16), B, M, N, K, F16, 0)
+    assert np.all(Cn == 0.0) and not np.any(np.signbit(Cn))
+
+
+# ------------------------------------------------------------ P5 cancellation
+@pytest.mark.parametrize("K", [2, 64, 1000])
+def test_alternating_rows_cancel(K):
+    M, N = 4, 6
+    sign = np.where(np.arange(K) % 2 == 0, 1.0, -1.0)
+    a = np.outer([1.0, 0.5, 2.0, -3.0], sign)          # A_ik = a_i (-1)^k
+    b = np.outer(np.ones(K), [1.0, -2.0, 0.25, 4.0, 1.5, -1.0])   # B_kj = b_j
+    C = oracle.gemm_relu_ref(enc(a, F16), enc(b, F16), M, N, K, F16, 0)
+    assert np.all(C == 0.0)
+
+
+# -------------------------------------------------------------- P6 ReLU alone
+@pytest.mark.parametrize("transB", [0, 1])
+def test_relu_identities(transB):
+    M, N, K = 13, 17, 29
+    A, B = wl.make_inputs(M, N, K, F16, transB, "uniform", 77)
+    negA = A ^ np.uint16(0x8000)                        # -A by the sign bit
+    X = oracle.gemm_relu_ref(A, B, M, N, K, F16, transB, relu=False)
+    Rp = oracle.gemm_relu_ref(A, B, M, N, K, F16, transB)
+    Rn = oracle.gemm_relu_ref(negA, B, M, N, K, F16, transB)
+    assert np.array_equal(Rp - Rn, X)
+    assert np.array_equal(Rp + Rn, np.abs(X))
+    assert np.all(Rp >= 0) and np.all(Rn >= 0)
+    assert np.any(X < 0) and np.any(X > 0)
+
+
+# ----------------------------------------------------- P7 exact brute force
+def test_bruteforce_all_small_shapes():
+    rng = np.random.default_rng(2024)
+    grid = np.arange(-8, 9) / 4.0                      # exact in both formats
+    for M, N, K in itertools.product(range(1, 7), repeat=3):
+        for dtype, transB in ((F16, 0), (BF16, 1)):
+            A = enc(rng.choice(grid, size=M * K), dtype)
+            B = enc(rng.choice(grid, size=K * N), dtype)
+            C = oracle.gemm_relu_ref(A, B, M, N, K, dtype, transB)
+            want = oracle.gemm_relu_fraction(A, B, M, N, K, dtype, transB)
+            got = [[Fraction(float(x)) for x in row] for row in C]
+            assert got == want, (M, N, K, dtype, transB)
+
+
+@pytest.mark.parametrize("transB", [0, 1])
+def test_bruteforce_exhaustive_2x2x2(transB):
+    # all 3^8 assignments of {-1, 0, 1} to the 4 + 4 operand entries
+    vals = np.array([-1.0, 0.0, 1.0])
+    for combo in itertools.product(range(3), repeat=8):
+        a = vals[list(combo[:4])]
+        b = vals[list(combo[4:])]
+        A, B = enc(a, F16), enc(b, F16)
+        C = oracle.gemm_relu_ref(A, B, 2, 2, 2, F16, transB)
+        am = a.reshape(2, 2)
+        bm = b.reshape(2, 2)
+        bkn = bm.T if transB else bm
+        for i in range(2):
+            for j in range(2):
+                s = int(am[i, 0] * bkn[0, j] + am[i, 1] * bkn[1, j])
+                assert C[i, j] == max(s, 0)
+
+
+# ---------------------------------------------------- P8 transB equivalence
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_transB_equivalence(dtype):
+    M, N, K = 19, 23, 37
+    A = wl.uniform((M, K), 31, dtype)
+    B = wl.uniform((K, N), 32, dtype)
+    Bt = np.ascontiguousarray(B.T)
+    C0 = oracle.gemm_relu_ref(A, B, M, N, K, dtype, 0)
+    C1 = oracle.gemm_relu_ref(A, Bt, M, N, K, dtype, 1)
+    assert np.array_equal(C0.view(np.uint64), C1.view(np.uint64))
+
+
+# ------------------------------------------------------- P9 power-of-two scale
+@pytest.mark.parametrize("s", [-3, 1, 4])
+def test_power_of_two_scaling(s):
+    M, N, K = 9, 10, 21
+    A = wl.uniform((M, K), 41, F16, lo=-1.0, hi=1.0)
+    B = wl.uniform((K, N), 42, F16)
+    a = A.view(np.float16).astype(np.float64)
+    As = enc(a * 2.0 ** s, F16)
+    # only exact scalings are meaningful: no element may under- or overflow
+    a_back = As.view(np.float16).astype(np.float64) / 2.0 ** s
+    keep = a_back == a
+    A2 = np.where(keep, A, np.uint16(0))
+    As2 = np.where(keep, As, np.uint16(0))
+    C = oracle.gemm_relu_ref(A2, B, M, N, K, F16, 0)
+    Cs = oracle.gemm_relu_ref(As2, B, M, N, K, F16, 0)
+    assert np.array_equal(Cs, C * 2.0 ** s)
+
+
+# ---------------------------------------------- sampled entry and error sums
+def test_sampled_matches_full_and_absum():
+    M, N, K = 37, 41, 53
+    for transB, dtype in ((0, F16), (1, BF16)):
+        A, B = wl.make_inputs(M, N, K, dtype, transB, "uniform", 9)
+        C = oracle.gemm_relu_ref(A, B, M, N, K, dtype, transB)
+        rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        v, absum = oracle.gemm_relu_ref_at(A, B, rows.ravel(), cols.ravel(), M, N, K,
+                                           dtype, transB)
+        assert np.array_equal(v.reshape(M, N), C)
+        a = np.abs(oracle.decode(A, dtype).reshape(M, K))
+        b = np.abs(oracle.decode(B, dtype).reshape((N, K) if transB else (K, N)))
+        S = a @ (b.T if transB else b)
+        assert np.allclose(absum.reshape(M, N), S, rtol=1e-12, atol=0)
+
+
+def test_integer_inputs_are_exact_against_fractions():
+    M, N, K = 7, 5, 300
+    A, B = wl.make_inputs(M, N, K, F16, 0, "uniform", 3, int_values=True)
+    C = oracle.gemm_relu_ref(A, B, M, N, K, F16, 0)
+    want = oracle.gemm_relu_fraction(A, B, M, N, K, F16, 0)
+    assert [[Fraction(float(x)) for x in r] for r in C] == want
+
+
+def test_rejects_bad_arguments():
+    A = np.zeros(4, np.uint16)
+    with pytest.raises(ValueError):
+        oracle.gemm_relu_ref(A, A, 2, 2, 2, 7, 0)       # bad dtype
+    with pytest.raises(ValueError):
+        oracle.gemm_relu_ref(A, A, 2, 2, 2, F16, 2)     # bad transB
+    with pytest.raises(ValueError):
+        oracle.gemm_relu_ref_at(A, A, [2], [0], 2, 2, 2, F16)   # row out of range
+
+
+def test_empty_shapes():
+    z = np.zeros(0, np.uint16)
+    assert oracle.gemm_relu_ref(z, z, 0, 5, 0, F16).shape == (0, 5)
+    C = oracle.gemm_relu_ref(z, z, 3, 4, 0, F16)
+    assert np.all(C == 0) and not np.any(np.signbit(C))
