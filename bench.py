@@ -1,0 +1,171 @@
+"""Throughput of the fused GEMM + ReLU on one MI355X.
+
+One step = one gemm_relu call (every stage of the hot path: tile rasterisation,
+global->LDS pipeline, MFMA contraction, ReLU, convert, store) over inputs
+already resident in HBM.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+Default workload: fp16 GEMM+ReLU at M = N = K = 8192 (row-major A and B,
+uniform[-1, 1] inputs from a fixed seed, fp32 accumulation, fp16 output) — the
+shape of the pages' headline GEMM figure.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+PEAK_TFLOPS_F16 = 2516.6      # MI355X dense fp16/bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+HBM_GBPS = 8000.0
+METRIC = "TFLOP/s and % of MI355X fp16 MFMA peak, fp16 GEMM+ReLU 8192³"
+KERNEL_SOURCES = ["dense_tiled_gemm_relu_amd/csrc/gemm_relu_kernel.hpp",
+                  "dense_tiled_gemm_relu_amd/csrc/configs.hpp",
+                  "dense_tiled_gemm_relu_amd/csrc/gemm_relu_api.hip"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, launches_per_record=None):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, A, B, target_s=15.0):
+    """The oracle, untuned, on a bounded sample of the same workload: the first
+    R rows of A against all of B (R x N x K multiply-adds), R sized so the run
+    takes about target_s seconds on this host's cores."""
+    import oracle
+    M, N, K, ic, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["transB"]
+    rows_a = A.reshape(M, K)
+    # calibration pass on a few rows (also warms the decoder and thread pool)
+    r0 = min(M, 16)
+    t = time.perf_counter()
+    oracle.gemm_relu_ref(rows_a[:r0], B, r0, N, K, ic, tb)
+    dt0 = time.perf_counter() - t
+    R = int(min(M, max(r0, round(r0 * target_s / max(dt0, 1e-3)))))
+    t = time.perf_counter()
+    _, threads = oracle.gemm_relu_ref(rows_a[:R], B, R, N, K, ic, tb, return_threads=True)
+    dt = time.perf_counter() - t
+    flops = 2.0 * R * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "rows 0..%d of A (%d x %d x %d multiply-adds of the %s workload, "
+                      "binary64), %.2f s wall" % (R - 1, R, N, K, w["name"], dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gemm_relu_f16_8192", choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the fused GEMM+ReLU has no multi-GPU path in this "
+              "library (an M or N split needs no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dense_tiled_gemm_relu_amd as gr
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if not os.path.exists(gr.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    w = dict(wl.WORKLOADS[args.workload], name=args.workload)
+    M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
+    A, B = wl.workload_inputs(args.workload)
+    tdt = {wl.F16: torch.float16, wl.BF16: torch.bfloat16, wl.F32: torch.float32}
+    Ad = torch.from_numpy(A.reshape(M, K).view(np.int16)).cuda().view(tdt[ic])
+    Bd = torch.from_numpy(B.reshape(wl.b_shape(M, N, K, tb)).view(np.int16)).cuda().view(tdt[ic])
+    Cd = torch.empty((M, N), dtype=tdt[oc], device="cuda")
+    plan = gr.gemm_relu_plan(Ad, Bd, Cd, M, N, K, ic, oc, tb)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        gr.gemm_relu(Ad, Bd, Cd, M, N, K, ic, oc, tb, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` calls, synchronised on both sides; HIP
+    # events on the launch stream give the kernels' own average duration
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    flops = 2.0 * M * N * K
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS_F16, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.DTYPE_NAMES[ic],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K,
+                   "in": wl.DTYPE_NAMES[ic], "out": wl.DTYPE_NAMES[oc], "transB": tb,
+                   "accumulate": "f32", "inputs": w["dist"], "tile_config": plan},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS_F16,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS_F16, 4),
+                     "traffic": measured_traffic(args.workload),
+                     "algorithmic_bytes": int(2 * M * K + 2 * K * N +
+                                              M * N * (4 if oc == wl.F32 else 2)),
+                     "kernel_ms": round(kernel_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, A, B)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,142 @@
+"""Fused dense GEMM + ReLU on AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``libgemm_relu.so`` (C-ABI in ``include/gemm_relu.h``):
+argument marshalling only — every step of C = max(A·op(B), 0) runs in the HIP
+kernels of that library.  There is no CPU or PyTorch fallback: if the library
+is missing, importing the binding's functions raises.
+
+Operation: page "TileLang：GPU/NPU 通用算子 DSL", §3.2 (GPU minimal example:
+fp16 A (M,K), B (K,N), fp32 accumulator, ReLU, fp16 C) and §3.3 (bf16 with B
+stored (N,K) and transpose_B, fp32 C).
+"""
+import ctypes
+import os
+
+F16 = 0
+BF16 = 1
+F32 = 2
+
+OK = 0
+EINVAL = -1
+EUNSUPPORTED = -2
+EHIP = -3
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgemm_relu.so")
+PROBE_LIB_PATH = os.path.join(_PKG, "libgemm_relu_probe.so")
+
+EXPORTS = ("gemm_relu", "gemm_relu_strerror", "gemm_relu_plan")
+
+_lib = None
+
+
+class GemmReluError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("gemm_relu failed (%d): %s" % (status, msg))
+        self.status = status
+
+
+def library():
+    """The loaded product library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("HIP library %s is not built; run __graft_entry__.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    i64 = ctypes.c_int64
+    vp = ctypes.c_void_p
+    lib.gemm_relu.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_int, vp]
+    lib.gemm_relu.restype = ctypes.c_int
+    lib.gemm_relu_strerror.argtypes = [ctypes.c_int]
+    lib.gemm_relu_strerror.restype = ctypes.c_char_p
+    lib.gemm_relu_plan.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int]
+    lib.gemm_relu_plan.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _addr(x):
+    """Device address of a tensor (data_ptr) or a raw integer address."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def gemm_relu_strerror(status):
+    return library().gemm_relu_strerror(int(status)).decode()
+
+
+def gemm_relu_status(A, B, C, M, N, K, in_dtype, out_dtype, transB, stream=None):
+    """Call the C-ABI and return its status code (no exception)."""
+    return library().gemm_relu(_addr(A), _addr(B), _addr(C), int(M), int(N), int(K),
+                               int(in_dtype), int(out_dtype), int(transB),
+                               _stream_handle(stream))
+
+
+def gemm_relu(A, B, C, M, N, K, in_dtype, out_dtype, transB, stream=None):
+    """C = max(A·op(B), 0) through the C-ABI; raises GemmReluError on failure.
+
+    A, B, C are device tensors or raw device addresses; stream is a
+    torch.cuda.Stream, a raw hipStream_t, or None for torch's current stream.
+    """
+    rc = gemm_relu_status(A, B, C, M, N, K, in_dtype, out_dtype, transB, stream)
+    if rc != OK:
+        raise GemmReluError(rc, gemm_relu_strerror(rc))
+
+
+def gemm_relu_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB):
+    """Configuration name gemm_relu would launch (None if the call is invalid)."""
+    r = library().gemm_relu_plan(_addr(A), _addr(B), _addr(C), int(M), int(N), int(K),
+                                 int(in_dtype), int(out_dtype), int(transB))
+    return None if r is None else r.decode()
+
+
+def _torch_dtype_code(dt):
+    import torch
+    return {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}[dt]
+
+
+def matmul_relu(A, B, transB=False, out_dtype=None, out=None, stream=None):
+    """Tensor front end: returns C = max(A·B, 0) (or max(A·Bᵀ, 0) with transB).
+
+    A: (M, K) fp16/bf16 CUDA tensor; B: (K, N), or (N, K) with transB, same
+    dtype.  C is allocated (like the page's T.empty) unless ``out`` is given;
+    its dtype defaults to A's.
+    """
+    import torch
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("A and B must share dtype float16 or bfloat16")
+    if not (A.is_cuda and B.is_cuda) or A.device != B.device:
+        raise ValueError("A and B must be on the same GPU")
+    if not (A.is_contiguous() and B.is_contiguous()):
+        raise ValueError("A and B must be contiguous (row-major)")
+    M, K = A.shape
+    if transB:
+        N, Kb = B.shape
+    else:
+        Kb, N = B.shape
+    if Kb != K:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, Kb))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or A.dtype, device=A.device)
+    elif out.shape != (M, N) or not out.is_contiguous() or out.device != A.device:
+        raise ValueError("out must be a contiguous (M, N) tensor on A's device")
+    gemm_relu(A, B, out, M, N, K, _torch_dtype_code(A.dtype), _torch_dtype_code(out.dtype),
+              1 if transB else 0, stream)
+    return out

@@ -1,0 +1,80 @@
+"""Build the HIP libraries of the package for gfx950.
+
+* ``libgemm_relu.so``       — the product: C-ABI gemm_relu / gemm_relu_strerror /
+                              gemm_relu_plan (include/gemm_relu.h);
+* ``libgemm_relu_probe.so`` — test-only lane-layout probes.
+
+Objects go to ``_build/`` at the repository root; the libraries are written
+next to this file, where the Python binding loads them.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+LIB = os.path.join(PKG, "libgemm_relu.so")
+PROBE_LIB = os.path.join(PKG, "libgemm_relu_probe.so")
+
+LIB_SOURCES = ["gemm_relu_api.hip", "inst_f16_nn.hip", "inst_f16_nt.hip",
+               "inst_bf16_nn.hip", "inst_bf16_nt.hip"]
+PROBE_SOURCES = ["probe_layouts.hip"]
+HEADERS = ["gemm_relu_kernel.hpp", "configs.hpp"]
+
+# gfx950 only.  Packed fp32 ALU ops are switched off: the compiler otherwise
+# forms v_pk_* fp32 instructions from ordinary float code.
+HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
+
+
+def _newer(target, deps):
+    if not os.path.exists(target):
+        return True
+    t = os.path.getmtime(target)
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def _compile(src, force, verbose):
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, h) for h in HEADERS] + \
+        [os.path.join(INCLUDE, "gemm_relu.h")]
+    if force or _newer(obj, deps):
+        cmd = [HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr[-4000:]))
+    return obj
+
+
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+
+
+def build(force=True, verbose=False, jobs=None):
+    """Compile and link both libraries.  force=False skips up-to-date objects."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    srcs = LIB_SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, force, verbose), srcs)))
+    _link([objs[s] for s in LIB_SOURCES], LIB, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
+    return LIB, PROBE_LIB
+
+
+if __name__ == "__main__":
+    print(build(force="--force" in sys.argv, verbose=True))

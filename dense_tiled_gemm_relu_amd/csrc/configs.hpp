@@ -1,0 +1,106 @@
+// Kernel configurations of the fused GEMM + ReLU and their launch table.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gemm_relu_kernel.hpp"
+
+namespace gemm_relu_hip {
+
+// Tile shapes.  "d" = direct global->LDS copies (needs K % 8 == 0, N % 8 == 0
+// and 16-byte aligned operands); "g" = register-staged copies with element-wise
+// bounds checks (any shape and alignment).
+enum ConfigId : int {
+    CFG_D256x256x64_S2 = 0,
+    CFG_D128x128x64_S3,
+    CFG_D64x64x64_S4,
+    CFG_G128x128x64,
+    CFG_G64x64x64,
+    CFG_COUNT
+};
+
+struct ConfigInfo {
+    const char* name;
+    int bm, bn;
+    bool direct;
+};
+
+inline const ConfigInfo& config_info(int id)
+{
+    static const ConfigInfo table[CFG_COUNT] = {
+        {"d256x256x64_s2", 256, 256, true},
+        {"d128x128x64_s3", 128, 128, true},
+        {"d64x64x64_s4", 64, 64, true},
+        {"g128x128x64", 128, 128, false},
+        {"g64x64x64", 64, 64, false},
+    };
+    return table[id];
+}
+
+template <int IN, int OUT, bool TB, int id> struct CfgOf;
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x64_S2> {
+    using type = Cfg<IN, OUT, TB, 256, 256, 64, 2, 2, 2, true>;
+};
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D128x128x64_S3> {
+    using type = Cfg<IN, OUT, TB, 128, 128, 64, 2, 2, 3, true>;
+};
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D64x64x64_S4> {
+    using type = Cfg<IN, OUT, TB, 64, 64, 64, 2, 2, 4, true>;
+};
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_G128x128x64> {
+    using type = Cfg<IN, OUT, TB, 128, 128, 64, 2, 2, 2, false>;
+};
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_G64x64x64> {
+    using type = Cfg<IN, OUT, TB, 64, 64, 64, 2, 2, 2, false>;
+};
+
+typedef hipError_t (*LaunchFn)(const KernelArgs& args, int grid, hipStream_t stream);
+
+template <class C>
+hipError_t launch_one(const KernelArgs& args, int grid, hipStream_t stream)
+{
+    void* params[] = {const_cast<KernelArgs*>(&args)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_relu_kernel<C>), dim3(grid),
+                           dim3(C::NTHREADS), params, 0, stream);
+}
+
+// One table per (input dtype, transB); defined in the instantiation units.
+LaunchFn launcher_f16_nn(int out_dt, int cfg);
+LaunchFn launcher_f16_nt(int out_dt, int cfg);
+LaunchFn launcher_bf16_nn(int out_dt, int cfg);
+LaunchFn launcher_bf16_nt(int out_dt, int cfg);
+
+}  // namespace gemm_relu_hip
+
+// Body of an instantiation unit: every configuration for one (IN, TRANS_B)
+// and the three output types.
+#define GEMM_RELU_DEFINE_LAUNCHER(FN, IN, TB)                                              \
+    namespace gemm_relu_hip {                                                              \
+    template <int OUT>                                                                     \
+    static LaunchFn FN##_out(int cfg)                                                      \
+    {                                                                                      \
+        switch (cfg) {                                                                     \
+        case CFG_D256x256x64_S2:                                                           \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2>::type>;     \
+        case CFG_D128x128x64_S3:                                                           \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D128x128x64_S3>::type>;     \
+        case CFG_D64x64x64_S4:                                                             \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x64x64_S4>::type>;       \
+        case CFG_G128x128x64:                                                              \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_G128x128x64>::type>;        \
+        case CFG_G64x64x64:                                                                \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_G64x64x64>::type>;          \
+        default:                                                                           \
+            return nullptr;                                                                \
+        }                                                                                  \
+    }                                                                                      \
+    LaunchFn FN(int out_dt, int cfg)                                                       \
+    {                                                                                      \
+        switch (out_dt) {                                                                  \
+        case DT_F16: return FN##_out<DT_F16>(cfg);                                         \
+        case DT_BF16: return FN##_out<DT_BF16>(cfg);                                       \
+        case DT_F32: return FN##_out<DT_F32>(cfg);                                         \
+        default: return nullptr;                                                           \
+        }                                                                                  \
+    }                                                                                      \
+    }

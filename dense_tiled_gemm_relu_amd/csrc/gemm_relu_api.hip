@@ -1,0 +1,222 @@
+// C-ABI of the fused GEMM + ReLU: argument checks, configuration choice, launch.
+//
+// Semantics (page "TileLang：GPU/NPU 通用算子 DSL", §3.2 and §3.3): C is
+// overwritten with max(A·op(B), 0); the grid has one workgroup per output tile
+// and a ceil-divided K loop, so every shape is covered, tails included.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "configs.hpp"
+#include "gemm_relu.h"
+
+using namespace gemm_relu_hip;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kNumCUs = 256;   // MI355X: 8 XCDs x 32 CUs
+
+struct Env {
+    bool sync = false;
+    int force_cfg = -1;   // GEMM_RELU_FORCE_CONFIG=<name>
+    int panel = 0;        // GEMM_RELU_PANEL=<tile rows>, 0 = default
+};
+
+// Debug and tuning switches, read on every call so a process can change them
+// between calls.
+Env env()
+{
+    Env e;
+    const char* s = std::getenv("GEMM_RELU_SYNC");
+    e.sync = s && s[0] == '1';
+    const char* f = std::getenv("GEMM_RELU_FORCE_CONFIG");
+    if (f && f[0]) {
+        for (int i = 0; i < CFG_COUNT; ++i)
+            if (std::strcmp(f, config_info(i).name) == 0) e.force_cfg = i;
+    }
+    const char* p = std::getenv("GEMM_RELU_PANEL");
+    if (p && p[0]) e.panel = std::atoi(p);
+    return e;
+}
+
+// Per-device "is this a gfx950" cache.
+struct DevState {
+    std::once_flag once;
+    bool ok = false;
+    hipError_t err = hipSuccess;
+};
+DevState g_dev[kMaxDevices];
+
+int check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return GEMM_RELU_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return GEMM_RELU_EUNSUPPORTED;
+    DevState& d = g_dev[dev];
+    std::call_once(d.once, [&] {
+        hipDeviceProp_t prop;
+        d.err = hipGetDeviceProperties(&prop, dev);
+        if (d.err == hipSuccess) d.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    });
+    if (d.err != hipSuccess) return GEMM_RELU_EHIP;
+    return d.ok ? GEMM_RELU_OK : GEMM_RELU_EUNSUPPORTED;
+}
+
+int elem_bytes(int dt) { return dt == GEMM_RELU_F32 ? 4 : 2; }
+
+bool overlaps(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb)
+{
+    if (na == 0 || nb == 0) return false;
+    return a < b + nb && b < a + na;
+}
+
+struct Plan {
+    int status = GEMM_RELU_OK;
+    bool empty = false;   // nothing to launch
+    int cfg = -1;
+    int tiles_m = 0, tiles_n = 0;
+};
+
+bool direct_ok(const void* A, const void* B, const void* C, int64_t N, int64_t K, int out_dt)
+{
+    const uintptr_t mask = 15;
+    return (K % 8 == 0) && (N % 8 == 0) && K <= (int64_t(1) << 22) && N <= (int64_t(1) << 24) &&
+           ((reinterpret_cast<uintptr_t>(A) & mask) == 0) &&
+           ((reinterpret_cast<uintptr_t>(B) & mask) == 0) &&
+           ((reinterpret_cast<uintptr_t>(C) & mask) == 0) && out_dt >= 0;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
+               int in_dt, int out_dt, int transB, const Env& e)
+{
+    Plan p;
+    const int64_t lim = INT32_MAX;
+    if (M < 0 || N < 0 || K < 0 || M > lim || N > lim || K > lim) {
+        p.status = GEMM_RELU_EINVAL;
+        return p;
+    }
+    if ((in_dt != GEMM_RELU_F16 && in_dt != GEMM_RELU_BF16) ||
+        (out_dt != GEMM_RELU_F16 && out_dt != GEMM_RELU_BF16 && out_dt != GEMM_RELU_F32) ||
+        (transB != 0 && transB != 1)) {
+        p.status = GEMM_RELU_EINVAL;
+        return p;
+    }
+    if (M == 0 || N == 0) {
+        p.empty = true;
+        return p;
+    }
+    const uint64_t a_bytes = uint64_t(M) * uint64_t(K) * 2u;
+    const uint64_t b_bytes = uint64_t(K) * uint64_t(N) * 2u;
+    const uint64_t c_bytes = uint64_t(M) * uint64_t(N) * uint64_t(elem_bytes(out_dt));
+    if ((a_bytes && !A) || (b_bytes && !B) || !C) {
+        p.status = GEMM_RELU_EINVAL;
+        return p;
+    }
+    if ((reinterpret_cast<uintptr_t>(A) & 1) || (reinterpret_cast<uintptr_t>(B) & 1) ||
+        (reinterpret_cast<uintptr_t>(C) & uintptr_t(elem_bytes(out_dt) - 1))) {
+        p.status = GEMM_RELU_EINVAL;
+        return p;
+    }
+    const uintptr_t ua = reinterpret_cast<uintptr_t>(A), ub = reinterpret_cast<uintptr_t>(B),
+                    uc = reinterpret_cast<uintptr_t>(C);
+    if (overlaps(uc, c_bytes, ua, a_bytes) || overlaps(uc, c_bytes, ub, b_bytes)) {
+        p.status = GEMM_RELU_EINVAL;
+        return p;
+    }
+
+    const bool direct = direct_ok(A, B, C, N, K, out_dt);
+    auto tiles = [&](int id) { return ceil_div(M, config_info(id).bm) * ceil_div(N, config_info(id).bn); };
+    int cfg;
+    const int forced = e.force_cfg;
+    if (forced >= 0 && (!config_info(forced).direct || direct)) {
+        cfg = forced;
+    } else if (direct) {
+        // Largest tile that still gives every CU at least one workgroup.
+        if (tiles(CFG_D256x256x64_S2) >= kNumCUs)
+            cfg = CFG_D256x256x64_S2;
+        else if (tiles(CFG_D128x128x64_S3) >= kNumCUs)
+            cfg = CFG_D128x128x64_S3;
+        else
+            cfg = CFG_D64x64x64_S4;
+    } else {
+        cfg = tiles(CFG_G128x128x64) >= kNumCUs ? CFG_G128x128x64 : CFG_G64x64x64;
+    }
+    const int64_t tm = ceil_div(M, config_info(cfg).bm), tn = ceil_div(N, config_info(cfg).bn);
+    if (tm * tn > lim) {
+        p.status = GEMM_RELU_EUNSUPPORTED;
+        return p;
+    }
+    p.cfg = cfg;
+    p.tiles_m = int(tm);
+    p.tiles_n = int(tn);
+    return p;
+}
+
+LaunchFn pick_launcher(int in_dt, int out_dt, int transB, int cfg)
+{
+    if (in_dt == GEMM_RELU_F16) return transB ? launcher_f16_nt(out_dt, cfg) : launcher_f16_nn(out_dt, cfg);
+    return transB ? launcher_bf16_nt(out_dt, cfg) : launcher_bf16_nn(out_dt, cfg);
+}
+
+}  // namespace
+
+extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                         int in_dtype, int out_dtype, int transB, void* stream)
+{
+    const Env e = env();
+    const Plan p = make_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB, e);
+    if (p.status != GEMM_RELU_OK) return p.status;
+    if (p.empty) return GEMM_RELU_OK;
+    const int dev = check_device();
+    if (dev != GEMM_RELU_OK) return dev;
+
+    KernelArgs args;
+    args.A = static_cast<const unsigned char*>(A);
+    args.B = static_cast<const unsigned char*>(B);
+    args.C = static_cast<unsigned char*>(C);
+    args.M = int(M);
+    args.N = int(N);
+    args.K = int(K);
+    args.tiles_m = p.tiles_m;
+    args.tiles_n = p.tiles_n;
+    const int panel = e.panel > 0 ? e.panel : 8;
+    args.panel = panel < p.tiles_m ? panel : p.tiles_m;
+
+    LaunchFn fn = pick_launcher(in_dtype, out_dtype, transB, p.cfg);
+    if (!fn) return GEMM_RELU_EUNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (fn(args, p.tiles_m * p.tiles_n, st) != hipSuccess) return GEMM_RELU_EHIP;
+    if (e.sync) {
+        if (hipStreamSynchronize(st) != hipSuccess) return GEMM_RELU_EHIP;
+        if (hipGetLastError() != hipSuccess) return GEMM_RELU_EHIP;
+    }
+    return GEMM_RELU_OK;
+}
+
+extern "C" const char* gemm_relu_strerror(int status)
+{
+    switch (status) {
+    case GEMM_RELU_OK: return "success";
+    case GEMM_RELU_EINVAL: return "invalid argument";
+    case GEMM_RELU_EUNSUPPORTED: return "unsupported device or size";
+    case GEMM_RELU_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+extern "C" const char* gemm_relu_plan(const void* A, const void* B, const void* C, int64_t M,
+                                      int64_t N, int64_t K, int in_dtype, int out_dtype,
+                                      int transB)
+{
+    const Plan p = make_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB, env());
+    if (p.status == GEMM_RELU_EINVAL) return nullptr;
+    if (p.status != GEMM_RELU_OK) return "unsupported";
+    if (p.empty) return "none";
+    return config_info(p.cfg).name;
+}

@@ -1,0 +1,564 @@
+// Fused dense GEMM + ReLU for CDNA4 (gfx950): C = max(A·op(B), 0).
+//
+// The operation is the running example of page "TileLang：GPU/NPU 通用算子 DSL"
+// (§3.2 GPU minimal example): a block of C is owned by one workgroup, its fp32
+// accumulator is cleared, the K range is walked in BK-wide steps that stage an
+// A tile and a B tile from global memory into shared memory through a
+// multi-buffered pipeline, each step is contracted on the matrix units, and
+// the accumulator goes through max(x, 0) and a type conversion before it is
+// stored.  §3.3 of the same page adds the bf16 variant with B stored (N, K)
+// (transpose_B) and an fp32 C.  Page "从 TVM 到 TileLang…", §三, adds the
+// thread-block rasterisation swizzle (panel of tile rows) for L2 reuse.
+//
+// What is specific to gfx950 here (none of it is on the pages):
+//   * v_mfma_f32_32x32x16_{f16,bf16}: each lane feeds 8 consecutive k of one
+//     row (or column) and owns 16 fp32 results of a 32x32 block;
+//   * global_load_lds_dwordx4: a wave writes 64 x 16 B straight into LDS, lane
+//     i at base + 16 i, with no register round trip; the XOR swizzle of the LDS
+//     layout is realised by choosing which global 16 B chunk each lane fetches;
+//   * ds_read_b64_tr_b16: the LDS transpose read that turns an n-contiguous B
+//     tile into k-contiguous MFMA operands, so row-major B needs no transpose
+//     pass;
+//   * 256 CUs in 8 XCDs with one L2 each: workgroup w is placed on XCD w mod 8,
+//     so the tile order is remapped to give each XCD a contiguous run of tiles
+//     before the panel swizzle is applied.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gemm_relu_hip {
+
+enum : int { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2 };
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+#define GR_LDS __attribute__((address_space(3)))
+
+struct KernelArgs {
+    const unsigned char* A;   // (M, K) row-major, 16-bit elements
+    const unsigned char* B;   // (K, N) row-major, or (N, K) row-major when transposed
+    unsigned char* C;         // (M, N) row-major, 2- or 4-byte elements
+    int M, N, K;
+    int tiles_m, tiles_n;
+    int panel;                // tile rows per rasterisation panel (>= 1)
+};
+
+// 16 zero bytes in global memory: the source of K-tail chunks of the direct loader.
+__device__ __attribute__((aligned(16))) const unsigned int g_zero16[4] = {0u, 0u, 0u, 0u};
+
+// ------------------------------------------------------------------ helpers
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14).
+__host__ __device__ constexpr int waitcnt_vm(int n)
+{
+    return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14);
+}
+
+// Barrier that orders LDS only: waits for this wave's LDS traffic (lgkmcnt), not
+// for its outstanding global loads, which keep streaming later pipeline stages.
+__device__ __forceinline__ void barrier_lds()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i's bytes land at LDS address M0 + 16 i.  Written as inline asm so that
+// the compiler does not treat later LDS reads as dependent on it (it would
+// otherwise drain every outstanding copy before each read); completion is
+// tracked explicitly with s_waitcnt vmcnt.  `lds` must be wave-uniform.
+__device__ __forceinline__ void dma16(const unsigned char* gbase, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(gbase), "s"(lds)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma16_abs(const unsigned char* gaddr, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gaddr), "s"(lds)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const GR_LDS unsigned char* p)
+{
+    return (uint32_t)(uintptr_t)p;
+}
+
+template <int IN_DT>
+__device__ __forceinline__ f32x16_t mfma_32x32x16(i16x8_t a, i16x8_t b, f32x16_t c)
+{
+    if constexpr (IN_DT == DT_F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ i16x8_t lds_read_b128(const GR_LDS unsigned char* p)
+{
+    return *reinterpret_cast<const GR_LDS i16x8_t*>(p);
+}
+
+__device__ __forceinline__ i16x4_t lds_read_tr16(const GR_LDS unsigned char* p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<GR_LDS i16x4_t*>(const_cast<GR_LDS unsigned char*>(p)));
+}
+
+// Output conversion after the ReLU.  max(x, 0) is written as a select so that
+// a negative (or -0) sum becomes +0.
+__device__ __forceinline__ float relu(float x) { return x > 0.0f ? x : 0.0f; }
+
+template <int OUT_DT> struct OutTraits;
+template <> struct OutTraits<DT_F16> {
+    static constexpr int bytes = 2;
+    __device__ static unsigned short cvt(float x)
+    {
+        return __builtin_bit_cast(unsigned short, (_Float16)x);
+    }
+};
+template <> struct OutTraits<DT_BF16> {
+    static constexpr int bytes = 2;
+    __device__ static unsigned short cvt(float x)
+    {
+        return __builtin_bit_cast(unsigned short, (__bf16)x);
+    }
+};
+template <> struct OutTraits<DT_F32> {
+    static constexpr int bytes = 4;
+};
+
+// ---------------------------------------------------------- configuration
+template <int IN_DT_, int OUT_DT_, bool TRANS_B_, int BM_, int BN_, int BK_, int WAVES_M_,
+          int WAVES_N_, int STAGES_, bool DIRECT_>
+struct Cfg {
+    static constexpr int IN_DT = IN_DT_, OUT_DT = OUT_DT_;
+    static constexpr bool TRANS_B = TRANS_B_, DIRECT = DIRECT_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
+    static constexpr int NWAVES = WAVES_M * WAVES_N;
+    static constexpr int NTHREADS = 64 * NWAVES;
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
+    static constexpr int TM = WM / 32, TN = WN / 32;               // 32x32 MFMA blocks per wave
+    static constexpr int KSUB = BK / 16;                           // MFMA k-steps per BK step
+    static constexpr int ROW_CH = BK / 8;                          // 16 B chunks per k-contiguous row
+    static constexpr int NROW_CH = BN / 8;                         // 16 B chunks per n-contiguous row
+    static constexpr int A_BYTES = BM * BK * 2;
+    static constexpr int B_BYTES = BN * BK * 2;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static constexpr int A_CH = BM * BK / 8;                       // 16 B chunks per stage
+    static constexpr int B_CH = BN * BK / 8;
+    static constexpr int A_PER_THREAD = A_CH / NTHREADS;
+    static constexpr int B_PER_THREAD = B_CH / NTHREADS;
+    static constexpr int LOADS_PER_STAGE = A_PER_THREAD + B_PER_THREAD;  // vm ops per wave per stage
+
+    static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tiling");
+    static_assert(BK == 32 || BK == 64, "BK");
+    static_assert(A_CH % NTHREADS == 0 && B_CH % NTHREADS == 0, "loader tiling");
+    static_assert(TRANS_B || BN >= 64, "n-contiguous B rows need >= 8 chunks for the swizzle");
+    static_assert(TRANS_B || TN == 1 || TN % 2 == 0, "B read offsets assume TN even or 1");
+    static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+    static_assert((STAGES - 2) * LOADS_PER_STAGE < 64, "vmcnt range");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity of a gfx950 CU");
+};
+
+// XOR swizzle of a k-contiguous tile row (A, or B stored (N,K)).  Rows that
+// share one 128-byte line of LDS banks get distinct 16 B chunk positions, so
+// the 8 lanes reading the same logical chunk of 8 consecutive rows never
+// collide.
+template <int ROW_CH>
+__device__ __forceinline__ int swz_krow(int r)
+{
+    if constexpr (ROW_CH >= 8)
+        return r & 7;
+    else
+        return (r / (8 / ROW_CH)) % ROW_CH;
+}
+
+// XOR swizzle of an n-contiguous B row (B stored (K,N)).  A transpose read
+// touches 4 consecutive k rows x 2 chunks per 16 lanes; XOR-ing the chunk
+// index with 2*(k mod 4) spreads those 8 chunks over distinct positions.
+__device__ __forceinline__ int swz_nrow(int k) { return 2 * (k & 3); }
+
+// ------------------------------------------------------------ tile order
+// Workgroup id -> (tile row, tile col).  First an XCD-aware remap: the
+// dispatcher places workgroup w on XCD (w mod 8), so tiles are renumbered to
+// give every XCD one contiguous run of the logical order.  Then a panel
+// swizzle: the logical order walks a panel of `panel` tile rows column by
+// column, so tiles resident together share A row panels and B column panels.
+__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int panel,
+                                            int& tm, int& tn)
+{
+    constexpr int NXCD = 8;
+    const int total = tiles_m * tiles_n;
+    const int per = total / NXCD, rem = total % NXCD;
+    const int xcd = wg % NXCD, local = wg / NXCD;
+    const int logical = xcd < rem ? xcd * (per + 1) + local
+                                  : rem * (per + 1) + (xcd - rem) * per + local;
+    const int panel_tiles = panel * tiles_n;
+    const int p = logical / panel_tiles;
+    const int within = logical - p * panel_tiles;
+    const int rows = min(panel, tiles_m - p * panel);
+    tm = p * panel + within % rows;
+    tn = within / rows;
+}
+
+// ------------------------------------------------------------- the kernel
+template <class C>
+__global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs args)
+{
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::STAGES;
+    constexpr int TM = C::TM, TN = C::TN, KSUB = C::KSUB;
+    constexpr int ROW_CH = C::ROW_CH, NROW_CH = C::NROW_CH;
+    constexpr int APT = C::A_PER_THREAD, BPT = C::B_PER_THREAD;
+
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[C::LDS_BYTES];
+    GR_LDS unsigned char* smem = (GR_LDS unsigned char*)(smem_raw);
+
+    const int M = args.M, N = args.N, K = args.K;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    int tm, tn;
+    tile_coords(blockIdx.x, args.tiles_m, args.tiles_n, args.panel, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = (K + BK - 1) / BK;
+
+    // ---- loader geometry: this thread owns LDS slots q = i*NTHREADS + tid of
+    // each stage region; a wave's 64 slots are contiguous (one 1 KiB DMA write).
+    // For every slot, the logical (row, chunk) it holds and the byte offset of
+    // that chunk's source relative to the tile's global origin.
+    uint32_t a_src[APT];
+    int a_kch[APT];      // k index of the chunk's first element within the step
+    int a_row_ok[APT];
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+        const int q = i * C::NTHREADS + tid;
+        const int r = q / ROW_CH, p = q % ROW_CH;
+        const int c = p ^ swz_krow<ROW_CH>(r);
+        const int row = min(m0 + r, M - 1) - m0;           // clamp: finite data, output discarded
+        a_src[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)c * 16u;
+        a_kch[i] = c * 8;
+        a_row_ok[i] = (m0 + r) < M;
+    }
+    uint32_t b_src[BPT];
+    int b_kch[BPT];      // transposed B: k of the chunk; (K,N) B: k row of the chunk
+    int b_ok[BPT];
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        const int q = i * C::NTHREADS + tid;
+        if constexpr (C::TRANS_B) {
+            const int r = q / ROW_CH, p = q % ROW_CH;
+            const int c = p ^ swz_krow<ROW_CH>(r);
+            const int row = min(n0 + r, N - 1) - n0;
+            b_src[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)c * 16u;
+            b_kch[i] = c * 8;
+            b_ok[i] = (n0 + r) < N;
+        } else {
+            const int k = q / NROW_CH, p = q % NROW_CH;
+            const int c = p ^ swz_nrow(k);
+            const int col = min(n0 + 8 * c, N - 8) - n0;     // direct path: N % 8 == 0
+            b_src[i] = (uint32_t)k * (uint32_t)N * 2u + (uint32_t)col * 2u;
+            b_kch[i] = k;
+            b_ok[i] = (n0 + 8 * c) < N;
+        }
+    }
+
+    const unsigned char* a_tile = args.A + (size_t)m0 * (size_t)K * 2u;
+    const unsigned char* b_tile = C::TRANS_B ? args.B + (size_t)n0 * (size_t)K * 2u
+                                             : args.B + (size_t)n0 * 2u;
+
+    // ---- direct loader: global -> LDS without registers.
+    const uint32_t smem_addr = lds_addr(smem);
+    auto issue_direct = [&](int t, int stage) {
+        const int k0 = t * BK;
+        const uint32_t sa = smem_addr + stage * C::STAGE_BYTES;
+        const uint32_t sb = sa + C::A_BYTES;
+        const unsigned char* ga = a_tile + (size_t)k0 * 2u;
+        const unsigned char* gb = C::TRANS_B ? b_tile + (size_t)k0 * 2u
+                                             : b_tile + (size_t)k0 * (size_t)N * 2u;
+        if (k0 + BK <= K) {
+#pragma unroll
+            for (int i = 0; i < APT; ++i) dma16(ga, a_src[i], sa + (i * C::NWAVES + wave) * 1024);
+#pragma unroll
+            for (int i = 0; i < BPT; ++i) dma16(gb, b_src[i], sb + (i * C::NWAVES + wave) * 1024);
+        } else {
+            // K tail (K % 8 == 0 on this path, so a chunk is wholly in or out):
+            // chunks past K fetch 16 zero bytes instead.
+            const unsigned char* zero = reinterpret_cast<const unsigned char*>(g_zero16);
+#pragma unroll
+            for (int i = 0; i < APT; ++i)
+                dma16_abs((k0 + a_kch[i] < K) ? ga + a_src[i] : zero,
+                          sa + (i * C::NWAVES + wave) * 1024);
+#pragma unroll
+            for (int i = 0; i < BPT; ++i)
+                dma16_abs((k0 + b_kch[i] < K) ? gb + b_src[i] : zero,
+                          sb + (i * C::NWAVES + wave) * 1024);
+        }
+    };
+
+    // ---- register-staged loader for any alignment: element-wise bounds checks,
+    // zero fill outside the matrix, then one 16 B LDS write per chunk.
+    u32x4_t ra[C::DIRECT ? 1 : APT], rb[C::DIRECT ? 1 : BPT];
+    auto load_chunk = [&](const unsigned char* base, size_t row_off, int e0, int e_lim,
+                          bool row_ok, bool vec_ok) -> u32x4_t {
+        // 8 consecutive 16-bit elements e0 .. e0+7 of one row; valid if e < e_lim.
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (!row_ok) return v;
+        const unsigned short* p =
+            reinterpret_cast<const unsigned short*>(base + row_off) + e0;
+        if (vec_ok && e0 + 8 <= e_lim) {
+            v = *reinterpret_cast<const u32x4_t*>(p);
+        } else {
+            unsigned short h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = (e0 + e < e_lim) ? p[e] : (unsigned short)0;
+            v = u32x4_t{h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16),
+                        h[4] | ((unsigned)h[5] << 16), h[6] | ((unsigned)h[7] << 16)};
+        }
+        return v;
+    };
+    const bool a_vec = ((K & 7) == 0) && ((reinterpret_cast<uintptr_t>(args.A) & 15) == 0);
+    const bool b_vec = (C::TRANS_B ? ((K & 7) == 0) : ((N & 7) == 0)) &&
+                       ((reinterpret_cast<uintptr_t>(args.B) & 15) == 0);
+    auto load_staged = [&](int t) {
+        const int k0 = t * BK;
+#pragma unroll
+        for (int i = 0; i < APT; ++i) {
+            const int q = i * C::NTHREADS + tid;
+            const int r = q / ROW_CH;
+            ra[C::DIRECT ? 0 : i] = load_chunk(args.A, (size_t)(m0 + r) * (size_t)K * 2u,
+                                               k0 + a_kch[i], K, a_row_ok[i], a_vec);
+        }
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            const int q = i * C::NTHREADS + tid;
+            if constexpr (C::TRANS_B) {
+                const int r = q / ROW_CH;
+                rb[C::DIRECT ? 0 : i] = load_chunk(args.B, (size_t)(n0 + r) * (size_t)K * 2u,
+                                                   k0 + b_kch[i], K, b_ok[i], b_vec);
+            } else {
+                const int k = q / NROW_CH, p = q % NROW_CH;
+                const int c = p ^ swz_nrow(k);
+                rb[C::DIRECT ? 0 : i] = load_chunk(args.B, (size_t)(k0 + k) * (size_t)N * 2u,
+                                                   n0 + 8 * c, N, k0 + k < K, b_vec);
+            }
+        }
+    };
+    auto store_staged = [&](int stage) {
+        GR_LDS unsigned char* sa = smem + stage * C::STAGE_BYTES;
+        GR_LDS unsigned char* sb = sa + C::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < APT; ++i)
+            *reinterpret_cast<GR_LDS u32x4_t*>(sa + (i * C::NTHREADS + tid) * 16) =
+                ra[C::DIRECT ? 0 : i];
+#pragma unroll
+        for (int i = 0; i < BPT; ++i)
+            *reinterpret_cast<GR_LDS u32x4_t*>(sb + (i * C::NTHREADS + tid) * 16) =
+                rb[C::DIRECT ? 0 : i];
+    };
+
+    // ---- fragment read geometry (per lane, relative to a stage's A / B region).
+    const int wave_m = wave / C::WAVES_N, wave_n = wave % C::WAVES_N;
+    const int wm0 = wave_m * C::WM, wn0 = wave_n * C::WN;
+    const int l32 = lane & 31, g = lane >> 5;
+    // k-contiguous rows: lane reads row (w0 + 32 i + l32), chunk (2 s + g).
+    uint32_t a_rd[KSUB];
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s) {
+        const int r = wm0 + l32;
+        a_rd[s] = (uint32_t)(r * BK * 2 + (((2 * s + g) ^ swz_krow<ROW_CH>(r)) * 16));
+    }
+    uint32_t b_rd[C::TRANS_B ? KSUB : 4];
+    if constexpr (C::TRANS_B) {
+#pragma unroll
+        for (int s = 0; s < KSUB; ++s) {
+            const int r = wn0 + l32;
+            b_rd[s] = (uint32_t)(r * BK * 2 + (((2 * s + g) ^ swz_krow<ROW_CH>(r)) * 16));
+        }
+    } else {
+        // Transpose read: 16-lane group h reads a 4 (k) x 16 (n) block; lane i16 of
+        // the group supplies row kk = 8 (h / 2) + i16 / 4 (+ 4 t + 16 s) and the
+        // 4 columns 16 (h % 2) + 4 (i16 % 4) of the 32-column MFMA block, and
+        // receives the 4 k values of column 16 (h % 2) + i16.
+        const int h = lane >> 4, i16 = lane & 15;
+        const int kk = 8 * (h >> 1) + (i16 >> 2);
+        const int x = swz_nrow(kk);
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            // 32-column block J = wn0/32 + j with parity par (j's high part adds 128 B per pair)
+            const int J = wn0 / 32 + par;
+            const int chunk = 4 * J + 2 * (h & 1) + ((i16 >> 1) & 1);
+            const int phys = chunk ^ x;
+            b_rd[par] = (uint32_t)(kk * BN * 2 + phys * 16 + (i16 & 1) * 8);
+        }
+        b_rd[2] = b_rd[3] = 0;
+    }
+
+    f32x16_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Fragments of one MFMA k-step: TM A blocks and TN B blocks of 32 x 16.
+    struct Frags {
+        i16x8_t a[TM], b[TN];
+    };
+    auto read_frags = [&](int stage, int s, Frags& f) {
+        const GR_LDS unsigned char* sa = smem + stage * C::STAGE_BYTES;
+        const GR_LDS unsigned char* sb = sa + C::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) f.a[i] = lds_read_b128(sa + a_rd[s] + i * 32 * BK * 2);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            if constexpr (C::TRANS_B) {
+                f.b[j] = lds_read_b128(sb + b_rd[s] + j * 32 * BK * 2);
+            } else {
+                const int hi = (TN == 1) ? 0 : (j >> 1) * 128;
+                const GR_LDS unsigned char* p = sb + b_rd[j & 1] + hi + s * 16 * BN * 2;
+                const i16x4_t lo4 = lds_read_tr16(p);
+                const i16x4_t hi4 = lds_read_tr16(p + 4 * BN * 2);
+                f.b[j] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+    };
+    // Operands swapped (B block as the MFMA's first source) so that each lane
+    // ends up owning 4 consecutive n of one output row.
+    auto mma = [&](const Frags& f) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = mfma_32x32x16<C::IN_DT>(f.b[j], f.a[i], acc[i][j]);
+    };
+
+    Frags fr[2];
+    if constexpr (C::DIRECT) {
+        // Pipeline: S-1 stages in flight ahead of the one being contracted.
+        // At the last k-step of stage t the wave waits for stage t+1, meets the
+        // others at a barrier (which also retires every read of stage t, so its
+        // buffer may be refilled), and starts reading stage t+1 while the last
+        // MFMAs of stage t run.
+#pragma unroll
+        for (int st = 0; st < S - 1; ++st)
+            if (st < nk) issue_direct(st, st);
+        if (nk > 0) {
+            if (nk - 1 >= S - 1)
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 2) * C::LOADS_PER_STAGE));
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            barrier_lds();
+            read_frags(0, 0, fr[0]);
+        }
+        for (int t = 0; t < nk; ++t) {
+            const int stage = t % S;
+            if (t + S - 1 < nk) issue_direct(t + S - 1, (t + S - 1) % S);
+#pragma unroll
+            for (int s = 0; s < KSUB; ++s) {
+                if (s + 1 < KSUB) {
+                    read_frags(stage, s + 1, fr[(s + 1) & 1]);
+                } else if (t + 1 < nk) {
+                    // stages issued after t+1: t+2 .. min(t+S-1, nk-1)
+                    if (nk - 2 - t >= S - 2)
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 2) * C::LOADS_PER_STAGE));
+                    else
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+                    barrier_lds();
+                    read_frags((t + 1) % S, 0, fr[(s + 1) & 1]);
+                }
+                mma(fr[s & 1]);
+            }
+        }
+    } else {
+        if (nk > 0) {
+            load_staged(0);
+            store_staged(0);
+        }
+        for (int t = 0; t < nk; ++t) {
+            barrier_lds();
+            if (t + 1 < nk) load_staged(t + 1);
+            read_frags(t & 1, 0, fr[0]);
+#pragma unroll
+            for (int s = 0; s < KSUB; ++s) {
+                if (s + 1 < KSUB) read_frags(t & 1, s + 1, fr[(s + 1) & 1]);
+                mma(fr[s & 1]);
+            }
+            if (t + 1 < nk) {
+                barrier_lds();
+                store_staged((t + 1) & 1);
+            }
+        }
+    }
+
+    // ---- epilogue: ReLU on the fp32 accumulators, convert, store.
+    // Lane owns C[m][n .. n+3] with m = m0 + wm0 + 32 i + l32 and
+    // n = n0 + wn0 + 32 j + 8 q + 4 g, for q = 0..3 (registers 4q .. 4q+3).
+    constexpr int OB = OutTraits<C::OUT_DT>::bytes;
+    const bool c_vec = ((N & 3) == 0) &&
+                       ((reinterpret_cast<uintptr_t>(args.C) & (4 * OB - 1)) == 0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm0 + 32 * i + l32;
+        if (m >= M) continue;
+        unsigned char* crow = args.C + (size_t)m * (size_t)N * OB;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn0 + 32 * j + 8 * q + 4 * g;
+                if (n >= N) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = relu(acc[i][j][4 * q + e]);
+                if constexpr (C::OUT_DT == DT_F32) {
+                    float* dst = reinterpret_cast<float*>(crow) + n;
+                    if (c_vec && n + 4 <= N) {
+                        *reinterpret_cast<u32x4_t*>(dst) =
+                            u32x4_t{__builtin_bit_cast(unsigned, v[0]), __builtin_bit_cast(unsigned, v[1]),
+                                    __builtin_bit_cast(unsigned, v[2]), __builtin_bit_cast(unsigned, v[3])};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < N) dst[e] = v[e];
+                    }
+                } else {
+                    unsigned short h[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) h[e] = OutTraits<C::OUT_DT>::cvt(v[e]);
+                    unsigned short* dst = reinterpret_cast<unsigned short*>(crow) + n;
+                    if (c_vec && n + 4 <= N) {
+                        *reinterpret_cast<u32x2_t*>(dst) =
+                            u32x2_t{h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16)};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < N) dst[e] = h[e];
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace gemm_relu_hip

@@ -1,0 +1,5 @@
+// Kernel instances for one input type and B layout (all tile configurations,
+// all three output types).
+#include "configs.hpp"
+
+GEMM_RELU_DEFINE_LAUNCHER(launcher_f16_nn, DT_F16, false)

@@ -1,0 +1,97 @@
+/*
+ * gemm_relu — fused dense GEMM + ReLU on AMD Instinct MI355X (gfx950).
+ *
+ * C-ABI of the library libgemm_relu.so.  Plain pointers and sizes only.
+ *
+ * The operation is the running example of page "TileLang：GPU/NPU 通用算子 DSL"
+ * (§3.2, GPU minimal example, and §3.3, Ascend 950 version):
+ *
+ *     C = max(A · op(B), 0)
+ *
+ * with 16-bit inputs, an fp32 accumulator that starts cleared (C is
+ * overwritten, never accumulated into), the max taken on the fp32 sum before
+ * it is converted to the storage type of C.  op(B) = B when B is stored (K, N)
+ * and op(B) = Bᵀ when B is stored (N, K) (§3.3's transpose_B).  The argument
+ * order (A, B, C, M, N, K) follows the gemm(A, B, C, M, N, K) call sketched on
+ * page "TileLang Skill：80行Python替代500行CUDA…" (its API example).
+ */
+#ifndef GEMM_RELU_H
+#define GEMM_RELU_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type codes. */
+#define GEMM_RELU_F16  0 /* IEEE binary16 (inputs or output) */
+#define GEMM_RELU_BF16 1 /* bfloat16 (inputs or output) */
+#define GEMM_RELU_F32  2 /* IEEE binary32 (output only) */
+
+/* Status codes.  The library never aborts, throws or prints. */
+#define GEMM_RELU_OK            0
+#define GEMM_RELU_EINVAL       -1 /* bad argument: size, pointer, code, overlap */
+#define GEMM_RELU_EUNSUPPORTED -2 /* valid request this build cannot run (device, size limits) */
+#define GEMM_RELU_EHIP         -3 /* a HIP runtime call or kernel launch failed */
+
+/*
+ * gemm_relu — C[i][j] = max( sum_k A[i][k] * opB[k][j], 0 ).
+ *
+ * Arguments
+ *   A          device pointer, M x K row-major, element type in_dtype.
+ *   B          device pointer; transB == 0: K x N row-major;
+ *                              transB == 1: N x K row-major (C = max(A·Bᵀ, 0)).
+ *   C          device pointer, M x N row-major, element type out_dtype.  Every
+ *              element is overwritten; nothing is read from C.
+ *   M, N, K    sizes, >= 0 and <= INT32_MAX.  M == 0 or N == 0: nothing to do,
+ *              returns GEMM_RELU_OK without touching the device.  K == 0: every
+ *              element of C becomes +0 (an empty sum).
+ *   in_dtype   GEMM_RELU_F16 or GEMM_RELU_BF16 (A and B share it).
+ *   out_dtype  GEMM_RELU_F16, GEMM_RELU_BF16 or GEMM_RELU_F32.
+ *   transB     0 or 1, as above.
+ *   stream     a hipStream_t, or NULL for the null stream.
+ *
+ * Layout: dense rows, no leading-dimension arguments.  A and B need 2-byte
+ * alignment, C the alignment of its element type; any shape is accepted (the
+ * fastest path is taken when K and N are multiples of 8 and all three pointers
+ * are 16-byte aligned).
+ *
+ * Numerics: products of the 16-bit inputs are summed in fp32 on the matrix
+ * units (order unspecified); the fp32 sum goes through max(x, 0) — a negative
+ * or zero sum gives +0 — and is rounded to nearest-even into out_dtype.
+ *
+ * Ownership: the caller owns A, B and C; the library keeps no pointer after the
+ * call returns and allocates no device memory.
+ *
+ * Execution: asynchronous on `stream`; the call returns after the launch.  A
+ * device-side fault surfaces at the caller's next synchronisation.  With the
+ * environment variable GEMM_RELU_SYNC=1 the call synchronises the stream and
+ * reports a failure as GEMM_RELU_EHIP.
+ *
+ * Errors: GEMM_RELU_EINVAL for negative or too-large sizes, a NULL pointer for
+ * an operand that has elements, a misaligned pointer, an unknown dtype code or
+ * combination, transB not in {0, 1}, or C overlapping A or B (checked before
+ * any HIP call); GEMM_RELU_EUNSUPPORTED when the current device is not gfx950;
+ * GEMM_RELU_EHIP when a HIP call fails.  On error nothing is launched.
+ */
+int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+              int in_dtype, int out_dtype, int transB, void* stream);
+
+/* Static message for a status code (never NULL). */
+const char* gemm_relu_strerror(int status);
+
+/*
+ * gemm_relu_plan — name of the kernel configuration gemm_relu would launch for
+ * these arguments, without touching the device ("none" when there is nothing
+ * to launch, NULL when gemm_relu would return GEMM_RELU_EINVAL).  Host-only;
+ * the pointers are inspected for alignment and overlap, never dereferenced.
+ */
+const char* gemm_relu_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
+                           int64_t K, int in_dtype, int out_dtype, int transB);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_RELU_H */

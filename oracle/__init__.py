@@ -158,3 +158,23 @@ def gemm_relu_fraction(A, B, M, N, K, dtype, transB=0, relu=True):
             row.append(max(s, Fraction(0)) if relu else s)
         out.append(row)
     return out
+
+
+def gemm_relu_ref_matmul(A, B, M, N, K, dtype, transB=0, relu=True):
+    """The same definition with numpy's binary64 matmul as the summation step.
+
+    Operands are decoded by the C decoder; the sum over k is one library
+    matrix product in binary64, so for integer-valued inputs (every partial sum
+    an integer below 2^53) the result is exact in any summation order.  For
+    full-size problems where the triple loop would take minutes.
+    """
+    A = _u16(A).reshape(-1)
+    B = _u16(B).reshape(-1)
+    if A.size != M * K or B.size != K * N:
+        raise ValueError("operand sizes do not match M, N, K")
+    a = decode(A, dtype).reshape(M, K)
+    b = decode(B, dtype).reshape((N, K) if transB else (K, N))
+    x = a @ (b.T if transB else b)
+    if not relu:
+        return x
+    return np.where(x > 0.0, x, 0.0)

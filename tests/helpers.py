@@ -42,3 +42,49 @@ def fp32_sum_bound(absum, ref, K, out_unit_roundoff):
     |gpu - ref| <= K * 2^-24 * S + u_out * |ref| + 2^-24, S = sum_k |a b|.
     """
     return K * 2.0 ** -24 * absum + out_unit_roundoff * np.abs(ref) + 2.0 ** -24
+
+
+# ------------------------------------------------------------------ GPU side
+def to_device(bits, dtype_code, shape):
+    """uint16 storage patterns -> contiguous CUDA tensor of fp16/bf16."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).reshape(shape).view(np.int16)).cuda()
+    return t.view(torch.float16 if dtype_code == 0 else torch.bfloat16)
+
+
+def out_tensor(M, N, out_code, fill=float("nan")):
+    import torch
+    dt = {0: torch.float16, 1: torch.bfloat16, 2: torch.float32}[out_code]
+    return torch.full((M, N), fill, dtype=dt, device="cuda")
+
+
+def from_device(C):
+    """CUDA tensor (fp16 / bf16 / fp32) -> exact binary64 numpy values."""
+    import torch
+    if C.dtype == torch.float32:
+        return C.cpu().numpy().astype(np.float64)
+    bits = C.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    if C.dtype == torch.float16:
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def unit_roundoff(out_code):
+    return {0: 2.0 ** -11, 1: 2.0 ** -8, 2: 2.0 ** -24}[out_code]
+
+
+def rel_tolerance(out_code):
+    """Relative term of the random-input bound: 2^-9 for fp16/fp32 outputs; a
+    bf16 output rounds with unit roundoff 2^-8, so its bound uses 2^-8."""
+    return 2.0 ** -8 if out_code == 1 else 2.0 ** -9
+
+
+def check_close(gpu, ref, K, out_code):
+    bound = np.abs(ref) * rel_tolerance(out_code) + 1e-3 * math.sqrt(max(K, 0))
+    err = np.abs(gpu - ref)
+    bad = ~(err <= bound)
+    if np.any(bad):
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%d elements out of tolerance, first %s: gpu %s ref %s"
+                             % (bad.sum(), idx.tolist(), gpu[bad][:5], ref[bad][:5]))
+    return float(err.max()) if err.size else 0.0

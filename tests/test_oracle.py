@@ -263,3 +263,22 @@ def test_empty_shapes():
     assert oracle.gemm_relu_ref(z, z, 0, 5, 0, F16).shape == (0, 5)
     C = oracle.gemm_relu_ref(z, z, 3, 4, 0, F16)
     assert np.all(C == 0) and not np.any(np.signbit(C))
+
+
+# --------------------------------------- the library-matmul form of the oracle
+@pytest.mark.parametrize("transB,dtype", [(0, F16), (1, BF16), (1, F16), (0, BF16)])
+def test_matmul_form_matches_loop_exactly_on_integers(transB, dtype):
+    M, N, K = 45, 38, 517
+    A, B = wl.make_inputs(M, N, K, dtype, transB, "uniform", 21, int_values=True)
+    C1 = oracle.gemm_relu_ref(A, B, M, N, K, dtype, transB)
+    C2 = oracle.gemm_relu_ref_matmul(A, B, M, N, K, dtype, transB)
+    assert np.array_equal(C1, C2) and not np.any(np.signbit(C2))
+
+
+def test_matmul_form_close_to_loop_on_floats():
+    M, N, K = 33, 29, 1000
+    A, B = wl.make_inputs(M, N, K, F16, 0, "uniform", 22)
+    C1 = oracle.gemm_relu_ref(A, B, M, N, K, F16, 0)
+    C2 = oracle.gemm_relu_ref_matmul(A, B, M, N, K, F16, 0)
+    # two binary64 summation orders of K products: relative gap ~ K * 2^-53
+    assert np.allclose(C1, C2, rtol=1e-12, atol=1e-12)

@@ -1,0 +1,265 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle.
+
+Integer-valued inputs have exactly one correct result (every partial sum is an
+integer far below 2^24, so fp32 accumulation is exact in any order): those
+cases are compared bit for bit.  Random inputs are compared element by element
+with the bound |gpu - ref| <= 2^-9 |ref| + 1e-3 sqrt(K) (2^-8 for a bf16 C,
+whose rounding alone reaches 2^-9), and with the fp32-summation error bound
+K 2^-24 S + u_out |ref| + 2^-24, S = sum_k |a b|.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import dense_tiled_gemm_relu_amd as gr
+import oracle
+import workloads as wl
+from tests.helpers import (check_close, from_device, fp32_sum_bound, out_tensor, to_device,
+                           unit_roundoff)
+
+pytestmark = pytest.mark.gpu
+
+DIRECT = ["d256x256x64_s2", "d128x128x64_s3", "d64x64x64_s4"]
+STAGED = ["g128x128x64", "g64x64x64"]
+COMBOS = [(i, o) for i in (wl.F16, wl.BF16) for o in (wl.F16, wl.BF16, wl.F32)]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    yield
+
+
+def run(A, B, M, N, K, in_code, out_code, transB, cfg=None, monkeypatch=None, poison=True):
+    """Upload, call gemm_relu through the C-ABI, return exact binary64 values."""
+    import torch
+    if cfg is not None:
+        monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", cfg)
+        Ad, Bd = to_device(A, in_code, (M, K)), to_device(B, in_code, wl.b_shape(M, N, K, transB))
+        Cd = out_tensor(M, N, out_code, float("nan") if poison else 0.0)
+        assert gr.gemm_relu_plan(Ad, Bd, Cd, M, N, K, in_code, out_code, transB) == cfg
+    else:
+        Ad, Bd = to_device(A, in_code, (M, K)), to_device(B, in_code, wl.b_shape(M, N, K, transB))
+        Cd = out_tensor(M, N, out_code, float("nan") if poison else 0.0)
+    gr.gemm_relu(Ad, Bd, Cd, M, N, K, in_code, out_code, transB)
+    torch.cuda.synchronize()
+    return from_device(Cd)
+
+
+def int_inputs(M, N, K, in_code, transB, seed, out_code):
+    # bf16 holds every integer only up to 256: keep |C| small there
+    lo, hi = (-1, 1) if out_code == wl.BF16 else (-2, 2)
+    A = wl.integers((M, K), seed, in_code, lo, hi)
+    B = wl.integers(wl.b_shape(M, N, K, transB), seed + 1, in_code, lo, hi)
+    return A, B
+
+
+def exact_limit(out_code):
+    return {wl.F16: 2048.0, wl.BF16: 256.0, wl.F32: 2.0 ** 24}[out_code]
+
+
+# --------------------------------------------------- every configuration
+@pytest.mark.parametrize("cfg", DIRECT + STAGED)
+@pytest.mark.parametrize("in_code,out_code", COMBOS)
+@pytest.mark.parametrize("transB", [0, 1])
+def test_configs_integer_bitexact(cfg, in_code, out_code, transB, monkeypatch):
+    # several tiles in every direction plus ragged M, N and K tails; direct
+    # configurations need K and N multiples of 8
+    M, N, K = (264, 520, 200) if cfg in DIRECT else (301, 517, 203)
+    A, B = int_inputs(M, N, K, in_code, transB, 100, out_code)
+    ref = oracle.gemm_relu_ref(A, B, M, N, K, in_code, transB)
+    assert np.abs(ref).max() < exact_limit(out_code)
+    got = run(A, B, M, N, K, in_code, out_code, transB, cfg, monkeypatch)
+    assert np.array_equal(got, ref)
+    assert not np.any(np.signbit(got))
+
+
+@pytest.mark.parametrize("cfg", DIRECT + STAGED)
+@pytest.mark.parametrize("in_code,out_code", [(wl.F16, wl.F16), (wl.BF16, wl.F32),
+                                              (wl.F16, wl.F32), (wl.BF16, wl.BF16)])
+@pytest.mark.parametrize("transB", [0, 1])
+def test_configs_uniform_tolerance(cfg, in_code, out_code, transB, monkeypatch):
+    M, N, K = (328, 264, 456) if cfg in DIRECT else (331, 263, 461)
+    A, B = wl.make_inputs(M, N, K, in_code, transB, "uniform", 200)
+    got = run(A, B, M, N, K, in_code, out_code, transB, cfg, monkeypatch)
+    ref = oracle.gemm_relu_ref(A, B, M, N, K, in_code, transB)
+    check_close(got, ref, K, out_code)
+    rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    _, absum = oracle.gemm_relu_ref_at(A, B, rows.ravel(), cols.ravel(), M, N, K, in_code, transB)
+    bound = fp32_sum_bound(absum.reshape(M, N), ref, K, unit_roundoff(out_code))
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+# ------------------------------------------------ coded mapping (index bugs)
+@pytest.mark.parametrize("cfg", DIRECT + STAGED)
+@pytest.mark.parametrize("transB", [0, 1])
+def test_coded_mapping(cfg, transB, monkeypatch):
+    """A selects one row of B per output row (A[i][pi(i)] = 1), and B's entries
+    encode their position, so every output element names its source."""
+    M, N, K = (200, 328, 264) if cfg in DIRECT else (203, 333, 269)
+    rng = np.random.default_rng(3)
+    pi = rng.permutation(K)[:M]
+    a = np.zeros((M, K))
+    a[np.arange(M), pi] = 1.0
+    k = np.arange(K)[:, None]
+    j = np.arange(N)[None, :]
+    bkn = ((131 * k + 7 * j) % 5 - 2).astype(np.float64)
+    b = bkn.T if transB else bkn
+    A, B = wl.encode(a, wl.F16), wl.encode(b, wl.F16)
+    got = run(A, B, M, N, K, wl.F16, wl.F16, transB, cfg, monkeypatch)
+    assert np.array_equal(got, np.maximum(bkn[pi, :], 0.0))
+
+
+# ----------------------------------------------------------- tail sweep
+SIZES = [1, 2, 7, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 258]
+TAIL_SHAPES = [(SIZES[i], SIZES[(i + 5) % 19], SIZES[(i + 11) % 19]) for i in range(19)] + \
+              [(SIZES[(i + 7) % 19], SIZES[i], SIZES[(i + 3) % 19]) for i in range(19)] + \
+              [(40, 8, 8), (8, 40, 24), (129, 264, 72), (257, 136, 8), (1, 8, 8)]
+
+
+@pytest.mark.parametrize("M,N,K", TAIL_SHAPES)
+@pytest.mark.parametrize("transB", [0, 1])
+def test_tail_sweep_integer(M, N, K, transB):
+    A, B = int_inputs(M, N, K, wl.F16, transB, 300 + M + N + K, wl.F16)
+    ref = oracle.gemm_relu_ref(A, B, M, N, K, wl.F16, transB)
+    got = run(A, B, M, N, K, wl.F16, wl.F16, transB)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("cfg", DIRECT + STAGED)
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (65, 72, 136), (33, 200, 520), (300, 16, 64)])
+def test_tail_shapes_every_config(cfg, M, N, K, monkeypatch):
+    A, B = int_inputs(M, N, K, wl.BF16, 0, 400 + M, wl.F32)
+    ref = oracle.gemm_relu_ref(A, B, M, N, K, wl.BF16, 0)
+    got = run(A, B, M, N, K, wl.BF16, wl.F32, 0, cfg, monkeypatch)
+    assert np.array_equal(got, ref)
+
+
+# --------------------------------------------------------- degenerate sizes
+@pytest.mark.parametrize("M,N,K", [(64, 64, 0), (37, 19, 0)])
+@pytest.mark.parametrize("out_code", [wl.F16, wl.F32])
+def test_zero_k_gives_positive_zeros(M, N, K, out_code):
+    got = run(np.zeros(0, np.uint16), np.zeros(0, np.uint16), M, N, K, wl.F16, out_code, 0)
+    assert np.all(got == 0.0) and not np.any(np.signbit(got))
+
+
+def test_empty_output_untouched():
+    import torch
+    C = torch.full((4, 4), 7.0, dtype=torch.float16, device="cuda")
+    A = torch.ones((0, 8), dtype=torch.float16, device="cuda")
+    B = torch.ones((8, 4), dtype=torch.float16, device="cuda")
+    gr.gemm_relu(A, B, C, 0, 4, 8, wl.F16, wl.F16, 0)
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0)
+
+
+# ------------------------------------------------------------ properties
+def test_determinism_and_guard_bands():
+    import torch
+    M, N, K = 520, 776, 1032
+    A, B = wl.make_inputs(M, N, K, wl.F16, 0, "uniform", 500)
+    Ad, Bd = to_device(A, wl.F16, (M, K)), to_device(B, wl.F16, (K, N))
+    guard = 4096
+    buf = torch.full((guard + M * N + guard,), float("nan"), dtype=torch.float16, device="cuda")
+    C = buf[guard:guard + M * N].view(M, N)
+    gr.gemm_relu(Ad, Bd, C, M, N, K, wl.F16, wl.F16, 0)
+    first = C.clone()
+    for _ in range(3):
+        gr.gemm_relu(Ad, Bd, C, M, N, K, wl.F16, wl.F16, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), C.view(torch.int16))
+    assert not torch.isnan(C).any()
+    assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + M * N:]).all()
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (301, 517, 203)])
+def test_transB_matches_row_major_B(M, N, K):
+    A, B = int_inputs(M, N, K, wl.F16, 0, 600, wl.F16)
+    Bt = np.ascontiguousarray(B.reshape(K, N).T)
+    g0 = run(A, B, M, N, K, wl.F16, wl.F16, 0)
+    g1 = run(A, Bt, M, N, K, wl.F16, wl.F16, 1)
+    assert np.array_equal(g0, g1)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (301, 517, 203)])
+def test_relu_pair_reconstructs_the_product(M, N, K):
+    A, B = int_inputs(M, N, K, wl.F16, 0, 700, wl.F16)
+    negA = A ^ np.uint16(0x8000)
+    X = oracle.gemm_relu_ref(A, B, M, N, K, wl.F16, 0, relu=False)
+    gp = run(A, B, M, N, K, wl.F16, wl.F16, 0)
+    gn = run(negA, B, M, N, K, wl.F16, wl.F16, 0)
+    assert np.array_equal(gp - gn, X)
+
+
+def test_runs_on_the_callers_stream():
+    import torch
+    M, N, K = 512, 512, 512
+    A, B = int_inputs(M, N, K, wl.F16, 0, 800, wl.F16)
+    Ad, Bd = to_device(A, wl.F16, (M, K)), to_device(B, wl.F16, (K, N))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        C = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+        gr.gemm_relu(Ad, Bd, C, M, N, K, wl.F16, wl.F16, 0)       # current stream = s
+    s.synchronize()
+    assert np.array_equal(from_device(C), oracle.gemm_relu_ref(A, B, M, N, K, wl.F16, 0))
+
+
+def test_matmul_relu_front_end():
+    import torch
+    M, N, K = 192, 320, 128
+    A, B = int_inputs(M, N, K, wl.BF16, 1, 900, wl.F32)
+    Ad, Bd = to_device(A, wl.BF16, (M, K)), to_device(B, wl.BF16, (N, K))
+    C = gr.matmul_relu(Ad, Bd, transB=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_device(C), oracle.gemm_relu_ref(A, B, M, N, K, wl.BF16, 1))
+
+
+# ------------------------------------------- the workloads at full size
+def _sample_positions(M, N, rng, n=2048):
+    """Random positions plus the first/last rows and columns (tile tails)."""
+    r = rng.integers(0, M, size=n)
+    c = rng.integers(0, N, size=n)
+    edge_r = np.concatenate([np.full(64, 0), np.full(64, M - 1), rng.integers(0, M, 128)])
+    edge_c = np.concatenate([rng.integers(0, N, 128), np.full(64, 0), np.full(64, N - 1)])
+    return np.concatenate([r, edge_r]), np.concatenate([c, edge_c])
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_workload_full_size(name):
+    """Each workload at its full size, with the configuration the bench times:
+    random inputs checked on sampled outputs (oracle dot products one by one),
+    integer inputs checked bit for bit on every output (the oracle's binary64
+    library-matmul form is exact on integers)."""
+    w = wl.WORKLOADS[name]
+    M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
+    A, B = wl.workload_inputs(name)
+    got = run(A, B, M, N, K, ic, oc, tb)
+    assert not np.any(np.isnan(got)) and np.all(got >= 0)
+    rng = np.random.default_rng(w["index"])
+    rows, cols = _sample_positions(M, N, rng)
+    ref, absum = oracle.gemm_relu_ref_at(A, B, rows, cols, M, N, K, ic, tb)
+    check_close(got[rows, cols], ref, K, oc)
+    assert np.all(np.abs(got[rows, cols] - ref) <= fp32_sum_bound(absum, ref, K, unit_roundoff(oc)))
+    # about half of the outputs of a zero-mean product are clamped to zero
+    frac0 = float(np.mean(got == 0.0))
+    assert 0.4 < frac0 < 0.6
+
+    Ai, Bi = wl.workload_inputs(name, int_values=True)
+    goti = run(Ai, Bi, M, N, K, ic, oc, tb)
+    if M * N * K <= 2 ** 37:
+        refi = oracle.gemm_relu_ref_matmul(Ai, Bi, M, N, K, ic, tb)
+        assert np.abs(refi).max() < exact_limit(oc)
+        assert np.array_equal(goti, refi)
+    else:
+        # 8192^3: every output of 32 full rows and 32 full columns
+        rr = np.unique(np.concatenate([rng.integers(0, M, 30), [0, M - 1]]))
+        cc = np.unique(np.concatenate([rng.integers(0, N, 30), [0, N - 1]]))
+        r1, c1 = np.meshgrid(rr, np.arange(N), indexing="ij")
+        r2, c2 = np.meshgrid(np.arange(M), cc, indexing="ij")
+        rows = np.concatenate([r1.ravel(), r2.ravel()])
+        cols = np.concatenate([c1.ravel(), c2.ravel()])
+        refi, _ = oracle.gemm_relu_ref_at(Ai, Bi, rows, cols, M, N, K, ic, tb)
+        assert np.abs(refi).max() < exact_limit(oc)
+        assert np.array_equal(goti[rows, cols], refi)

@@ -1,0 +1,78 @@
+"""gfx950 lane layouts the kernel relies on, checked on the device.
+
+Each probe runs one wave on tiny in-bounds buffers through the same helpers the
+GEMM kernel uses (MFMA wrapper, LDS transpose read, direct global->LDS copy).
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import dense_tiled_gemm_relu_amd as gr
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def probe():
+    import torch
+    assert torch.cuda.is_available()
+    lib = ctypes.CDLL(gr.PROBE_LIB_PATH)
+    for name in ("probe_mfma_32x32x16", "probe_tr16", "probe_dma16"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.probe_mfma_32x32x16.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int]
+    lib.probe_tr16.argtypes = [ctypes.c_void_p] * 3
+    lib.probe_dma16.argtypes = [ctypes.c_void_p] * 3
+    return lib
+
+
+def _dev(arr):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+def test_mfma_32x32x16_layout(probe, dtype):
+    import torch
+    rng = np.random.default_rng(7)
+    x = rng.integers(-3, 4, size=(32, 16)).astype(np.float64)
+    y = rng.integers(-3, 4, size=(16, 32)).astype(np.float64)
+    X = _dev(wl.encode(x, dtype).view(np.int16))
+    Y = _dev(wl.encode(y, dtype).view(np.int16))
+    D = torch.zeros((32, 32), dtype=torch.float32, device="cuda")
+    assert probe.probe_mfma_32x32x16(X.data_ptr(), Y.data_ptr(), D.data_ptr(), dtype) == 0
+    assert np.array_equal(D.cpu().numpy().astype(np.float64), x @ y)
+
+
+def test_lds_transpose_read(probe):
+    """16 lanes read a 4 x 16 block, 8 bytes each (lane q: row q // 4, columns
+    4 (q % 4) .. +3); lane i then holds column i, rows 0..3."""
+    import torch
+    src = np.arange(4096, dtype=np.uint16)           # LDS viewed as 16 rows x 256
+    off = np.zeros(64, dtype=np.uint32)
+    want = np.zeros((64, 4), dtype=np.uint16)
+    for h in range(4):
+        r0, c0 = 4 * h, 16 * h + 8 * (h % 2)
+        for q in range(16):
+            off[16 * h + q] = ((r0 + q // 4) * 256 + c0 + 4 * (q % 4)) * 2
+            for e in range(4):
+                want[16 * h + q, e] = (r0 + e) * 256 + c0 + q
+    assert off.max() + 8 <= 8192 and np.all(off % 8 == 0)
+    out = torch.zeros(256, dtype=torch.int16, device="cuda")
+    assert probe.probe_tr16(_dev(src.view(np.int16)).data_ptr(),
+                            _dev(off.view(np.int32)).data_ptr(), out.data_ptr()) == 0
+    got = out.cpu().numpy().view(np.uint16).reshape(64, 4)
+    assert np.array_equal(got, want)
+
+
+def test_direct_global_to_lds_copy(probe):
+    """Lane l's 16 bytes land at LDS offset 16 l whatever global chunk it fetched."""
+    import torch
+    src = np.arange(512, dtype=np.uint16)
+    perm = ((np.arange(64) * 37 + 5) % 64).astype(np.uint32)
+    out = torch.zeros(512, dtype=torch.int16, device="cuda")
+    assert probe.probe_dma16(_dev(src.view(np.int16)).data_ptr(),
+                             _dev(perm.view(np.int32)).data_ptr(), out.data_ptr()) == 0
+    got = out.cpu().numpy().view(np.uint16).reshape(64, 8)
+    assert np.array_equal(got, src.reshape(64, 8)[perm])
