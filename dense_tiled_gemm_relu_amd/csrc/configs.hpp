@@ -12,6 +12,12 @@ namespace gemm_relu_hip {
 // bounds checks (any shape and alignment).
 enum ConfigId : int {
     CFG_D256x256x64_S2 = 0,
+    CFG_D256x256x32_S4,
+    CFG_D256x256x32_S5,
+    CFG_D256x256x32_S4_I,
+    CFG_D256x256x32_S4_W8I,
+    CFG_D256x256x32_S5_W8I,
+    CFG_D256x256x64_S2_W8,
     CFG_D128x128x64_S3,
     CFG_D64x64x64_S4,
     CFG_G128x128x64,
@@ -29,6 +35,12 @@ inline const ConfigInfo& config_info(int id)
 {
     static const ConfigInfo table[CFG_COUNT] = {
         {"d256x256x64_s2", 256, 256, true},
+        {"d256x256x32_s4", 256, 256, true},
+        {"d256x256x32_s5", 256, 256, true},
+        {"d256x256x32_s4_i", 256, 256, true},
+        {"d256x256x32_s4_w8i", 256, 256, true},
+        {"d256x256x32_s5_w8i", 256, 256, true},
+        {"d256x256x64_s2_w8", 256, 256, true},
         {"d128x128x64_s3", 128, 128, true},
         {"d64x64x64_s4", 64, 64, true},
         {"g128x128x64", 128, 128, false},
@@ -40,6 +52,24 @@ inline const ConfigInfo& config_info(int id)
 template <int IN, int OUT, bool TB, int id> struct CfgOf;
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x64_S2> {
     using type = Cfg<IN, OUT, TB, 256, 256, 64, 2, 2, 2, true>;
+};
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4> {
+    using type = Cfg<IN, OUT, TB, 256, 256, 32, 2, 2, 4, true>;
+};
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S5> {
+    using type = Cfg<IN, OUT, TB, 256, 256, 32, 2, 2, 5, true>;
+};
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I> {
+    using type = Cfg<IN, OUT, TB, 256, 256, 32, 2, 2, 4, true, true>;
+};
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_W8I> {
+    using type = Cfg<IN, OUT, TB, 256, 256, 32, 2, 4, 4, true, true>;
+};
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S5_W8I> {
+    using type = Cfg<IN, OUT, TB, 256, 256, 32, 2, 4, 5, true, true>;
+};
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_W8> {
+    using type = Cfg<IN, OUT, TB, 256, 256, 64, 2, 4, 2, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D128x128x64_S3> {
     using type = Cfg<IN, OUT, TB, 128, 128, 64, 2, 2, 3, true>;
@@ -82,6 +112,18 @@ LaunchFn launcher_bf16_nt(int out_dt, int cfg);
         switch (cfg) {                                                                     \
         case CFG_D256x256x64_S2:                                                           \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2>::type>;     \
+        case CFG_D256x256x32_S4:                                                           \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4>::type>;     \
+        case CFG_D256x256x32_S5:                                                           \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S5>::type>;     \
+        case CFG_D256x256x32_S4_I:                                                         \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I>::type>;   \
+        case CFG_D256x256x32_S4_W8I:                                                       \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_W8I>::type>; \
+        case CFG_D256x256x32_S5_W8I:                                                       \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S5_W8I>::type>; \
+        case CFG_D256x256x64_S2_W8:                                                        \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_W8>::type>;  \
         case CFG_D128x128x64_S3:                                                           \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D128x128x64_S3>::type>;     \
         case CFG_D64x64x64_S4:                                                             \

@@ -24,6 +24,7 @@ struct Env {
     bool sync = false;
     int force_cfg = -1;   // GEMM_RELU_FORCE_CONFIG=<name>
     int panel = 0;        // GEMM_RELU_PANEL=<tile rows>, 0 = default
+    int nxcd = 8;         // GEMM_RELU_XCDS=<n>: 1 disables the XCD-aware tile remap
 };
 
 // Debug and tuning switches, read on every call so a process can change them
@@ -40,6 +41,8 @@ Env env()
     }
     const char* p = std::getenv("GEMM_RELU_PANEL");
     if (p && p[0]) e.panel = std::atoi(p);
+    const char* x = std::getenv("GEMM_RELU_XCDS");
+    if (x && x[0]) e.nxcd = std::atoi(x) > 0 ? std::atoi(x) : 1;
     return e;
 }
 
@@ -137,9 +140,10 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     if (forced >= 0 && (!config_info(forced).direct || direct)) {
         cfg = forced;
     } else if (direct) {
-        // Largest tile that still gives every CU at least one workgroup.
-        if (tiles(CFG_D256x256x64_S2) >= kNumCUs)
-            cfg = CFG_D256x256x64_S2;
+        // Largest tile that still gives every CU at least one workgroup; the
+        // 256x256 tile runs the interleaved 4-stage pipeline.
+        if (tiles(CFG_D256x256x32_S4_I) >= kNumCUs)
+            cfg = CFG_D256x256x32_S4_I;
         else if (tiles(CFG_D128x128x64_S3) >= kNumCUs)
             cfg = CFG_D128x128x64_S3;
         else
@@ -187,6 +191,7 @@ extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64
     args.tiles_n = p.tiles_n;
     const int panel = e.panel > 0 ? e.panel : 8;
     args.panel = panel < p.tiles_m ? panel : p.tiles_m;
+    args.nxcd = e.nxcd;
 
     LaunchFn fn = pick_launcher(in_dtype, out_dtype, transB, p.cfg);
     if (!fn) return GEMM_RELU_EUNSUPPORTED;

@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gemm_relu_hip {
 
 enum : int { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2 };
@@ -48,6 +50,7 @@ struct KernelArgs {
     int M, N, K;
     int tiles_m, tiles_n;
     int panel;                // tile rows per rasterisation panel (>= 1)
+    int nxcd;                 // XCDs the dispatcher round-robins over (1 = no remap)
 };
 
 // 16 zero bytes in global memory: the source of K-tail chunks of the direct loader.
@@ -146,10 +149,10 @@ template <> struct OutTraits<DT_F32> {
 
 // ---------------------------------------------------------- configuration
 template <int IN_DT_, int OUT_DT_, bool TRANS_B_, int BM_, int BN_, int BK_, int WAVES_M_,
-          int WAVES_N_, int STAGES_, bool DIRECT_>
+          int WAVES_N_, int STAGES_, bool DIRECT_, bool INTERLEAVE_ = false>
 struct Cfg {
     static constexpr int IN_DT = IN_DT_, OUT_DT = OUT_DT_;
-    static constexpr bool TRANS_B = TRANS_B_, DIRECT = DIRECT_;
+    static constexpr bool TRANS_B = TRANS_B_, DIRECT = DIRECT_, INTERLEAVE = INTERLEAVE_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
     static constexpr int NWAVES = WAVES_M * WAVES_N;
@@ -173,29 +176,59 @@ struct Cfg {
     static_assert(BK == 32 || BK == 64, "BK");
     static_assert(A_CH % NTHREADS == 0 && B_CH % NTHREADS == 0, "loader tiling");
     static_assert(TRANS_B || BN >= 64, "n-contiguous B rows need >= 8 chunks for the swizzle");
-    static_assert(TRANS_B || TN == 1 || TN % 2 == 0, "B read offsets assume TN even or 1");
-    static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+        static_assert(STAGES >= 2 && STAGES <= 5, "stages");
     static_assert((STAGES - 2) * LOADS_PER_STAGE < 64, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity of a gfx950 CU");
+
+    // Interleaved direct pipeline: the LOADS_PER_STAGE copies of the stage
+    // STAGES-1 ahead are spread over the KSUB k-steps of a BK step, one per
+    // scheduling region; each region also carries a share of the next
+    // k-step's fragment reads and of the current k-step's MFMAs.
+    static constexpr int NM = TM * TN;                          // MFMAs per k-step
+    static constexpr int NR = TM + (TRANS_B ? TN : 2 * TN);     // LDS read ops per k-step
+    static constexpr int REGIONS = LOADS_PER_STAGE / KSUB;      // = copies per k-step
+    static_assert(!INTERLEAVE || (DIRECT && STAGES >= 3), "interleave needs >= 3 direct stages");
+    static_assert(!INTERLEAVE || (LOADS_PER_STAGE % KSUB == 0 && REGIONS >= 1 &&
+                                  NM % REGIONS == 0),
+                  "interleave: copies and MFMAs must split evenly over the regions");
+    // Copies issued after the last copy of stage t+1 when the wave waits for it
+    // (start of the last k-step of step t) in the steady state: the whole of
+    // stages t+2 .. t+S-2 and the first KSUB-1 k-steps' share of stage t+S-1.
+    static constexpr int STEADY_ALLOWANCE =
+        (STAGES - 3) * LOADS_PER_STAGE + (KSUB - 1) * (LOADS_PER_STAGE / KSUB);
+    static_assert(!INTERLEAVE || STEADY_ALLOWANCE < 64, "vmcnt range");
 };
 
-// XOR swizzle of a k-contiguous tile row (A, or B stored (N,K)).  Rows that
-// share one 128-byte line of LDS banks get distinct 16 B chunk positions, so
-// the 8 lanes reading the same logical chunk of 8 consecutive rows never
-// collide.
+// LDS banks on gfx950: 64 banks x 4 bytes, so one cycle serves 256 bytes —
+// 16 lanes of a 16-byte read, 32 lanes of an 8-byte read.  The swizzles below
+// make those lane groups hit 16 distinct 16-byte bank groups.
+
+// XOR swizzle of a k-contiguous tile row (A, or B stored (N,K)) of ROW_CH
+// chunks: RPW = 16 / ROW_CH rows share one 256-byte bank window, and the
+// 16 lanes that read one logical chunk of 16 consecutive rows land on
+// (row mod RPW, chunk ^ swz) pairs that are all distinct.
 template <int ROW_CH>
 __device__ __forceinline__ int swz_krow(int r)
 {
-    if constexpr (ROW_CH >= 8)
-        return r & 7;
+    if constexpr (ROW_CH >= 16)
+        return r & 15;
     else
-        return (r / (8 / ROW_CH)) % ROW_CH;
+        return (r / (16 / ROW_CH)) % ROW_CH;
 }
 
-// XOR swizzle of an n-contiguous B row (B stored (K,N)).  A transpose read
-// touches 4 consecutive k rows x 2 chunks per 16 lanes; XOR-ing the chunk
-// index with 2*(k mod 4) spreads those 8 chunks over distinct positions.
-__device__ __forceinline__ int swz_nrow(int k) { return 2 * (k & 3); }
+// XOR swizzle of an n-contiguous B row (B stored (K,N)) of NROW_CH chunks.
+// A transpose read serves 32 lanes per cycle: 4 consecutive k rows x 4
+// consecutive chunks (64 bytes of n).  XOR-ing the chunk index with
+// 4 (k mod 4) puts the 4 rows on 4 disjoint chunk quads of the bank window;
+// with 8-chunk rows two rows share a window, so 4 ((k / 2) mod 2) suffices.
+template <int NROW_CH>
+__device__ __forceinline__ int swz_nrow(int k)
+{
+    if constexpr (NROW_CH >= 16)
+        return 4 * (k & 3);
+    else
+        return 4 * ((k >> 1) & 1);
+}
 
 // ------------------------------------------------------------ tile order
 // Workgroup id -> (tile row, tile col).  First an XCD-aware remap: the
@@ -203,13 +236,12 @@ __device__ __forceinline__ int swz_nrow(int k) { return 2 * (k & 3); }
 // give every XCD one contiguous run of the logical order.  Then a panel
 // swizzle: the logical order walks a panel of `panel` tile rows column by
 // column, so tiles resident together share A row panels and B column panels.
-__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int panel,
+__device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int panel, int nxcd,
                                             int& tm, int& tn)
 {
-    constexpr int NXCD = 8;
     const int total = tiles_m * tiles_n;
-    const int per = total / NXCD, rem = total % NXCD;
-    const int xcd = wg % NXCD, local = wg / NXCD;
+    const int per = total / nxcd, rem = total % nxcd;
+    const int xcd = wg % nxcd, local = wg / nxcd;
     const int logical = xcd < rem ? xcd * (per + 1) + local
                                   : rem * (per + 1) + (xcd - rem) * per + local;
     const int panel_tiles = panel * tiles_n;
@@ -238,7 +270,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     int tm, tn;
-    tile_coords(blockIdx.x, args.tiles_m, args.tiles_n, args.panel, tm, tn);
+    tile_coords(blockIdx.x, args.tiles_m, args.tiles_n, args.panel, args.nxcd, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int nk = (K + BK - 1) / BK;
 
@@ -274,7 +306,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
             b_ok[i] = (n0 + r) < N;
         } else {
             const int k = q / NROW_CH, p = q % NROW_CH;
-            const int c = p ^ swz_nrow(k);
+            const int c = p ^ swz_nrow<NROW_CH>(k);
             const int col = min(n0 + 8 * c, N - 8) - n0;     // direct path: N % 8 == 0
             b_src[i] = (uint32_t)k * (uint32_t)N * 2u + (uint32_t)col * 2u;
             b_kch[i] = k;
@@ -357,7 +389,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
                                                    k0 + b_kch[i], K, b_ok[i], b_vec);
             } else {
                 const int k = q / NROW_CH, p = q % NROW_CH;
-                const int c = p ^ swz_nrow(k);
+                const int c = p ^ swz_nrow<NROW_CH>(k);
                 rb[C::DIRECT ? 0 : i] = load_chunk(args.B, (size_t)(k0 + k) * (size_t)N * 2u,
                                                    n0 + 8 * c, N, k0 + k < K, b_vec);
             }
@@ -387,7 +419,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         const int r = wm0 + l32;
         a_rd[s] = (uint32_t)(r * BK * 2 + (((2 * s + g) ^ swz_krow<ROW_CH>(r)) * 16));
     }
-    uint32_t b_rd[C::TRANS_B ? KSUB : 4];
+    uint32_t b_rd[C::TRANS_B ? KSUB : TN];
     if constexpr (C::TRANS_B) {
 #pragma unroll
         for (int s = 0; s < KSUB; ++s) {
@@ -397,20 +429,18 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     } else {
         // Transpose read: 16-lane group h reads a 4 (k) x 16 (n) block; lane i16 of
         // the group supplies row kk = 8 (h / 2) + i16 / 4 (+ 4 t + 16 s) and the
-        // 4 columns 16 (h % 2) + 4 (i16 % 4) of the 32-column MFMA block, and
-        // receives the 4 k values of column 16 (h % 2) + i16.
+        // 4 columns 16 (h % 2) + 4 (i16 % 4) of the 32-column MFMA block j, and
+        // receives the 4 k values of column 16 (h % 2) + i16.  The swizzle of
+        // row kk equals that of kk + 4 t + 16 s, so one offset per block serves
+        // every (s, t).
         const int h = lane >> 4, i16 = lane & 15;
         const int kk = 8 * (h >> 1) + (i16 >> 2);
-        const int x = swz_nrow(kk);
 #pragma unroll
-        for (int par = 0; par < 2; ++par) {
-            // 32-column block J = wn0/32 + j with parity par (j's high part adds 128 B per pair)
-            const int J = wn0 / 32 + par;
-            const int chunk = 4 * J + 2 * (h & 1) + ((i16 >> 1) & 1);
-            const int phys = chunk ^ x;
-            b_rd[par] = (uint32_t)(kk * BN * 2 + phys * 16 + (i16 & 1) * 8);
+        for (int j = 0; j < TN; ++j) {
+            const int n = wn0 + 32 * j + 16 * (h & 1) + 4 * (i16 & 3);
+            const int phys = (n >> 3) ^ swz_nrow<NROW_CH>(kk);
+            b_rd[j] = (uint32_t)(kk * BN * 2 + phys * 16 + (n & 7) * 2);
         }
-        b_rd[2] = b_rd[3] = 0;
     }
 
     f32x16_t acc[TM][TN];
@@ -425,6 +455,26 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     struct Frags {
         i16x8_t a[TM], b[TN];
     };
+    // One LDS read op q of k-step s: q < TM reads A block q; the rest read B
+    // block j (transposed B: one 16-byte read; (K,N) B: two transpose reads,
+    // the k halves 0..3 and 4..7 of the block).
+    auto read_op = [&](int stage, int s, int q, Frags& f) {
+        const GR_LDS unsigned char* sa = smem + stage * C::STAGE_BYTES;
+        const GR_LDS unsigned char* sb = sa + C::A_BYTES;
+        if (q < TM) {
+            f.a[q] = lds_read_b128(sa + a_rd[s] + q * 32 * BK * 2);
+        } else if constexpr (C::TRANS_B) {
+            const int j = q - TM;
+            f.b[j] = lds_read_b128(sb + b_rd[s] + j * 32 * BK * 2);
+        } else {
+            const int j = (q - TM) >> 1, half = (q - TM) & 1;
+            const i16x4_t v = lds_read_tr16(sb + b_rd[j] + s * 16 * BN * 2 + half * 4 * BN * 2);
+            if (half == 0)
+                f.b[j].lo = v;
+            else
+                f.b[j].hi = v;
+        }
+    };
     auto read_frags = [&](int stage, int s, Frags& f) {
         const GR_LDS unsigned char* sa = smem + stage * C::STAGE_BYTES;
         const GR_LDS unsigned char* sb = sa + C::A_BYTES;
@@ -435,8 +485,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
             if constexpr (C::TRANS_B) {
                 f.b[j] = lds_read_b128(sb + b_rd[s] + j * 32 * BK * 2);
             } else {
-                const int hi = (TN == 1) ? 0 : (j >> 1) * 128;
-                const GR_LDS unsigned char* p = sb + b_rd[j & 1] + hi + s * 16 * BN * 2;
+                const GR_LDS unsigned char* p = sb + b_rd[j] + s * 16 * BN * 2;
                 const i16x4_t lo4 = lds_read_tr16(p);
                 const i16x4_t hi4 = lds_read_tr16(p + 4 * BN * 2);
                 f.b[j] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -454,7 +503,101 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     };
 
     Frags fr[2];
-    if constexpr (C::DIRECT) {
+    if constexpr (C::INTERLEAVE) {
+        constexpr int R = C::REGIONS, NM = C::NM, NR = C::NR, LS = C::LOADS_PER_STAGE / KSUB;
+        // one copy (index l of the stage's LOADS_PER_STAGE) of stage t into its buffer
+        auto issue_one = [&](int t, int stage, int l) {
+            const int k0 = t * BK;
+            const uint32_t sa = smem_addr + stage * C::STAGE_BYTES;
+            const uint32_t sb = sa + C::A_BYTES;
+            const unsigned char* ga = a_tile + (size_t)k0 * 2u;
+            const unsigned char* gb = C::TRANS_B ? b_tile + (size_t)k0 * 2u
+                                                 : b_tile + (size_t)k0 * (size_t)N * 2u;
+            const unsigned char* zero = reinterpret_cast<const unsigned char*>(g_zero16);
+            const bool full = k0 + BK <= K;
+            if (l < APT) {
+                const uint32_t dst = sa + (l * C::NWAVES + wave) * 1024;
+                if (full) dma16(ga, a_src[l], dst);
+                else dma16_abs((k0 + a_kch[l] < K) ? ga + a_src[l] : zero, dst);
+            } else {
+                const int i = l - APT;
+                const uint32_t dst = sb + (i * C::NWAVES + wave) * 1024;
+                if (full) dma16(gb, b_src[i], dst);
+                else dma16_abs((k0 + b_kch[i] < K) ? gb + b_src[i] : zero, dst);
+            }
+        };
+        // MFMA p of a k-step: B block p / TM against A block p % TM
+        auto mfma_op = [&](const Frags& f, int p) {
+            const int j = p / TM, i = p % TM;
+            acc[i][j] = mfma_32x32x16<C::IN_DT>(f.b[j], f.a[i], acc[i][j]);
+        };
+
+#pragma unroll
+        for (int st = 0; st < S - 1; ++st)
+            if (st < nk) issue_direct(st, st);
+        if (nk > 0) {
+            if (nk - 1 >= S - 2)
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 2) * C::LOADS_PER_STAGE));
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            barrier_lds();
+#pragma unroll
+            for (int q = 0; q < NR; ++q) read_op(0, 0, q, fr[0]);
+        }
+        // One BK step.  STEADY: the stage S-1 ahead exists and lies wholly inside
+        // K, so the step needs no run-time checks.
+        auto step = [&](int t, auto steady_tag) {
+            constexpr bool STEADY = decltype(steady_tag)::value;
+            const int stage = t % S;
+            const bool loads = STEADY || t + S - 1 < nk;
+            const int ld_stage = (t + S - 1) % S;
+            const int ld_k0 = (t + S - 1) * BK;
+            const unsigned char* ga = a_tile + (size_t)ld_k0 * 2u;
+            const unsigned char* gb = C::TRANS_B ? b_tile + (size_t)ld_k0 * 2u
+                                                 : b_tile + (size_t)ld_k0 * (size_t)N * 2u;
+            const uint32_t lsa = smem_addr + ld_stage * C::STAGE_BYTES;
+            const uint32_t lsb = lsa + C::A_BYTES;
+#pragma unroll
+            for (int s = 0; s < KSUB; ++s) {
+                const bool last = s + 1 == KSUB;
+                if (last && (STEADY || t + 1 < nk)) {
+                    if (loads)
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::STEADY_ALLOWANCE));
+                    else
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+                    barrier_lds();
+                }
+                const bool reads = !last || STEADY || t + 1 < nk;
+                const int rd_stage = last ? (t + 1) % S : stage;
+                const int rd_s = last ? 0 : s + 1;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int l = s * LS + r;
+                    if constexpr (STEADY) {
+                        if (l < APT)
+                            dma16(ga, a_src[l], lsa + (l * C::NWAVES + wave) * 1024);
+                        else
+                            dma16(gb, b_src[l - APT], lsb + ((l - APT) * C::NWAVES + wave) * 1024);
+                    } else {
+                        if (loads) issue_one(t + S - 1, ld_stage, l);
+                    }
+                    if (reads) {
+#pragma unroll
+                        for (int q = r * NR / R; q < (r + 1) * NR / R; ++q)
+                            read_op(rd_stage, rd_s, q, fr[(s + 1) & 1]);
+                    }
+#pragma unroll
+                    for (int p = r * NM / R; p < (r + 1) * NM / R; ++p) mfma_op(fr[s & 1], p);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+        // steady steps: stage t+S-1 < nk and its k range ends inside K
+        const int t_steady = max(0, min(nk, K / BK) - (S - 1));
+        for (int t = 0; t < t_steady; ++t) step(t, std::integral_constant<bool, true>{});
+        for (int t = t_steady; t < nk; ++t) step(t, std::integral_constant<bool, false>{});
+    } else if constexpr (C::DIRECT) {
         // Pipeline: S-1 stages in flight ahead of the one being contracted.
         // At the last k-step of stage t the wave waits for stage t+1, meets the
         // others at a barrier (which also retires every read of stage t, so its

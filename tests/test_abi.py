@@ -78,9 +78,9 @@ def test_null_operands_allowed_when_K_is_zero():
 
 
 @pytest.mark.parametrize("M,N,K,transB,aligned,want", [
-    (8192, 8192, 8192, 0, True, "d256x256x64_s2"),
-    (4096, 4096, 4096, 0, True, "d256x256x64_s2"),
-    (4096, 7168, 4096, 1, True, "d256x256x64_s2"),
+    (8192, 8192, 8192, 0, True, "d256x256x32_s4_i"),
+    (4096, 4096, 4096, 0, True, "d256x256x32_s4_i"),
+    (4096, 7168, 4096, 1, True, "d256x256x32_s4_i"),
     (256, 256, 256, 0, True, "d64x64x64_s4"),
     (64, 8192, 8192, 0, True, "d64x64x64_s4"),
     (2048, 2048, 512, 0, True, "d128x128x64_s3"),
