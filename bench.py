@@ -55,6 +55,61 @@ def measured_traffic(workload, launches_per_record=None):
     return rec.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 256 * 1024 * 1024
+
+
+def calibrate_copy():
+    """Three plain device copies of COPY_BYTES (torch copy_), for scaling the
+    FETCH_SIZE / WRITE_SIZE counters: the copy reads and writes exactly
+    COPY_BYTES per dispatch."""
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("copied %d bytes x 3" % COPY_BYTES)
+
+
+def _pmc_per_dispatch(csv_dir, counter, kernel_substr):
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit("no %s rows for %s under %s" % (counter, kernel_substr, csv_dir))
+    v = sorted(vals.items(), key=lambda kv: int(kv[0]))
+    return [x for _, x in v]
+
+
+def ingest_traffic(workload, fetch_dir, write_dir, copyf_dir, copyw_dir):
+    """HBM bytes per launch of the GEMM kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the plain copy of COPY_BYTES.  Writes
+    profiles/traffic_<workload>.json stamped with the kernel source hash."""
+    f = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", "gemm_relu_kernel")[1:]   # drop first (cold)
+    w = _pmc_per_dispatch(write_dir, "WRITE_SIZE", "gemm_relu_kernel")[1:]
+    cf = _pmc_per_dispatch(copyf_dir, "FETCH_SIZE", "copyBuffer")
+    cw = _pmc_per_dispatch(copyw_dir, "WRITE_SIZE", "copyBuffer")
+    kib = 1024.0
+    fetch_scale = COPY_BYTES / (sum(cf) / len(cf) * kib)
+    write_scale = COPY_BYTES / (sum(cw) / len(cw) * kib)
+    fetch = sum(f) / len(f) * kib * fetch_scale
+    write = sum(w) / len(w) * kib * write_scale
+    rec = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+           "fetch_bytes_per_launch": int(fetch), "write_bytes_per_launch": int(write),
+           "hbm_bytes_per_launch": int(fetch + write),
+           "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+           "raw_fetch_kib": [round(x) for x in f], "raw_write_kib": [round(x) for x in w]}
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(w, A, B, target_s=15.0):
     """The oracle, untuned, on a bounded sample of the same workload: the first
     R rows of A against all of B (R x N x K multiply-adds), R sized so the run
@@ -82,15 +137,25 @@ def cpu_baseline(w, A, B, target_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gemm_relu_f16_8192", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only the plain copy used to scale HBM byte counters")
+    ap.add_argument("--ingest-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"),
+                    help="rocprofv3 --pmc output dirs -> profiles/traffic_<workload>.json")
     args = ap.parse_args()
+    if args.ingest_traffic:
+        ingest_traffic(args.workload, *args.ingest_traffic)
+        return
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the fused GEMM+ReLU has no multi-GPU path in this "
-              "library (an M or N split needs no exchange; see the design notes). "
+              "library (an M or N split of C would need no exchange between GPUs). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
