@@ -84,13 +84,16 @@ struct Plan {
     int tiles_m = 0, tiles_n = 0;
 };
 
-bool direct_ok(const void* A, const void* B, const void* C, int64_t N, int64_t K, int out_dt)
+// A direct-copy configuration needs its 32-bit copy offsets to fit (a tile's
+// rows of A or transposed B span BM * K * 2 bytes; a (K,N) B step spans
+// BK * N * 2 bytes) and, for a (K,N) B, at least one full tile of columns: the
+// last tile column is moved back to end at N.  Any 2-byte alignment is fine.
+bool direct_fits(int id, int64_t N, int64_t K, int transB)
 {
-    const uintptr_t mask = 15;
-    return (K % 8 == 0) && (N % 8 == 0) && K <= (int64_t(1) << 22) && N <= (int64_t(1) << 24) &&
-           ((reinterpret_cast<uintptr_t>(A) & mask) == 0) &&
-           ((reinterpret_cast<uintptr_t>(B) & mask) == 0) &&
-           ((reinterpret_cast<uintptr_t>(C) & mask) == 0) && out_dt >= 0;
+    const ConfigInfo& ci = config_info(id);
+    if (!ci.direct) return true;
+    if (K > (int64_t(1) << 22) || N > (int64_t(1) << 24)) return false;
+    return transB || N >= ci.bn;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -133,23 +136,24 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
         return p;
     }
 
-    const bool direct = direct_ok(A, B, C, N, K, out_dt);
     auto tiles = [&](int id) { return ceil_div(M, config_info(id).bm) * ceil_div(N, config_info(id).bn); };
-    int cfg;
+    auto usable = [&](int id) { return direct_fits(id, N, K, transB); };
+    // Estimated time of a direct configuration: rounds of workgroups over the
+    // CUs times the tile area over the tile's MFMA efficiency relative to the
+    // 256x256 tile (measured on MI355X: 128x128 ~0.57, 64x64 ~0.5).
+    auto cost = [&](int id) {
+        const ConfigInfo& ci = config_info(id);
+        const double eff = ci.bm >= 256 ? 1.0 : ci.bm >= 128 ? 0.57 : 0.5;
+        return double(ceil_div(tiles(id), kNumCUs)) * ci.bm * ci.bn / eff;
+    };
+    int cfg = -1;
     const int forced = e.force_cfg;
-    if (forced >= 0 && (!config_info(forced).direct || direct)) {
+    if (forced >= 0 && usable(forced)) {
         cfg = forced;
-    } else if (direct) {
-        // Largest tile that still gives every CU at least one workgroup; the
-        // 256x256 tile runs the interleaved 4-stage pipeline.
-        if (tiles(CFG_D256x256x32_S4_I) >= kNumCUs)
-            cfg = CFG_D256x256x32_S4_I;
-        else if (tiles(CFG_D128x128x64_S3) >= kNumCUs)
-            cfg = CFG_D128x128x64_S3;
-        else
-            cfg = CFG_D64x64x64_S4;
     } else {
-        cfg = tiles(CFG_G128x128x64) >= kNumCUs ? CFG_G128x128x64 : CFG_G64x64x64;
+        for (int id : {CFG_D256x256x32_S4_I, CFG_D128x128x64_S3, CFG_D64x64x64_S4})
+            if (usable(id) && (cfg < 0 || cost(id) < cost(cfg))) cfg = id;
+        if (cfg < 0) cfg = tiles(CFG_G128x128x64) >= kNumCUs ? CFG_G128x128x64 : CFG_G64x64x64;
     }
     const int64_t tm = ceil_div(M, config_info(cfg).bm), tn = ceil_div(N, config_info(cfg).bn);
     if (tm * tn > lim) {

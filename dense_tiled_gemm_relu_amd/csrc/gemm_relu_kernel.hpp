@@ -53,9 +53,6 @@ struct KernelArgs {
     int nxcd;                 // XCDs the dispatcher round-robins over (1 = no remap)
 };
 
-// 16 zero bytes in global memory: the source of K-tail chunks of the direct loader.
-__device__ __attribute__((aligned(16))) const unsigned int g_zero16[4] = {0u, 0u, 0u, 0u};
-
 // ------------------------------------------------------------------ helpers
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4]<<14).
 __host__ __device__ constexpr int waitcnt_vm(int n)
@@ -84,16 +81,6 @@ __device__ __forceinline__ void dma16(const unsigned char* gbase, uint32_t voff,
                  "global_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(voff), "s"(gbase), "s"(lds)
-                 : "memory", "m0");
-}
-
-__device__ __forceinline__ void dma16_abs(const unsigned char* gaddr, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %1\n\t"
-                 "s_nop 0\n\t"
-                 "global_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gaddr), "s"(lds)
                  : "memory", "m0");
 }
 
@@ -271,46 +258,49 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
 
     int tm, tn;
     tile_coords(blockIdx.x, args.tiles_m, args.tiles_n, args.panel, args.nxcd, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int nk = (K + BK - 1) / BK;
+    const int m0 = tm * BM;
+    // (K,N) B on the direct path: the last tile column is moved back to end at N,
+    // so every B chunk it copies lies inside its row (the columns it shares with
+    // its neighbour are recomputed bit for bit and stored twice).
+    const int n0 = (C::DIRECT && !C::TRANS_B) ? min(tn * BN, N - BN) : tn * BN;
+    // Direct path: K / BK full steps through the copy pipeline plus, if K % BK,
+    // one register-staged tail step.  Register-staged path: ceil(K / BK) steps.
+    const int nk = C::DIRECT ? K / BK : (K + BK - 1) / BK;
 
     // ---- loader geometry: this thread owns LDS slots q = i*NTHREADS + tid of
     // each stage region; a wave's 64 slots are contiguous (one 1 KiB DMA write).
     // For every slot, the logical (row, chunk) it holds and the byte offset of
     // that chunk's source relative to the tile's global origin.
+    // Slot q of a k-contiguous region holds row q / ROW_CH, logical chunk
+    // (q % ROW_CH) ^ swz; slot q of an n-contiguous B region holds k row
+    // q / NROW_CH, logical chunk (q % NROW_CH) ^ swz.
+    auto krow_slot = [&](int q, int& r, int& c) {
+        r = q / ROW_CH;
+        c = (q % ROW_CH) ^ swz_krow<ROW_CH>(r);
+    };
+    auto nrow_slot = [&](int q, int& k, int& c) {
+        k = q / NROW_CH;
+        c = (q % NROW_CH) ^ swz_nrow<NROW_CH>(k);
+    };
     uint32_t a_src[APT];
-    int a_kch[APT];      // k index of the chunk's first element within the step
-    int a_row_ok[APT];
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
-        const int q = i * C::NTHREADS + tid;
-        const int r = q / ROW_CH, p = q % ROW_CH;
-        const int c = p ^ swz_krow<ROW_CH>(r);
+        int r, c;
+        krow_slot(i * C::NTHREADS + tid, r, c);
         const int row = min(m0 + r, M - 1) - m0;           // clamp: finite data, output discarded
         a_src[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)c * 16u;
-        a_kch[i] = c * 8;
-        a_row_ok[i] = (m0 + r) < M;
     }
     uint32_t b_src[BPT];
-    int b_kch[BPT];      // transposed B: k of the chunk; (K,N) B: k row of the chunk
-    int b_ok[BPT];
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
-        const int q = i * C::NTHREADS + tid;
+        int r, c;
         if constexpr (C::TRANS_B) {
-            const int r = q / ROW_CH, p = q % ROW_CH;
-            const int c = p ^ swz_krow<ROW_CH>(r);
+            krow_slot(i * C::NTHREADS + tid, r, c);
             const int row = min(n0 + r, N - 1) - n0;
             b_src[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)c * 16u;
-            b_kch[i] = c * 8;
-            b_ok[i] = (n0 + r) < N;
         } else {
-            const int k = q / NROW_CH, p = q % NROW_CH;
-            const int c = p ^ swz_nrow<NROW_CH>(k);
-            const int col = min(n0 + 8 * c, N - 8) - n0;     // direct path: N % 8 == 0
-            b_src[i] = (uint32_t)k * (uint32_t)N * 2u + (uint32_t)col * 2u;
-            b_kch[i] = k;
-            b_ok[i] = (n0 + 8 * c) < N;
+            nrow_slot(i * C::NTHREADS + tid, r, c);
+            b_src[i] = (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u;
         }
     }
 
@@ -327,38 +317,28 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         const unsigned char* ga = a_tile + (size_t)k0 * 2u;
         const unsigned char* gb = C::TRANS_B ? b_tile + (size_t)k0 * 2u
                                              : b_tile + (size_t)k0 * (size_t)N * 2u;
-        if (k0 + BK <= K) {
+        // every pipelined step lies inside K and every chunk inside its row
 #pragma unroll
-            for (int i = 0; i < APT; ++i) dma16(ga, a_src[i], sa + (i * C::NWAVES + wave) * 1024);
+        for (int i = 0; i < APT; ++i) dma16(ga, a_src[i], sa + (i * C::NWAVES + wave) * 1024);
 #pragma unroll
-            for (int i = 0; i < BPT; ++i) dma16(gb, b_src[i], sb + (i * C::NWAVES + wave) * 1024);
-        } else {
-            // K tail (K % 8 == 0 on this path, so a chunk is wholly in or out):
-            // chunks past K fetch 16 zero bytes instead.
-            const unsigned char* zero = reinterpret_cast<const unsigned char*>(g_zero16);
-#pragma unroll
-            for (int i = 0; i < APT; ++i)
-                dma16_abs((k0 + a_kch[i] < K) ? ga + a_src[i] : zero,
-                          sa + (i * C::NWAVES + wave) * 1024);
-#pragma unroll
-            for (int i = 0; i < BPT; ++i)
-                dma16_abs((k0 + b_kch[i] < K) ? gb + b_src[i] : zero,
-                          sb + (i * C::NWAVES + wave) * 1024);
-        }
+        for (int i = 0; i < BPT; ++i) dma16(gb, b_src[i], sb + (i * C::NWAVES + wave) * 1024);
     };
 
-    // ---- register-staged loader for any alignment: element-wise bounds checks,
-    // zero fill outside the matrix, then one 16 B LDS write per chunk.
-    u32x4_t ra[C::DIRECT ? 1 : APT], rb[C::DIRECT ? 1 : BPT];
+    // ---- register-staged loader: 16 B loads where a chunk lies inside its row
+    // (any 2-byte alignment: the loads run in unaligned-access mode), element-wise
+    // loads with zero fill where it crosses the end of the row or the matrix,
+    // then one 16 B LDS write per chunk.  The whole step of the register-staged
+    // configurations; the K tail step of the direct ones.
+    u32x4_t ra[APT], rb[BPT];
     auto load_chunk = [&](const unsigned char* base, size_t row_off, int e0, int e_lim,
-                          bool row_ok, bool vec_ok) -> u32x4_t {
+                          bool row_ok) -> u32x4_t {
         // 8 consecutive 16-bit elements e0 .. e0+7 of one row; valid if e < e_lim.
         u32x4_t v = {0u, 0u, 0u, 0u};
         if (!row_ok) return v;
         const unsigned short* p =
             reinterpret_cast<const unsigned short*>(base + row_off) + e0;
-        if (vec_ok && e0 + 8 <= e_lim) {
-            v = *reinterpret_cast<const u32x4_t*>(p);
+        if (e0 + 8 <= e_lim) {
+            __builtin_memcpy(&v, p, 16);
         } else {
             unsigned short h[8];
 #pragma unroll
@@ -368,44 +348,57 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         }
         return v;
     };
-    const bool a_vec = ((K & 7) == 0) && ((reinterpret_cast<uintptr_t>(args.A) & 15) == 0);
-    const bool b_vec = (C::TRANS_B ? ((K & 7) == 0) : ((N & 7) == 0)) &&
-                       ((reinterpret_cast<uintptr_t>(args.B) & 15) == 0);
+    // chunk of slot q of stage t: A rows m0.., transposed-B rows n0.., (K,N)-B
+    // rows k0.. with columns n0..
+    auto a_chunk = [&](int t, int q) -> u32x4_t {
+        int r, c;
+        krow_slot(q, r, c);
+        return load_chunk(args.A, (size_t)(m0 + r) * (size_t)K * 2u, t * BK + 8 * c, K, m0 + r < M);
+    };
+    auto b_chunk = [&](int t, int q) -> u32x4_t {
+        int r, c;
+        if constexpr (C::TRANS_B) {
+            krow_slot(q, r, c);
+            return load_chunk(args.B, (size_t)(n0 + r) * (size_t)K * 2u, t * BK + 8 * c, K,
+                              n0 + r < N);
+        } else {
+            nrow_slot(q, r, c);
+            return load_chunk(args.B, (size_t)(t * BK + r) * (size_t)N * 2u, n0 + 8 * c, N,
+                              t * BK + r < K);
+        }
+    };
     auto load_staged = [&](int t) {
-        const int k0 = t * BK;
 #pragma unroll
-        for (int i = 0; i < APT; ++i) {
-            const int q = i * C::NTHREADS + tid;
-            const int r = q / ROW_CH;
-            ra[C::DIRECT ? 0 : i] = load_chunk(args.A, (size_t)(m0 + r) * (size_t)K * 2u,
-                                               k0 + a_kch[i], K, a_row_ok[i], a_vec);
-        }
+        for (int i = 0; i < APT; ++i) ra[i] = a_chunk(t, i * C::NTHREADS + tid);
 #pragma unroll
-        for (int i = 0; i < BPT; ++i) {
-            const int q = i * C::NTHREADS + tid;
-            if constexpr (C::TRANS_B) {
-                const int r = q / ROW_CH;
-                rb[C::DIRECT ? 0 : i] = load_chunk(args.B, (size_t)(n0 + r) * (size_t)K * 2u,
-                                                   k0 + b_kch[i], K, b_ok[i], b_vec);
-            } else {
-                const int k = q / NROW_CH, p = q % NROW_CH;
-                const int c = p ^ swz_nrow<NROW_CH>(k);
-                rb[C::DIRECT ? 0 : i] = load_chunk(args.B, (size_t)(k0 + k) * (size_t)N * 2u,
-                                                   n0 + 8 * c, N, k0 + k < K, b_vec);
-            }
-        }
+        for (int i = 0; i < BPT; ++i) rb[i] = b_chunk(t, i * C::NTHREADS + tid);
     };
     auto store_staged = [&](int stage) {
         GR_LDS unsigned char* sa = smem + stage * C::STAGE_BYTES;
         GR_LDS unsigned char* sb = sa + C::A_BYTES;
 #pragma unroll
         for (int i = 0; i < APT; ++i)
-            *reinterpret_cast<GR_LDS u32x4_t*>(sa + (i * C::NTHREADS + tid) * 16) =
-                ra[C::DIRECT ? 0 : i];
+            *reinterpret_cast<GR_LDS u32x4_t*>(sa + (i * C::NTHREADS + tid) * 16) = ra[i];
 #pragma unroll
         for (int i = 0; i < BPT; ++i)
-            *reinterpret_cast<GR_LDS u32x4_t*>(sb + (i * C::NTHREADS + tid) * 16) =
-                rb[C::DIRECT ? 0 : i];
+            *reinterpret_cast<GR_LDS u32x4_t*>(sb + (i * C::NTHREADS + tid) * 16) = rb[i];
+    };
+
+    // one chunk at a time (load, then LDS write): few live registers, for the
+    // single K-tail step of the direct configurations
+    auto fill_staged = [&](int t, int stage) {
+        GR_LDS unsigned char* sa = smem + stage * C::STAGE_BYTES;
+        GR_LDS unsigned char* sb = sa + C::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < APT; ++i) {
+            const int q = i * C::NTHREADS + tid;
+            *reinterpret_cast<GR_LDS u32x4_t*>(sa + q * 16) = a_chunk(t, q);
+        }
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            const int q = i * C::NTHREADS + tid;
+            *reinterpret_cast<GR_LDS u32x4_t*>(sb + q * 16) = b_chunk(t, q);
+        }
     };
 
     // ---- fragment read geometry (per lane, relative to a stage's A / B region).
@@ -513,18 +506,10 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
             const unsigned char* ga = a_tile + (size_t)k0 * 2u;
             const unsigned char* gb = C::TRANS_B ? b_tile + (size_t)k0 * 2u
                                                  : b_tile + (size_t)k0 * (size_t)N * 2u;
-            const unsigned char* zero = reinterpret_cast<const unsigned char*>(g_zero16);
-            const bool full = k0 + BK <= K;
-            if (l < APT) {
-                const uint32_t dst = sa + (l * C::NWAVES + wave) * 1024;
-                if (full) dma16(ga, a_src[l], dst);
-                else dma16_abs((k0 + a_kch[l] < K) ? ga + a_src[l] : zero, dst);
-            } else {
-                const int i = l - APT;
-                const uint32_t dst = sb + (i * C::NWAVES + wave) * 1024;
-                if (full) dma16(gb, b_src[i], dst);
-                else dma16_abs((k0 + b_kch[i] < K) ? gb + b_src[i] : zero, dst);
-            }
+            if (l < APT)
+                dma16(ga, a_src[l], sa + (l * C::NWAVES + wave) * 1024);
+            else
+                dma16(gb, b_src[l - APT], sb + ((l - APT) * C::NWAVES + wave) * 1024);
         };
         // MFMA p of a k-step: B block p / TM against A block p % TM
         auto mfma_op = [&](const Frags& f, int p) {
@@ -544,8 +529,8 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
 #pragma unroll
             for (int q = 0; q < NR; ++q) read_op(0, 0, q, fr[0]);
         }
-        // One BK step.  STEADY: the stage S-1 ahead exists and lies wholly inside
-        // K, so the step needs no run-time checks.
+        // One BK step.  STEADY: the stage S-1 ahead exists, so the step needs
+        // no run-time checks.
         auto step = [&](int t, auto steady_tag) {
             constexpr bool STEADY = decltype(steady_tag)::value;
             const int stage = t % S;
@@ -593,8 +578,8 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
                 }
             }
         };
-        // steady steps: stage t+S-1 < nk and its k range ends inside K
-        const int t_steady = max(0, min(nk, K / BK) - (S - 1));
+        // steady steps: stage t+S-1 < nk
+        const int t_steady = max(0, nk - (S - 1));
         for (int t = 0; t < t_steady; ++t) step(t, std::integral_constant<bool, true>{});
         for (int t = t_steady; t < nk; ++t) step(t, std::integral_constant<bool, false>{});
     } else if constexpr (C::DIRECT) {
@@ -633,6 +618,22 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
                 mma(fr[s & 1]);
             }
         }
+    }
+    if constexpr (C::DIRECT) {
+        // K tail (K % BK != 0): one register-staged step with element-wise zero
+        // fill past K, after every wave has left the copy ring.
+        if (K % BK != 0) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            barrier_lds();
+            fill_staged(nk, 0);
+            barrier_lds();
+            read_frags(0, 0, fr[0]);
+#pragma unroll
+            for (int s = 0; s < KSUB; ++s) {
+                if (s + 1 < KSUB) read_frags(0, s + 1, fr[(s + 1) & 1]);
+                mma(fr[s & 1]);
+            }
+        }
     } else {
         if (nk > 0) {
             load_staged(0);
@@ -657,9 +658,9 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     // ---- epilogue: ReLU on the fp32 accumulators, convert, store.
     // Lane owns C[m][n .. n+3] with m = m0 + wm0 + 32 i + l32 and
     // n = n0 + wn0 + 32 j + 8 q + 4 g, for q = 0..3 (registers 4q .. 4q+3).
+    // Four values inside the row go out as one 8- or 16-byte store (any element
+    // alignment: unaligned-access mode); a row's last partial group element-wise.
     constexpr int OB = OutTraits<C::OUT_DT>::bytes;
-    const bool c_vec = ((N & 3) == 0) &&
-                       ((reinterpret_cast<uintptr_t>(args.C) & (4 * OB - 1)) == 0);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int m = m0 + wm0 + 32 * i + l32;
@@ -676,10 +677,12 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
                 for (int e = 0; e < 4; ++e) v[e] = relu(acc[i][j][4 * q + e]);
                 if constexpr (C::OUT_DT == DT_F32) {
                     float* dst = reinterpret_cast<float*>(crow) + n;
-                    if (c_vec && n + 4 <= N) {
-                        *reinterpret_cast<u32x4_t*>(dst) =
-                            u32x4_t{__builtin_bit_cast(unsigned, v[0]), __builtin_bit_cast(unsigned, v[1]),
-                                    __builtin_bit_cast(unsigned, v[2]), __builtin_bit_cast(unsigned, v[3])};
+                    if (n + 4 <= N) {
+                        const u32x4_t w = {__builtin_bit_cast(unsigned, v[0]),
+                                           __builtin_bit_cast(unsigned, v[1]),
+                                           __builtin_bit_cast(unsigned, v[2]),
+                                           __builtin_bit_cast(unsigned, v[3])};
+                        __builtin_memcpy(dst, &w, 16);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
@@ -690,9 +693,10 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
 #pragma unroll
                     for (int e = 0; e < 4; ++e) h[e] = OutTraits<C::OUT_DT>::cvt(v[e]);
                     unsigned short* dst = reinterpret_cast<unsigned short*>(crow) + n;
-                    if (c_vec && n + 4 <= N) {
-                        *reinterpret_cast<u32x2_t*>(dst) =
-                            u32x2_t{h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16)};
+                    if (n + 4 <= N) {
+                        const u32x2_t w = {h[0] | ((unsigned)h[1] << 16),
+                                           h[2] | ((unsigned)h[3] << 16)};
+                        __builtin_memcpy(dst, &w, 8);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)

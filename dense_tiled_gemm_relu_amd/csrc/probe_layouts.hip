@@ -60,6 +60,27 @@ __global__ void k_dma16(const uint16_t* src, const uint32_t* chunk, uint16_t* ou
     for (int i = threadIdx.x; i < 512; i += 64) out[i] = lds[i];
 }
 
+// Lane l copies 16 bytes starting at element off[l] of src (2-byte aligned,
+// in bounds: off[l] + 8 <= n) into LDS with one direct copy, and also loads the
+// same 16 bytes into registers with a plain vector load; both land in out
+// (direct copy: out[0..511], register load: out[512..1023]).
+__global__ void k_unaligned16(const uint16_t* src, const uint32_t* off, uint32_t n, uint16_t* out)
+{
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[512];
+    for (int i = threadIdx.x; i < 512; i += 64) lds[i] = 0xFFFF;
+    __syncthreads();
+    uint32_t o = off[threadIdx.x];
+    if (o + 8 > n) o = 0;   // keep every access inside src
+    const GR_LDS unsigned char* base = (const GR_LDS unsigned char*)lds;
+    dma16(reinterpret_cast<const unsigned char*>(src), o * 2u, lds_addr(base));
+    u32x4_t v;
+    __builtin_memcpy(&v, src + o, 16);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    for (int i = threadIdx.x; i < 512; i += 64) out[i] = lds[i];
+    *reinterpret_cast<u32x4_t*>(out + 512 + 8 * threadIdx.x) = v;
+}
+
 int finish(hipError_t e)
 {
     if (e != hipSuccess) return -3;
@@ -80,6 +101,12 @@ extern "C" int probe_mfma_32x32x16(const void* X, const void* Y, void* D, int in
 extern "C" int probe_tr16(const void* src, const void* off, void* out)
 {
     k_tr16<<<1, 64>>>((const uint16_t*)src, (const uint32_t*)off, (uint16_t*)out);
+    return finish(hipGetLastError());
+}
+
+extern "C" int probe_unaligned16(const void* src, const void* off, unsigned n, void* out)
+{
+    k_unaligned16<<<1, 64>>>((const uint16_t*)src, (const uint32_t*)off, n, (uint16_t*)out);
     return finish(hipGetLastError());
 }
 

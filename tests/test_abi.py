@@ -42,7 +42,7 @@ def test_strerror():
 
 
 # fake, well-aligned and disjoint addresses: validation inspects, never dereferences
-A, B, C = 0x10000000, 0x20000000, 0x30000000
+A, B, C = 1 << 32, 2 << 32, 3 << 32
 
 
 @pytest.mark.parametrize("args", [
@@ -84,9 +84,13 @@ def test_null_operands_allowed_when_K_is_zero():
     (256, 256, 256, 0, True, "d64x64x64_s4"),
     (64, 8192, 8192, 0, True, "d64x64x64_s4"),
     (2048, 2048, 512, 0, True, "d128x128x64_s3"),
-    (4097, 3001, 5003, 0, True, "g128x128x64"),      # K, N not multiples of 8
-    (4096, 4096, 4096, 0, False, "g128x128x64"),     # misaligned pointer
-    (100, 100, 100, 0, True, "g64x64x64"),
+    (4096, 7168, 4096, 0, True, "d256x256x32_s4_i"),
+    (4097, 3001, 5003, 0, True, "d256x256x32_s4_i"),  # ragged and 2-byte aligned rows
+    (4096, 4096, 4096, 0, False, "d256x256x32_s4_i"), # 2-byte aligned base pointer
+    (100, 100, 100, 0, True, "d64x64x64_s4"),
+    (100, 40, 100, 0, True, "g64x64x64"),              # fewer than 64 columns of (K,N) B
+    (100, 40, 100, 1, True, "d64x64x64_s4"),           # transposed B rows are clamped
+    (64, 64, 1 << 23, 0, True, "g64x64x64"),           # copy offsets would overflow 32 bits
 ])
 def test_plan_selection(M, N, K, transB, aligned, want):
     off = 0 if aligned else 2
@@ -96,9 +100,9 @@ def test_plan_selection(M, N, K, transB, aligned, want):
 def test_forced_configuration(monkeypatch):
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "g64x64x64")
     assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0) == "g64x64x64"
-    # a direct configuration cannot be forced onto an unaligned problem
+    # a configuration that cannot serve the problem falls back to the automatic choice
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x256x64_s2")
-    assert gr.gemm_relu_plan(A, B, C, 100, 100, 100, 0, 0, 0) == "g64x64x64"
+    assert gr.gemm_relu_plan(A, B, C, 100, 100, 100, 0, 0, 0) == "d64x64x64_s4"
 
 
 def test_missing_library_fails_loudly(tmp_path):

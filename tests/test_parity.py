@@ -33,6 +33,16 @@ def _gpu():
     yield
 
 
+BN_OF = {"d256x256x64_s2": 256, "d256x256x32_s4": 256, "d256x256x32_s5": 256,
+         "d256x256x32_s4_i": 256, "d256x256x32_s4_w8i": 256, "d256x256x32_s5_w8i": 256,
+         "d256x256x64_s2_w8": 256, "d128x128x64_s3": 128, "d64x64x64_s4": 64}
+
+
+def usable(cfg, N, transB):
+    """Direct-copy configurations need a full tile of columns of a (K,N) B."""
+    return cfg not in BN_OF or transB or N >= BN_OF[cfg]
+
+
 def run(A, B, M, N, K, in_code, out_code, transB, cfg=None, monkeypatch=None, poison=True):
     """Upload, call gemm_relu through the C-ABI, return exact binary64 values."""
     import torch
@@ -65,10 +75,11 @@ def exact_limit(out_code):
 @pytest.mark.parametrize("cfg", DIRECT + STAGED)
 @pytest.mark.parametrize("in_code,out_code", COMBOS)
 @pytest.mark.parametrize("transB", [0, 1])
-def test_configs_integer_bitexact(cfg, in_code, out_code, transB, monkeypatch):
-    # several tiles in every direction plus ragged M, N and K tails; direct
-    # configurations need K and N multiples of 8
-    M, N, K = (264, 520, 200) if cfg in DIRECT else (301, 517, 203)
+@pytest.mark.parametrize("shape", [(264, 520, 200), (301, 517, 203)], ids=["k8", "ragged"])
+def test_configs_integer_bitexact(cfg, in_code, out_code, transB, shape, monkeypatch):
+    # several tiles in every direction plus M, N and K tails (K % BK != 0 in
+    # both shapes; the ragged one has odd row lengths, so 2-byte-aligned rows)
+    M, N, K = shape
     A, B = int_inputs(M, N, K, in_code, transB, 100, out_code)
     ref = oracle.gemm_relu_ref(A, B, M, N, K, in_code, transB)
     assert np.abs(ref).max() < exact_limit(out_code)
@@ -82,7 +93,7 @@ def test_configs_integer_bitexact(cfg, in_code, out_code, transB, monkeypatch):
                                               (wl.F16, wl.F32), (wl.BF16, wl.BF16)])
 @pytest.mark.parametrize("transB", [0, 1])
 def test_configs_uniform_tolerance(cfg, in_code, out_code, transB, monkeypatch):
-    M, N, K = (328, 264, 456) if cfg in DIRECT else (331, 263, 461)
+    M, N, K = (331, 263, 461)
     A, B = wl.make_inputs(M, N, K, in_code, transB, "uniform", 200)
     got = run(A, B, M, N, K, in_code, out_code, transB, cfg, monkeypatch)
     ref = oracle.gemm_relu_ref(A, B, M, N, K, in_code, transB)
@@ -99,7 +110,7 @@ def test_configs_uniform_tolerance(cfg, in_code, out_code, transB, monkeypatch):
 def test_coded_mapping(cfg, transB, monkeypatch):
     """A selects one row of B per output row (A[i][pi(i)] = 1), and B's entries
     encode their position, so every output element names its source."""
-    M, N, K = (200, 328, 264) if cfg in DIRECT else (203, 333, 269)
+    M, N, K = (203, 333, 269)
     rng = np.random.default_rng(3)
     pi = rng.permutation(K)[:M]
     a = np.zeros((M, K))
@@ -130,12 +141,35 @@ def test_tail_sweep_integer(M, N, K, transB):
 
 
 @pytest.mark.parametrize("cfg", DIRECT + STAGED)
-@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (65, 72, 136), (33, 200, 520), (300, 16, 64)])
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (65, 72, 136), (33, 200, 520), (300, 16, 64),
+                                   (70, 300, 24), (257, 263, 1), (5, 259, 37)])
 def test_tail_shapes_every_config(cfg, M, N, K, monkeypatch):
+    if not usable(cfg, N, 0):
+        pytest.skip("needs a full tile of B columns")
     A, B = int_inputs(M, N, K, wl.BF16, 0, 400 + M, wl.F32)
     ref = oracle.gemm_relu_ref(A, B, M, N, K, wl.BF16, 0)
     got = run(A, B, M, N, K, wl.BF16, wl.F32, 0, cfg, monkeypatch)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("off_a,off_b,off_c", [(1, 0, 0), (0, 1, 0), (0, 0, 1), (1, 3, 5)])
+@pytest.mark.parametrize("transB", [0, 1])
+def test_unaligned_pointers(off_a, off_b, off_c, transB):
+    """Operands that start 2, 6 or 10 bytes past an aligned allocation."""
+    import torch
+    M, N, K = 300, 520, 264
+    A, B = int_inputs(M, N, K, wl.F16, transB, 450, wl.F16)
+    Ab = torch.zeros(M * K + 8, dtype=torch.int16, device="cuda")
+    Bb = torch.zeros(K * N + 8, dtype=torch.int16, device="cuda")
+    Cb = torch.full((M * N + 8,), float("nan"), dtype=torch.float16, device="cuda")
+    Ab[off_a:off_a + M * K] = torch.from_numpy(A.reshape(-1).view(np.int16)).cuda()
+    Bb[off_b:off_b + K * N] = torch.from_numpy(B.reshape(-1).view(np.int16)).cuda()
+    Ad, Bd, Cd = Ab[off_a:], Bb[off_b:], Cb[off_c:off_c + M * N]
+    gr.gemm_relu(Ad, Bd, Cd, M, N, K, wl.F16, wl.F16, transB)
+    torch.cuda.synchronize()
+    got = from_device(Cd.view(M, N))
+    assert np.array_equal(got, oracle.gemm_relu_ref(A, B, M, N, K, wl.F16, transB))
+    assert torch.isnan(Cb[:off_c]).all() and torch.isnan(Cb[off_c + M * N:]).all()
 
 
 # --------------------------------------------------------- degenerate sizes

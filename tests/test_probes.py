@@ -19,11 +19,12 @@ def probe():
     import torch
     assert torch.cuda.is_available()
     lib = ctypes.CDLL(gr.PROBE_LIB_PATH)
-    for name in ("probe_mfma_32x32x16", "probe_tr16", "probe_dma16"):
+    for name in ("probe_mfma_32x32x16", "probe_tr16", "probe_dma16", "probe_unaligned16"):
         getattr(lib, name).restype = ctypes.c_int
     lib.probe_mfma_32x32x16.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int]
     lib.probe_tr16.argtypes = [ctypes.c_void_p] * 3
     lib.probe_dma16.argtypes = [ctypes.c_void_p] * 3
+    lib.probe_unaligned16.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_uint, ctypes.c_void_p]
     return lib
 
 
@@ -76,3 +77,21 @@ def test_direct_global_to_lds_copy(probe):
                              _dev(perm.view(np.int32)).data_ptr(), out.data_ptr()) == 0
     got = out.cpu().numpy().view(np.uint16).reshape(64, 8)
     assert np.array_equal(got, src.reshape(64, 8)[perm])
+
+
+def test_unaligned_16_byte_loads(probe):
+    """16-byte direct copies and vector loads from 2-byte-aligned addresses
+    (rows of an odd-length fp16 matrix) return the 8 elements that start there."""
+    import torch
+    n = 4096
+    src = np.arange(n, dtype=np.uint16) * np.uint16(7) + np.uint16(3)
+    rng = np.random.default_rng(11)
+    off = rng.integers(0, n - 8, size=64).astype(np.uint32)
+    off[:8] = [1, 3, 5, 7, 9, 2, 4, 6]                    # every residue mod 8
+    out = torch.zeros(1024, dtype=torch.int16, device="cuda")
+    assert probe.probe_unaligned16(_dev(src.view(np.int16)).data_ptr(),
+                                   _dev(off.view(np.int32)).data_ptr(), n, out.data_ptr()) == 0
+    got = out.cpu().numpy().view(np.uint16).reshape(2, 64, 8)
+    want = np.stack([src[o:o + 8] for o in off])
+    assert np.array_equal(got[1], want), "plain vector load"
+    assert np.array_equal(got[0], want), "direct global->LDS copy"
