@@ -20,6 +20,7 @@ enum ConfigId : int {
     CFG_D256x256x64_S2_W8,
     CFG_D128x128x64_S3,
     CFG_D64x64x64_S4,
+    CFG_D64x32x128_S4,
     CFG_G128x128x64,
     CFG_G64x64x64,
     CFG_COUNT
@@ -43,6 +44,7 @@ inline const ConfigInfo& config_info(int id)
         {"d256x256x64_s2_w8", 256, 256, true},
         {"d128x128x64_s3", 128, 128, true},
         {"d64x64x64_s4", 64, 64, true},
+        {"d64x32x128_s4", 64, 32, true},
         {"g128x128x64", 128, 128, false},
         {"g64x64x64", 64, 64, false},
     };
@@ -76,6 +78,11 @@ template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D128x128x64_S3
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D64x64x64_S4> {
     using type = Cfg<IN, OUT, TB, 64, 64, 64, 2, 2, 4, true>;
+};
+// Skinny / memory-bound problems: 2 waves, a long BK and 96 KiB of LDS, so one
+// workgroup per CU and twice as many workgroups as the 64x64 tile.
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D64x32x128_S4> {
+    using type = Cfg<IN, OUT, TB, 64, 32, 128, 2, 1, 4, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_G128x128x64> {
     using type = Cfg<IN, OUT, TB, 128, 128, 64, 2, 2, 2, false>;
@@ -128,6 +135,8 @@ LaunchFn launcher_bf16_nt(int out_dt, int cfg);
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D128x128x64_S3>::type>;     \
         case CFG_D64x64x64_S4:                                                             \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x64x64_S4>::type>;       \
+        case CFG_D64x32x128_S4:                                                            \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x32x128_S4>::type>;      \
         case CFG_G128x128x64:                                                              \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_G128x128x64>::type>;        \
         case CFG_G64x64x64:                                                                \

@@ -5,6 +5,7 @@
 // and a ceil-divided K loop, so every shape is covered, tails included.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -138,20 +139,24 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
 
     auto tiles = [&](int id) { return ceil_div(M, config_info(id).bm) * ceil_div(N, config_info(id).bn); };
     auto usable = [&](int id) { return direct_fits(id, N, K, transB); };
-    // Estimated time of a direct configuration: rounds of workgroups over the
-    // CUs times the tile area over the tile's MFMA efficiency relative to the
-    // 256x256 tile (measured on MI355X: 128x128 ~0.57, 64x64 ~0.5).
+    // Estimated time of a direct configuration, per K: rounds of workgroups
+    // over the CUs, each round the longer of the tile's MFMA time (tile area
+    // over its efficiency relative to the 256x256 tile, measured on MI355X:
+    // 128x128 ~0.57, 64x64 ~0.5, the two-wave 64x32 tile ~0.25) and the time
+    // to stream its (BM + BN) x K operands into one CU (~50 GB/s per CU from
+    // beyond L2, i.e. 98 area units per row or column).
     auto cost = [&](int id) {
         const ConfigInfo& ci = config_info(id);
-        const double eff = ci.bm >= 256 ? 1.0 : ci.bm >= 128 ? 0.57 : 0.5;
-        return double(ceil_div(tiles(id), kNumCUs)) * ci.bm * ci.bn / eff;
+        const double eff = ci.bm >= 256 ? 1.0 : ci.bm >= 128 ? 0.57 : ci.bn >= 64 ? 0.5 : 0.25;
+        const double per_round = std::max(ci.bm * ci.bn / eff, 98.0 * (ci.bm + ci.bn));
+        return double(ceil_div(tiles(id), kNumCUs)) * per_round;
     };
     int cfg = -1;
     const int forced = e.force_cfg;
     if (forced >= 0 && usable(forced)) {
         cfg = forced;
     } else {
-        for (int id : {CFG_D256x256x32_S4_I, CFG_D128x128x64_S3, CFG_D64x64x64_S4})
+        for (int id : {CFG_D256x256x32_S4_I, CFG_D128x128x64_S3, CFG_D64x64x64_S4, CFG_D64x32x128_S4})
             if (usable(id) && (cfg < 0 || cost(id) < cost(cfg))) cfg = id;
         if (cfg < 0) cfg = tiles(CFG_G128x128x64) >= kNumCUs ? CFG_G128x128x64 : CFG_G64x64x64;
     }

@@ -160,9 +160,9 @@ struct Cfg {
     static constexpr int LOADS_PER_STAGE = A_PER_THREAD + B_PER_THREAD;  // vm ops per wave per stage
 
     static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tiling");
-    static_assert(BK == 32 || BK == 64, "BK");
+    static_assert(BK == 32 || BK == 64 || BK == 128, "BK");
     static_assert(A_CH % NTHREADS == 0 && B_CH % NTHREADS == 0, "loader tiling");
-    static_assert(TRANS_B || BN >= 64, "n-contiguous B rows need >= 8 chunks for the swizzle");
+    static_assert(TRANS_B || BN >= 32, "n-contiguous B rows of at least 4 chunks");
         static_assert(STAGES >= 2 && STAGES <= 5, "stages");
     static_assert((STAGES - 2) * LOADS_PER_STAGE < 64, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity of a gfx950 CU");
@@ -207,14 +207,17 @@ __device__ __forceinline__ int swz_krow(int r)
 // A transpose read serves 32 lanes per cycle: 4 consecutive k rows x 4
 // consecutive chunks (64 bytes of n).  XOR-ing the chunk index with
 // 4 (k mod 4) puts the 4 rows on 4 disjoint chunk quads of the bank window;
-// with 8-chunk rows two rows share a window, so 4 ((k / 2) mod 2) suffices.
+// with 8-chunk rows two rows share a window, so 4 ((k / 2) mod 2) suffices;
+// 4-chunk rows already place 4 consecutive rows in one window.
 template <int NROW_CH>
 __device__ __forceinline__ int swz_nrow(int k)
 {
     if constexpr (NROW_CH >= 16)
         return 4 * (k & 3);
-    else
+    else if constexpr (NROW_CH == 8)
         return 4 * ((k >> 1) & 1);
+    else
+        return 0;
 }
 
 // ------------------------------------------------------------ tile order

@@ -81,15 +81,15 @@ def test_null_operands_allowed_when_K_is_zero():
     (8192, 8192, 8192, 0, True, "d256x256x32_s4_i"),
     (4096, 4096, 4096, 0, True, "d256x256x32_s4_i"),
     (4096, 7168, 4096, 1, True, "d256x256x32_s4_i"),
-    (256, 256, 256, 0, True, "d64x64x64_s4"),
-    (64, 8192, 8192, 0, True, "d64x64x64_s4"),
+    (256, 256, 256, 0, True, "d64x32x128_s4"),
+    (64, 8192, 8192, 0, True, "d64x32x128_s4"),        # skinny: twice the workgroups of 64x64
     (2048, 2048, 512, 0, True, "d128x128x64_s3"),
     (4096, 7168, 4096, 0, True, "d256x256x32_s4_i"),
     (4097, 3001, 5003, 0, True, "d256x256x32_s4_i"),  # ragged and 2-byte aligned rows
     (4096, 4096, 4096, 0, False, "d256x256x32_s4_i"), # 2-byte aligned base pointer
-    (100, 100, 100, 0, True, "d64x64x64_s4"),
-    (100, 40, 100, 0, True, "g64x64x64"),              # fewer than 64 columns of (K,N) B
-    (100, 40, 100, 1, True, "d64x64x64_s4"),           # transposed B rows are clamped
+    (100, 100, 100, 0, True, "d64x32x128_s4"),
+    (100, 24, 100, 0, True, "g64x64x64"),              # fewer than 32 columns of (K,N) B
+    (100, 24, 100, 1, True, "d64x32x128_s4"),          # transposed B rows are clamped
     (64, 64, 1 << 23, 0, True, "g64x64x64"),           # copy offsets would overflow 32 bits
 ])
 def test_plan_selection(M, N, K, transB, aligned, want):
@@ -102,7 +102,7 @@ def test_forced_configuration(monkeypatch):
     assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0) == "g64x64x64"
     # a configuration that cannot serve the problem falls back to the automatic choice
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x256x64_s2")
-    assert gr.gemm_relu_plan(A, B, C, 100, 100, 100, 0, 0, 0) == "d64x64x64_s4"
+    assert gr.gemm_relu_plan(A, B, C, 100, 100, 100, 0, 0, 0) == "d64x32x128_s4"
 
 
 def test_missing_library_fails_loudly(tmp_path):
