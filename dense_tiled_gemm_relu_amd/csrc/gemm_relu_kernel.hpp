@@ -661,9 +661,58 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     // ---- epilogue: ReLU on the fp32 accumulators, convert, store.
     // Lane owns C[m][n .. n+3] with m = m0 + wm0 + 32 i + l32 and
     // n = n0 + wn0 + 32 j + 8 q + 4 g, for q = 0..3 (registers 4q .. 4q+3).
-    // Four values inside the row go out as one 8- or 16-byte store (any element
-    // alignment: unaligned-access mode); a row's last partial group element-wise.
     constexpr int OB = OutTraits<C::OUT_DT>::bytes;
+    if constexpr (OB == 2 && BM * BN * 2 <= C::LDS_BYTES) {
+        // 16-bit C: the tile goes through the (now idle) LDS ring so that the
+        // global stores are whole rows, 16 bytes per lane, instead of 8-byte
+        // pieces of 32 different rows.  Row r of the staged tile keeps its
+        // 16-byte chunk c at c ^ (r mod 16) (mod the row's chunk count when
+        // shorter): conflict-free row reads, 2-way writes.
+        constexpr int RB = BN * 2, RCH = BN / 8;          // bytes and chunks per tile row
+        constexpr int XM = (RCH < 16 ? RCH : 16) - 1;
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        barrier_lds();
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm0 + 32 * i + l32;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = wn0 + 32 * j + 8 * q + 4 * g;
+                    unsigned short h[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        h[e] = OutTraits<C::OUT_DT>::cvt(relu(acc[i][j][4 * q + e]));
+                    const u32x2_t w = {h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16)};
+                    *reinterpret_cast<GR_LDS u32x2_t*>(
+                        smem + r * RB + (((c >> 3) ^ (r & XM)) << 4) + (c & 7) * 2) = w;
+                }
+        }
+        barrier_lds();
+        constexpr int ROWS_PER_PASS = C::NTHREADS / RCH;
+        static_assert(C::NTHREADS % RCH == 0 && BM % ROWS_PER_PASS == 0, "epilogue row passes");
+        const int cc = tid % RCH;
+#pragma unroll 4
+        for (int r = tid / RCH; r < BM; r += ROWS_PER_PASS) {
+            const int m = m0 + r, n = n0 + 8 * cc;
+            if (m >= M || n >= N) continue;
+            const u32x4_t v = *reinterpret_cast<const GR_LDS u32x4_t*>(
+                smem + r * RB + ((cc ^ (r & XM)) << 4));
+            unsigned short* dst = reinterpret_cast<unsigned short*>(args.C) + (size_t)m * N + n;
+            if (n + 8 <= N) {
+                __builtin_memcpy(dst, &v, 16);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N) dst[e] = (unsigned short)(v[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+        return;
+    }
+    // Otherwise (fp32 C, or a tile larger than the ring): four values inside the
+    // row go out as one 8- or 16-byte store (any element alignment:
+    // unaligned-access mode); a row's last partial group element-wise.
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int m = m0 + wm0 + 32 * i + l32;
