@@ -134,6 +134,47 @@ def cpu_baseline(w, A, B, target_s=15.0):
                       "binary64), %.2f s wall" % (R - 1, R, N, K, w["name"], dt)}
 
 
+def mfma_ceiling(gr, stream, blocks=1024, steps=2048):
+    """MFMA-only throughput on random fp16 operands with no memory traffic (the
+    probe library's probe_mfma_rate: 4 waves per CU, each streaming the 32 MFMAs
+    of one BK=32 step of a 128x128 wave tile).  The chip is power-limited, so
+    this, not 2.4 GHz x 4096 flop/clk/CU, is what the contraction step alone can
+    reach on this machine now.  None if the probe library is not built."""
+    import ctypes
+    import torch
+    if not os.path.exists(gr.PROBE_LIB_PATH):
+        return None
+    lib = ctypes.CDLL(gr.PROBE_LIB_PATH)
+    lib.probe_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    src = torch.empty(blocks * 8 * 256 * 8, dtype=torch.float16, device="cuda").uniform_(-1, 1)
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    ticks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
+    st = stream.cuda_stream
+
+    def run(n):
+        rc = lib.probe_mfma_rate(src.data_ptr(), src.numel() * 2, out.data_ptr(), ticks.data_ptr(),
+                                 blocks, n, st)
+        if rc != 0:
+            raise RuntimeError("probe_mfma_rate failed: %d" % rc)
+
+    run(steps // 8)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    run(steps)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    sec = ev0.elapsed_time(ev1) * 1e-3
+    t = ticks.view(blocks, 2).double()
+    cycles = t[:, 0].mean().item()
+    clock_mhz = (t[:, 0] / t[:, 1]).mean().item() * 100.0
+    flops = blocks * 4 * steps * 32 * (32 * 32 * 16 * 2)
+    return {"tflops": round(flops / sec / 1e12, 1), "clock_mhz": round(clock_mhz),
+            "cycles_per_mfma": round(cycles / (steps * 32), 2),
+            "kind": "MFMA-only, random fp16 operands, no memory traffic (probe_mfma_rate)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +269,9 @@ def main():
                                               M * N * (4 if oc == wl.F32 else 2)),
                      "kernel_ms": round(kernel_ms, 5)},
     }
+    ceiling = mfma_ceiling(gr, stream)
+    if ceiling is not None:
+        out["mfma_ceiling"] = dict(ceiling, frac=round(achieved / ceiling["tflops"], 4))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, A, B)
     print(json.dumps(out), flush=True)

@@ -2,7 +2,8 @@
 
 * ``libgemm_relu.so``       — the product: C-ABI gemm_relu / gemm_relu_strerror /
                               gemm_relu_plan (include/gemm_relu.h);
-* ``libgemm_relu_probe.so`` — test-only lane-layout probes.
+* ``libgemm_relu_probe.so`` — test-only lane-layout probes and the MFMA-rate
+  diagnostic (MFMA-only throughput on random operands).
 
 Objects go to ``_build/`` at the repository root; the libraries are written
 next to this file, where the Python binding loads them.
@@ -24,7 +25,7 @@ PROBE_LIB = os.path.join(PKG, "libgemm_relu_probe.so")
 
 LIB_SOURCES = ["gemm_relu_api.hip", "inst_f16_nn.hip", "inst_f16_nt.hip",
                "inst_bf16_nn.hip", "inst_bf16_nt.hip"]
-PROBE_SOURCES = ["probe_layouts.hip"]
+PROBE_SOURCES = ["probe_layouts.hip", "probe_mfma_rate.hip"]
 HEADERS = ["gemm_relu_kernel.hpp", "configs.hpp"]
 
 # gfx950 only.  Packed fp32 ALU ops are switched off: the compiler otherwise

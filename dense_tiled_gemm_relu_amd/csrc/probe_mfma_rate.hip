@@ -1,0 +1,77 @@
+// MFMA-only throughput on random operands: the practical ceiling of the GEMM's
+// contraction step on a power-limited chip.
+//
+// Each workgroup is 4 waves (one per SIMD, 512 registers each, one workgroup per
+// CU).  Every wave repeats `steps` rounds of 32 independent
+// v_mfma_f32_32x32x16_f16 over 16 accumulators and 4 + 4 operand registers: the
+// MFMA stream of one BK=32 step of a 128x128 wave tile, with no memory traffic
+// and no LDS.  The operands are the caller's random fp16 data, so the multiplier
+// arrays toggle as they do in the GEMM; on MI355X this, not the instruction
+// rate, sets the shader clock.  Wave 0 of each workgroup records the shader
+// cycles (s_memtime) and 100 MHz reference ticks (s_memrealtime) of its loop.
+// Diagnostic only; built into the probe library, not the product library.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kOperandRegs = 8;     // 4 A + 4 B fragments per lane
+
+__global__ void __launch_bounds__(kThreads, 1)
+k_mfma_rate(const f16x8_t* src, float* out, unsigned long long* ticks, int steps)
+{
+    const int tid = threadIdx.x;
+    const size_t base = (size_t)blockIdx.x * kOperandRegs * kThreads + tid;
+    f16x8_t a[4], b[4];
+    for (int i = 0; i < 4; ++i) {
+        a[i] = src[base + (size_t)i * kThreads];
+        b[i] = src[base + (size_t)(4 + i) * kThreads];
+    }
+    f32x16_t acc[16];
+    for (int i = 0; i < 16; ++i)
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+    const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the timer reads have returned
+    for (int it = 0; it < steps; ++it) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int p = 0; p < 16; ++p)
+                acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[p / 4], a[p % 4], acc[p], 0, 0, 0);
+        __builtin_amdgcn_s_barrier();
+    }
+    const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    float s = 0.0f;
+    for (int i = 0; i < 16; ++i)
+        for (int r = 0; r < 16; ++r) s += acc[i][r];
+    out[(size_t)blockIdx.x * kThreads + tid] = s;     // keeps the MFMAs live
+    if (tid == 0) {
+        ticks[2 * (size_t)blockIdx.x] = c1 - c0;
+        ticks[2 * (size_t)blockIdx.x + 1] = r1 - r0;
+    }
+}
+
+}  // namespace
+
+// src: at least blocks * 8 * 256 * 16 bytes of fp16 data; out: blocks * 256
+// floats; ticks: 2 * blocks values (shader cycles, reference ticks per
+// workgroup).  Launches on `stream` without synchronising.  Returns 0, -1 on
+// bad sizes, -3 on a launch failure.
+extern "C" int probe_mfma_rate(const void* src, size_t src_bytes, void* out, void* ticks,
+                               int blocks, int steps, void* stream)
+{
+    if (!src || !out || !ticks || blocks <= 0 || steps <= 0 ||
+        src_bytes < (size_t)blocks * kOperandRegs * kThreads * sizeof(f16x8_t))
+        return -1;
+    hipLaunchKernelGGL(k_mfma_rate, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const f16x8_t*)src, (float*)out, (unsigned long long*)ticks, steps);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
