@@ -6,6 +6,7 @@ already resident in HBM.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline]
+    python bench.py --table      # one JSON line per workload (warm and cold L2/MALL)
 
 Default workload: fp16 GEMM+ReLU at M = N = K = 8192 (row-major A and B,
 uniform[-1, 1] inputs from a fixed seed, fp32 accumulation, fp16 output) — the
@@ -175,6 +176,71 @@ def mfma_ceiling(gr, stream, blocks=1024, steps=2048):
             "kind": "MFMA-only, random fp16 operands, no memory traffic (probe_mfma_rate)"}
 
 
+def table(gr):
+    """One JSON line per workload: median per-call kernel time over 5 trials of
+    20 back-to-back calls (HIP events on the launch stream, 10 warm-up calls),
+    and a cold-cache time (median of 20 calls, each after a 512 MiB write
+    that evicts the 256 MiB MALL and the L2s)."""
+    import statistics
+    import torch
+    stream = torch.cuda.current_stream()
+    tdt = {wl.F16: torch.float16, wl.BF16: torch.bfloat16, wl.F32: torch.float32}
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    ceiling = mfma_ceiling(gr, stream)
+    print(json.dumps({"mfma_ceiling": ceiling}), flush=True)
+    for name in sorted(wl.WORKLOADS, key=lambda n: wl.WORKLOADS[n]["index"]):
+        w = wl.WORKLOADS[name]
+        M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
+        A, B = wl.workload_inputs(name)
+        Ad = torch.from_numpy(A.reshape(M, K).view(np.int16)).cuda().view(tdt[ic])
+        Bd = torch.from_numpy(B.reshape(wl.b_shape(M, N, K, tb)).view(np.int16)).cuda().view(tdt[ic])
+        Cd = torch.empty((M, N), dtype=tdt[oc], device="cuda")
+
+        def call():
+            gr.gemm_relu(Ad, Bd, Cd, M, N, K, ic, oc, tb, stream)
+
+        for _ in range(10):
+            call()
+        trials = []
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            trials.append(e0.elapsed_time(e1) * 1e3 / 20)
+        cold = []
+        for i in range(20):
+            flush.fill_(float(i))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1) * 1e3)
+        t = statistics.median(trials)
+        tc = statistics.median(cold)
+        flops = 2.0 * M * N * K
+        nbytes = 2 * M * K + 2 * K * N + M * N * (4 if oc == wl.F32 else 2)
+        print(json.dumps({
+            "workload": name, "M": M, "N": N, "K": K, "in": wl.DTYPE_NAMES[ic],
+            "out": wl.DTYPE_NAMES[oc], "transB": tb,
+            "tile_config": gr.gemm_relu_plan(Ad, Bd, Cd, M, N, K, ic, oc, tb),
+            "t_median_us": round(t, 2), "t_trials_us": [round(x, 2) for x in trials],
+            "tflops": round(flops / t / 1e6, 1),
+            "pct_peak": round(100 * flops / t / 1e6 / PEAK_TFLOPS_F16, 2),
+            "pct_of_mfma_ceiling": (round(100 * flops / t / 1e6 / ceiling["tflops"], 1)
+                                    if ceiling else None),
+            "algorithmic_GBps": round(nbytes / t / 1e3, 1),
+            "pct_hbm": round(100 * nbytes / t / 1e3 / HBM_GBPS, 2),
+            "t_cold_median_us": round(tc, 2), "tflops_cold": round(flops / tc / 1e6, 1)}),
+            flush=True)
+        del Ad, Bd, Cd
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +248,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gemm_relu_f16_8192", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--table", action="store_true",
+                    help="time every workload (warm and cold caches), one JSON line each")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only the plain copy used to scale HBM byte counters")
     ap.add_argument("--ingest-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"),
@@ -209,6 +277,9 @@ def main():
     if not os.path.exists(gr.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
+    if args.table:
+        table(gr)
+        return
 
     w = dict(wl.WORKLOADS[args.workload], name=args.workload)
     M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
