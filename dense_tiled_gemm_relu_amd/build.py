@@ -25,7 +25,7 @@ PROBE_LIB = os.path.join(PKG, "libgemm_relu_probe.so")
 
 LIB_SOURCES = ["gemm_relu_api.hip", "inst_f16_nn.hip", "inst_f16_nt.hip",
                "inst_bf16_nn.hip", "inst_bf16_nt.hip"]
-PROBE_SOURCES = ["probe_layouts.hip", "probe_mfma_rate.hip"]
+PROBE_SOURCES = ["probe_layouts.hip", "probe_mfma_rate.hip", "probe_fp8.hip"]
 HEADERS = ["gemm_relu_kernel.hpp", "configs.hpp"]
 
 # gfx950 only.  Packed fp32 ALU ops are switched off: the compiler otherwise

@@ -9,17 +9,21 @@ The operation (page "TileLang：GPU/NPU 通用算子 DSL", §3.2 GPU minimal exa
 
     ref[i, j] = max( sum_k a(i, k) * b(k, j), 0 )
 
-computed in binary64 from the exact values of the 16-bit inputs.  Two
-independent implementations live here:
+computed in binary64 from the exact values of the inputs: binary16 and
+bfloat16, or the OCP 8-bit formats E4M3 and E5M2 (the FP8 GEMM of that page's
+§4.1; the pages give it no scale factors, so it is the same definition over the
+8-bit values).  Two independent implementations live here:
 
 * ``gemm_relu_ref`` / ``gemm_relu_ref_at`` — a plain C triple loop
-  (``oracle.c``) with its own binary16 / bfloat16 decoders, OpenMP over rows;
+  (``oracle.c``) with its own decoders written from the field definitions,
+  OpenMP over rows;
 * ``gemm_relu_fraction`` — exact rational arithmetic in pure Python
   (``fractions.Fraction``), for tiny shapes only; it decodes through numpy's
-  float16 and a bit shift for bfloat16, so it shares no decoder with the C code.
+  float16, a bit shift for bfloat16 and torch's CPU float8 types, so it shares
+  no decoder with the C code.
 
-Inputs are 16-bit storage patterns (numpy ``uint16`` arrays); outputs are
-binary64 numpy arrays.
+Inputs are storage patterns (numpy ``uint16`` arrays for the 16-bit types,
+``uint8`` for the 8-bit ones); outputs are binary64 numpy arrays.
 """
 import ctypes
 import os
@@ -31,6 +35,9 @@ from . import build as _build
 
 F16 = 0
 BF16 = 1
+F8E4M3 = 3
+F8E5M2 = 4
+FP8 = (F8E4M3, F8E5M2)
 
 _lib = None
 
@@ -50,13 +57,18 @@ def _load():
     lib.oracle_dec_f16.restype = ctypes.c_double
     lib.oracle_dec_bf16.argtypes = [ctypes.c_uint16]
     lib.oracle_dec_bf16.restype = ctypes.c_double
-    lib.oracle_decode.argtypes = [u16p, f64p, i64, ctypes.c_int]
+    lib.oracle_dec_e4m3.argtypes = [ctypes.c_uint8]
+    lib.oracle_dec_e4m3.restype = ctypes.c_double
+    lib.oracle_dec_e5m2.argtypes = [ctypes.c_uint8]
+    lib.oracle_dec_e5m2.restype = ctypes.c_double
+    vp = ctypes.c_void_p
+    lib.oracle_decode.argtypes = [vp, f64p, i64, ctypes.c_int]
     lib.oracle_decode.restype = None
-    lib.oracle_gemm_relu_f64.argtypes = [u16p, u16p, f64p, i64, i64, i64,
+    lib.oracle_gemm_relu_f64.argtypes = [vp, vp, f64p, i64, i64, i64,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     lib.oracle_gemm_relu_f64.restype = ctypes.c_int
-    lib.oracle_gemm_relu_f64_at.argtypes = [u16p, u16p, i64p, i64p, i64, f64p, f64p,
+    lib.oracle_gemm_relu_f64_at.argtypes = [vp, vp, i64p, i64p, i64, f64p, f64p,
                                             i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int]
     lib.oracle_gemm_relu_f64_at.restype = ctypes.c_int
@@ -64,10 +76,14 @@ def _load():
     return lib
 
 
-def _u16(x):
+def _bits(x, dtype):
+    """Contiguous storage patterns of the input type: uint8 for the 8-bit
+    formats, uint16 for the 16-bit ones."""
     x = np.ascontiguousarray(x)
-    if x.dtype != np.uint16:
-        raise TypeError("oracle inputs are uint16 storage patterns, got %s" % x.dtype)
+    want = np.uint8 if dtype in FP8 else np.uint16
+    if x.dtype != want:
+        raise TypeError("oracle inputs of type %d are %s storage patterns, got %s"
+                        % (dtype, np.dtype(want).name, x.dtype))
     return x
 
 
@@ -75,13 +91,16 @@ def _ptr(x, ctype):
     return x.ctypes.data_as(ctypes.POINTER(ctype))
 
 
+def _vptr(x):
+    return ctypes.c_void_p(x.ctypes.data)
+
+
 def decode(bits, dtype):
-    """Exact binary64 values of 16-bit patterns (C decoder)."""
+    """Exact binary64 values of storage patterns (C decoder)."""
     lib = _load()
-    bits = _u16(bits)
+    bits = _bits(bits, dtype)
     out = np.empty(bits.shape, dtype=np.float64)
-    lib.oracle_decode(_ptr(bits, ctypes.c_uint16), _ptr(out, ctypes.c_double),
-                      bits.size, dtype)
+    lib.oracle_decode(_vptr(bits), _ptr(out, ctypes.c_double), bits.size, dtype)
     return out
 
 
@@ -93,13 +112,13 @@ def gemm_relu_ref(A, B, M, N, K, dtype, transB=0, relu=True, threads=0,
     (K,N) if transB == 0, (N,K) if transB == 1.
     """
     lib = _load()
-    A = _u16(A).reshape(-1)
-    B = _u16(B).reshape(-1)
+    A = _bits(A, dtype).reshape(-1)
+    B = _bits(B, dtype).reshape(-1)
     if A.size != M * K or B.size != K * N:
         raise ValueError("operand sizes do not match M, N, K")
     C = np.empty((M, N), dtype=np.float64)
     used = ctypes.c_int(0)
-    rc = lib.oracle_gemm_relu_f64(_ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16),
+    rc = lib.oracle_gemm_relu_f64(_vptr(A), _vptr(B),
                                   _ptr(C, ctypes.c_double), M, N, K, dtype, int(transB),
                                   1 if relu else 0, threads, ctypes.byref(used))
     if rc != 0:
@@ -113,8 +132,8 @@ def gemm_relu_ref_at(A, B, rows, cols, M, N, K, dtype, transB=0, relu=True):
     Returns (values, absum) where absum[t] = sum_k |a(i,k) b(k,j)|.
     """
     lib = _load()
-    A = _u16(A).reshape(-1)
-    B = _u16(B).reshape(-1)
+    A = _bits(A, dtype).reshape(-1)
+    B = _bits(B, dtype).reshape(-1)
     if A.size != M * K or B.size != K * N:
         raise ValueError("operand sizes do not match M, N, K")
     rows = np.ascontiguousarray(rows, dtype=np.int64)
@@ -123,7 +142,7 @@ def gemm_relu_ref_at(A, B, rows, cols, M, N, K, dtype, transB=0, relu=True):
         raise ValueError("rows and cols differ in shape")
     out = np.empty(rows.shape, dtype=np.float64)
     absum = np.empty(rows.shape, dtype=np.float64)
-    rc = lib.oracle_gemm_relu_f64_at(_ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16),
+    rc = lib.oracle_gemm_relu_f64_at(_vptr(A), _vptr(B),
                                      _ptr(rows, ctypes.c_int64), _ptr(cols, ctypes.c_int64),
                                      rows.size, _ptr(out, ctypes.c_double),
                                      _ptr(absum, ctypes.c_double), M, N, K, dtype,
@@ -134,12 +153,18 @@ def gemm_relu_ref_at(A, B, rows, cols, M, N, K, dtype, transB=0, relu=True):
 
 
 def _exact(bits, dtype):
-    """Exact rational values of 16-bit patterns through numpy (not the C decoder)."""
-    bits = _u16(bits)
+    """Exact rational values of storage patterns through numpy or torch's CPU
+    float8 types (not the C decoder)."""
+    bits = _bits(bits, dtype)
     if dtype == F16:
         vals = bits.view(np.float16).astype(np.float64)
-    else:
+    elif dtype == BF16:
         vals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        import torch
+        t = torch.from_numpy(bits.reshape(-1).copy())
+        fmt = torch.float8_e4m3fn if dtype == F8E4M3 else torch.float8_e5m2
+        vals = t.view(fmt).to(torch.float64).numpy()
     return [Fraction(float(v)) for v in vals.reshape(-1)]
 
 
@@ -168,8 +193,8 @@ def gemm_relu_ref_matmul(A, B, M, N, K, dtype, transB=0, relu=True):
     an integer below 2^53) the result is exact in any summation order.  For
     full-size problems where the triple loop would take minutes.
     """
-    A = _u16(A).reshape(-1)
-    B = _u16(B).reshape(-1)
+    A = _bits(A, dtype).reshape(-1)
+    B = _bits(B, dtype).reshape(-1)
     if A.size != M * K or B.size != K * N:
         raise ValueError("operand sizes do not match M, N, K")
     a = decode(A, dtype).reshape(M, K)

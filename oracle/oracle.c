@@ -19,10 +19,13 @@
  * or dec(B[j*K+k]) when transB = 1.  The result stays binary64: no rounding to
  * the storage type of C happens here.
  *
- * dec() turns a 16-bit storage pattern into its exact value.  binary16 and
- * bfloat16 are decoded from their field definitions (sign, biased exponent,
- * fraction; bfloat16 is the upper half of a binary32 pattern: 8 exponent bits,
- * 7 fraction bits), not by reinterpreting bits through a hardware type.
+ * dec() turns a storage pattern into its exact value.  binary16 and bfloat16
+ * (16-bit patterns) and the two OCP 8-bit floating-point formats E4M3 and E5M2
+ * (8-bit patterns; the "FP8 GEMM" that page's §4.1 lists among the kernels the
+ * DSL covers) are decoded from their field definitions (sign, biased exponent,
+ * fraction), not by reinterpreting bits through a hardware type.  The pages
+ * give FP8 no scale factors, so an FP8 product here is the same definition
+ * over the exact values of the 8-bit inputs.
  *
  * Readings where the pages are silent (listed with the others in the design
  * notes): a negative sum maps to +0.0; K = 0 gives an empty sum, so every
@@ -36,7 +39,7 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_F16 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F16 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 3, ORACLE_FP8_E5M2 = 4 };
 
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
 double oracle_dec_f16(uint16_t h)
@@ -70,22 +73,65 @@ double oracle_dec_bf16(uint16_t h)
     return sign ? -v : v;
 }
 
-static double dec(uint16_t h, int dtype)
+/* OCP 8-bit E4M3 ("FN": finite only): 1 sign bit, 4 exponent bits (bias 7),
+ * 3 fraction bits.  Exponent field 15 with fraction 7 is NaN; every other
+ * pattern is finite (largest 1.75 * 2^8 = 448).  No infinities. */
+double oracle_dec_e4m3(uint8_t h)
 {
-    return dtype == ORACLE_F16 ? oracle_dec_f16(h) : oracle_dec_bf16(h);
+    int sign = (h >> 7) & 1;
+    int e = (h >> 3) & 0xf;
+    int f = h & 0x7;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -9);               /* subnormal: f * 2^-3 * 2^-6 */
+    else if (e == 15 && f == 7)
+        v = NAN;
+    else
+        v = ldexp((double)(8 + f), e - 10);     /* (1 + f/2^3) * 2^(e-7) */
+    return sign ? -v : v;
 }
 
-void oracle_decode(const uint16_t* x, double* out, int64_t n, int dtype)
+/* OCP 8-bit E5M2: 1 sign bit, 5 exponent bits (bias 15), 2 fraction bits,
+ * with IEEE infinities and NaNs at exponent field 31. */
+double oracle_dec_e5m2(uint8_t h)
+{
+    int sign = (h >> 7) & 1;
+    int e = (h >> 2) & 0x1f;
+    int f = h & 0x3;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -16);              /* subnormal: f * 2^-2 * 2^-14 */
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(4 + f), e - 17);     /* (1 + f/2^2) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Exact value of element idx of a storage array of the given type. */
+static double dec_at(const void* x, int64_t idx, int dtype)
+{
+    switch (dtype) {
+    case ORACLE_F16: return oracle_dec_f16(((const uint16_t*)x)[idx]);
+    case ORACLE_BF16: return oracle_dec_bf16(((const uint16_t*)x)[idx]);
+    case ORACLE_FP8_E4M3: return oracle_dec_e4m3(((const uint8_t*)x)[idx]);
+    default: return oracle_dec_e5m2(((const uint8_t*)x)[idx]);
+    }
+}
+
+void oracle_decode(const void* x, double* out, int64_t n, int dtype)
 {
     for (int64_t i = 0; i < n; ++i)
-        out[i] = dec(x[i], dtype);
+        out[i] = dec_at(x, i, dtype);
 }
 
 static int bad_args(const void* A, const void* B, const void* C,
                     int64_t M, int64_t N, int64_t K, int dtype, int transB)
 {
     if (M < 0 || N < 0 || K < 0) return 1;
-    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return 1;
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16 && dtype != ORACLE_FP8_E4M3 &&
+        dtype != ORACLE_FP8_E5M2)
+        return 1;
     if (transB != 0 && transB != 1) return 1;
     if ((M > 0 && K > 0 && !A) || (N > 0 && K > 0 && !B) || (M > 0 && N > 0 && !C)) return 1;
     return 0;
@@ -103,7 +149,7 @@ static int64_t b_index(int64_t k, int64_t j, int64_t N, int64_t K, int transB)
  * Returns 0, or -1 on bad arguments.  *threads_used (if not NULL) receives the
  * number of threads the row loop ran on.
  */
-int oracle_gemm_relu_f64(const uint16_t* A, const uint16_t* B, double* C,
+int oracle_gemm_relu_f64(const void* A, const void* B, double* C,
                          int64_t M, int64_t N, int64_t K,
                          int dtype, int transB, int relu, int threads,
                          int* threads_used)
@@ -167,7 +213,7 @@ int oracle_gemm_relu_f64(const uint16_t* A, const uint16_t* B, double* C,
  * If absum is not NULL it also receives S = sum_k |a(i,k) * b(k,j)|, the scale
  * of the floating-point summation error bound.
  */
-int oracle_gemm_relu_f64_at(const uint16_t* A, const uint16_t* B,
+int oracle_gemm_relu_f64_at(const void* A, const void* B,
                             const int64_t* rows, const int64_t* cols, int64_t n,
                             double* out, double* absum,
                             int64_t M, int64_t N, int64_t K,
@@ -182,7 +228,7 @@ int oracle_gemm_relu_f64_at(const uint16_t* A, const uint16_t* B,
         int64_t i = rows[t], j = cols[t];
         double s = 0.0, sa = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            double p = dec(A[i * K + k], dtype) * dec(B[b_index(k, j, N, K, transB)], dtype);
+            double p = dec_at(A, i * K + k, dtype) * dec_at(B, b_index(k, j, N, K, transB), dtype);
             s += p;
             sa += fabs(p);
         }

@@ -282,3 +282,84 @@ def test_matmul_form_close_to_loop_on_floats():
     C2 = oracle.gemm_relu_ref_matmul(A, B, M, N, K, F16, 0)
     # two binary64 summation orders of K products: relative gap ~ K * 2^-53
     assert np.allclose(C1, C2, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------ 8-bit inputs
+F8E4M3, F8E5M2 = oracle.F8E4M3, oracle.F8E5M2
+
+
+@pytest.mark.parametrize("dtype", [F8E4M3, F8E5M2])
+def test_decode_fp8_exhaustive_against_torch(dtype):
+    """All 256 patterns against torch's CPU float8 types (a library decoder)."""
+    import torch
+    bits = np.arange(256, dtype=np.uint8)
+    got = oracle.decode(bits, dtype)
+    fmt = torch.float8_e4m3fn if dtype == F8E4M3 else torch.float8_e5m2
+    want = torch.from_numpy(bits.copy()).view(fmt).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.signbit(got[0x80]) and not np.signbit(got[0])
+
+
+def test_decode_e5m2_is_the_top_byte_of_binary16():
+    """E5M2 has binary16's sign and exponent fields and its 2 leading fraction
+    bits: pattern c means the binary16 pattern c << 8."""
+    bits = np.arange(256, dtype=np.uint8)
+    got = oracle.decode(bits, F8E5M2)
+    want = oracle.decode(bits.astype(np.uint16) << 8, F16)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+def test_decode_e4m3_landmarks():
+    bits = np.arange(256, dtype=np.uint8)
+    v = oracle.decode(bits, F8E4M3)
+    assert v[0x38] == 1.0 and v[0xB8] == -1.0
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0          # largest finite
+    assert v[0x08] == 2.0 ** -6                              # smallest normal
+    assert v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9  # subnormals
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.isfinite(v).sum() == 254                       # no infinities
+    assert np.all(np.diff(v[:0x7F]) > 0)                     # monotone over the positives
+
+
+@pytest.mark.parametrize("dtype", [F8E4M3, F8E5M2])
+@pytest.mark.parametrize("transB", [0, 1])
+def test_bruteforce_fp8_small_shapes(dtype, transB):
+    """Exact rational brute force (decoded through torch) on random 8-bit
+    patterns, every shape up to 4 x 4 x 5.  Values are kept to zero and
+    2^-8 <= |x| <= 2^8 so that every partial sum is exact in binary64 (E5M2's
+    full range would span more than 53 bits of products)."""
+    rng = np.random.default_rng(77 + dtype)
+    vals = oracle.decode(np.arange(256, dtype=np.uint8), dtype)
+    with np.errstate(invalid="ignore"):
+        ok = (vals == 0) | ((np.abs(vals) >= 2.0 ** -8) & (np.abs(vals) <= 2.0 ** 8))
+    finite = np.flatnonzero(ok)
+    for M, N, K in itertools.product(range(1, 5), range(1, 5), range(0, 6)):
+        A = rng.choice(finite, size=M * K).astype(np.uint8)
+        B = rng.choice(finite, size=K * N).astype(np.uint8)
+        got = oracle.gemm_relu_ref(A, B, M, N, K, dtype, transB)
+        want = oracle.gemm_relu_fraction(A, B, M, N, K, dtype, transB)
+        assert [[Fraction(float(x)) for x in row] for row in got] == want
+
+
+@pytest.mark.parametrize("dtype", [F8E4M3, F8E5M2])
+def test_fp8_transB_and_matmul_form(dtype):
+    M, N, K = 9, 11, 70
+    A = wl.integers((M, K), 5, dtype)
+    Bkn = wl.integers((K, N), 6, dtype)
+    Bnk = np.ascontiguousarray(Bkn.reshape(K, N).T)
+    ref = oracle.gemm_relu_ref(A, Bkn, M, N, K, dtype, 0)
+    assert np.array_equal(ref, oracle.gemm_relu_ref(A, Bnk, M, N, K, dtype, 1))
+    assert np.array_equal(ref, oracle.gemm_relu_ref_matmul(A, Bkn, M, N, K, dtype, 0))
+    a = wl.integers((M, K), 5, F16)
+    b = wl.integers((K, N), 6, F16)
+    # the same integers through the binary16 path
+    assert np.array_equal(ref, oracle.gemm_relu_ref(a, b, M, N, K, F16, 0))
+
+
+def test_fp8_inputs_must_be_bytes():
+    with pytest.raises(TypeError):
+        oracle.gemm_relu_ref(np.zeros(4, np.uint16), np.zeros(4, np.uint16), 2, 2, 2, F8E4M3)

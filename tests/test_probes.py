@@ -61,8 +61,8 @@ def test_lds_transpose_read(probe):
                 want[16 * h + q, e] = (r0 + e) * 256 + c0 + q
     assert off.max() + 8 <= 8192 and np.all(off % 8 == 0)
     out = torch.zeros(256, dtype=torch.int16, device="cuda")
-    assert probe.probe_tr16(_dev(src.view(np.int16)).data_ptr(),
-                            _dev(off.view(np.int32)).data_ptr(), out.data_ptr()) == 0
+    src_d, off_d = _dev(src.view(np.int16)), _dev(off.view(np.int32))   # alive through the call
+    assert probe.probe_tr16(src_d.data_ptr(), off_d.data_ptr(), out.data_ptr()) == 0
     got = out.cpu().numpy().view(np.uint16).reshape(64, 4)
     assert np.array_equal(got, want)
 
@@ -73,8 +73,8 @@ def test_direct_global_to_lds_copy(probe):
     src = np.arange(512, dtype=np.uint16)
     perm = ((np.arange(64) * 37 + 5) % 64).astype(np.uint32)
     out = torch.zeros(512, dtype=torch.int16, device="cuda")
-    assert probe.probe_dma16(_dev(src.view(np.int16)).data_ptr(),
-                             _dev(perm.view(np.int32)).data_ptr(), out.data_ptr()) == 0
+    src_d, perm_d = _dev(src.view(np.int16)), _dev(perm.view(np.int32))
+    assert probe.probe_dma16(src_d.data_ptr(), perm_d.data_ptr(), out.data_ptr()) == 0
     got = out.cpu().numpy().view(np.uint16).reshape(64, 8)
     assert np.array_equal(got, src.reshape(64, 8)[perm])
 
@@ -89,8 +89,8 @@ def test_unaligned_16_byte_loads(probe):
     off = rng.integers(0, n - 8, size=64).astype(np.uint32)
     off[:8] = [1, 3, 5, 7, 9, 2, 4, 6]                    # every residue mod 8
     out = torch.zeros(1024, dtype=torch.int16, device="cuda")
-    assert probe.probe_unaligned16(_dev(src.view(np.int16)).data_ptr(),
-                                   _dev(off.view(np.int32)).data_ptr(), n, out.data_ptr()) == 0
+    src_d, off_d = _dev(src.view(np.int16)), _dev(off.view(np.int32))
+    assert probe.probe_unaligned16(src_d.data_ptr(), off_d.data_ptr(), n, out.data_ptr()) == 0
     got = out.cpu().numpy().view(np.uint16).reshape(2, 64, 8)
     want = np.stack([src[o:o + 8] for o in off])
     assert np.array_equal(got[1], want), "plain vector load"
@@ -119,3 +119,82 @@ def test_mfma_rate_probe(probe):
     cyc = ticks.view(blocks, 2)[:, 0].double().mean().item() / (steps * 32)
     assert 31.9 <= cyc <= 40.0, cyc
     assert torch.isfinite(out).all()
+
+
+# ---------------------------------------------------------- 8-bit data paths
+def _fp8_lib():
+    lib = ctypes.CDLL(gr.PROBE_LIB_PATH)
+    for n in ("probe_mfma_f8_raw", "probe_tr8_raw", "probe_unaligned8"):
+        getattr(lib, n).restype = ctypes.c_int
+    lib.probe_mfma_f8_raw.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int]
+    lib.probe_tr8_raw.argtypes = [ctypes.c_void_p] * 3
+    lib.probe_unaligned8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint,
+                                     ctypes.c_void_p]
+    return lib
+
+
+@pytest.mark.parametrize("dtype", [wl.F8E4M3, wl.F8E5M2])
+def test_mfma_32x32x64_f8_layout(dtype):
+    """v_mfma_f32_32x32x64_f8f6f4 without block scales: lane l feeds row/column
+    l % 32 with the 32 bytes of k-group l / 32 (byte e of an A lane meets byte
+    e of the B lane of the same group), and owns D[8 (r/4) + 4 (l/32) + r%4][l%32]
+    in result register r — the layout of the 16-bit MFMA the kernel uses."""
+    import torch
+    lib = _fp8_lib()
+    rng = np.random.default_rng(21 + dtype)
+    av = rng.integers(-3, 4, size=(64, 32)).astype(np.float64)
+    bv = rng.integers(-3, 4, size=(64, 32)).astype(np.float64)
+    ab, bb = _dev(wl.encode(av, dtype)), _dev(wl.encode(bv, dtype))
+    d = torch.zeros(64 * 16, dtype=torch.float32, device="cuda")
+    fmt = 0 if dtype == wl.F8E4M3 else 1
+    assert lib.probe_mfma_f8_raw(ab.data_ptr(), bb.data_ptr(), d.data_ptr(), fmt) == 0
+    X = np.zeros((32, 64))
+    Y = np.zeros((64, 32))
+    for l in range(64):
+        X[l % 32, 32 * (l // 32):32 * (l // 32) + 32] = av[l]
+        Y[32 * (l // 32):32 * (l // 32) + 32, l % 32] = bv[l]
+    D = X @ Y
+    want = np.array([[D[8 * (r // 4) + 4 * (l // 32) + r % 4, l % 32] for r in range(16)]
+                     for l in range(64)])
+    assert np.array_equal(d.cpu().numpy().reshape(64, 16), want)
+
+
+def test_lds_transpose_read_b8():
+    """ds_read_b64_tr_b8: in each 16-lane group, lane i supplies the address of
+    8 bytes (row i / 2, columns 8 (i % 2) .. +7 of a 8 x 16 byte block) and
+    receives the 8 rows of column i."""
+    import torch
+    lib = _fp8_lib()
+    P = 256
+    rng = np.random.default_rng(9)
+    M = rng.integers(0, 256, size=(16, P)).astype(np.uint8)
+    off = np.zeros(64, dtype=np.uint32)
+    col0 = np.zeros(64, dtype=np.int64)
+    for l in range(64):
+        h, i16 = l // 16, l % 16
+        col0[l] = 16 * (h & 1) + 32 * (h >> 1)
+        off[l] = (i16 // 2) * P + col0[l] + 8 * (i16 % 2)
+    src_d, off_d = _dev(M.reshape(-1)), _dev(off.view(np.int32))
+    out = torch.zeros(512, dtype=torch.uint8, device="cuda")
+    assert lib.probe_tr8_raw(src_d.data_ptr(), off_d.data_ptr(), out.data_ptr()) == 0
+    want = np.stack([M[0:8, col0[l] + l % 16] for l in range(64)])
+    assert np.array_equal(out.cpu().numpy().reshape(64, 8), want)
+
+
+def test_byte_unaligned_16_byte_loads():
+    """16-byte direct copies and vector loads from any byte offset (rows of an
+    odd-length 8-bit matrix) return the 16 bytes that start there."""
+    import torch
+    lib = _fp8_lib()
+    n = 4096
+    src = (np.arange(n) * 7 + 3).astype(np.uint8)
+    rng = np.random.default_rng(13)
+    off = rng.integers(0, n - 16, size=64).astype(np.uint32)
+    off[:16] = np.arange(16) + 1                          # every residue mod 16
+    src_d, off_d = _dev(src), _dev(off.view(np.int32))
+    out = torch.zeros(2048, dtype=torch.uint8, device="cuda")
+    assert lib.probe_unaligned8(src_d.data_ptr(), off_d.data_ptr(), n, out.data_ptr()) == 0
+    got = out.cpu().numpy().reshape(2, 64, 16)
+    want = np.stack([src[o:o + 16] for o in off])
+    assert np.array_equal(got[1], want), "plain vector load"
+    assert np.array_equal(got[0], want), "direct global->LDS copy"

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs and the workload table for the fused GEMM + ReLU.
 
 This module holds no arithmetic of the method: it only draws numbers and encodes
-them as 16-bit storage patterns.  Both the GPU tests and the CPU oracle tests
+them as 16-bit or 8-bit storage patterns.  Both the GPU tests and the CPU oracle tests
 take their inputs from here, so the two sides see the same bits.
 
 Recipe (the pages fix the shapes and dtypes but no generator):
@@ -10,14 +10,24 @@ Recipe (the pages fix the shapes and dtypes but no generator):
 * uniform[-1, 1] drawn in binary64, rounded to binary16 by numpy (nearest-even);
 * normal(0, sigma) drawn in binary64, rounded to binary32 (nearest-even), then
   to bfloat16 (nearest-even on the upper half);
-* integer variants draw from {lo..hi} and are exact in either 16-bit format.
+* 8-bit inputs (OCP E4M3 / E5M2): the same binary64 draws rounded to nearest
+  even by torch's CPU float8 conversion (uniform[-1, 1] never reaches either
+  format's overflow);
+* integer variants draw from {lo..hi} and are exact in every input format.
 """
 import numpy as np
 
 F16 = 0
 BF16 = 1
 F32 = 2
-DTYPE_NAMES = {F16: "f16", BF16: "bf16", F32: "f32"}
+F8E4M3 = 3
+F8E5M2 = 4
+FP8 = (F8E4M3, F8E5M2)
+DTYPE_NAMES = {F16: "f16", BF16: "bf16", F32: "f32", F8E4M3: "f8e4m3", F8E5M2: "f8e5m2"}
+
+
+def elem_bytes(dtype):
+    return 1 if dtype in FP8 else (4 if dtype == F32 else 2)
 
 
 def f32_to_bf16_bits(x):
@@ -28,13 +38,19 @@ def f32_to_bf16_bits(x):
 
 
 def encode(values, dtype):
-    """binary64 values -> 16-bit patterns of ``dtype`` (nearest-even)."""
+    """binary64 values -> storage patterns of ``dtype`` (nearest-even): uint16
+    for the 16-bit types, uint8 for the 8-bit ones."""
     values = np.asarray(values, dtype=np.float64)
     if dtype == F16:
         return values.astype(np.float16).view(np.uint16)
     if dtype == BF16:
         return f32_to_bf16_bits(values.astype(np.float32))
-    raise ValueError("16-bit input dtypes only")
+    if dtype in FP8:
+        import torch
+        fmt = torch.float8_e4m3fn if dtype == F8E4M3 else torch.float8_e5m2
+        t = torch.from_numpy(np.ascontiguousarray(values)).to(fmt)
+        return t.view(torch.uint8).numpy().copy()
+    raise ValueError("input dtypes are f16, bf16, f8e4m3 and f8e5m2")
 
 
 def uniform(shape, seed, dtype=F16, lo=-1.0, hi=1.0):
