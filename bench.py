@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 import workloads as wl  # noqa: E402
 
 PEAK_TFLOPS_F16 = 2516.6      # MI355X dense fp16/bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_TFLOPS_F8 = 5033.2       # MI355X dense fp8 MFMA: 256 CU x 8192 flop/clk x 2.4 GHz
 HBM_GBPS = 8000.0
 METRIC = "TFLOP/s and % of MI355X fp16 MFMA peak, fp16 GEMM+ReLU 8192³"
 KERNEL_SOURCES = ["dense_tiled_gemm_relu_amd/csrc/gemm_relu_kernel.hpp",
@@ -135,27 +136,49 @@ def cpu_baseline(w, A, B, target_s=15.0):
                       "binary64), %.2f s wall" % (R - 1, R, N, K, w["name"], dt)}
 
 
-def mfma_ceiling(gr, stream, blocks=1024, steps=2048):
-    """MFMA-only throughput on random fp16 operands with no memory traffic (the
-    probe library's probe_mfma_rate: 4 waves per CU, each streaming the 32 MFMAs
-    of one BK=32 step of a 128x128 wave tile).  The chip is power-limited, so
-    this, not 2.4 GHz x 4096 flop/clk/CU, is what the contraction step alone can
-    reach on this machine now.  None if the probe library is not built."""
+def peak_tflops(in_dtype):
+    return PEAK_TFLOPS_F8 if in_dtype in wl.FP8 else PEAK_TFLOPS_F16
+
+
+def torch_dtype(code):
+    import torch
+    return {wl.F16: torch.float16, wl.BF16: torch.bfloat16, wl.F32: torch.float32,
+            wl.F8E4M3: torch.float8_e4m3fn, wl.F8E5M2: torch.float8_e5m2}[code]
+
+
+def to_device(bits, code, shape):
+    """Storage patterns (uint16 or uint8) -> a CUDA tensor of the input type."""
+    import torch
+    bits = np.ascontiguousarray(bits).reshape(shape)
+    raw = bits.view(np.uint8) if code in wl.FP8 else bits.view(np.int16)
+    return torch.from_numpy(raw).cuda().view(torch_dtype(code))
+
+
+def mfma_ceiling(gr, stream, blocks=1024, steps=2048, fp8=False):
+    """MFMA-only throughput on random operands with no memory traffic (the probe
+    library's probe_mfma_rate: 4 waves per CU, each streaming the 32 MFMAs of
+    one step of a 128x128 wave tile; fp16 32x32x16, or with fp8=True E4M3
+    32x32x64).  The chip is power-limited, so this, not 2.4 GHz x the
+    instruction rate, is what the contraction step alone can reach on this machine
+    now.  None if the probe library is not built."""
     import ctypes
     import torch
     if not os.path.exists(gr.PROBE_LIB_PATH):
         return None
     lib = ctypes.CDLL(gr.PROBE_LIB_PATH)
     lib.probe_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                    ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    src = torch.empty(blocks * 8 * 256 * 8, dtype=torch.float16, device="cuda").uniform_(-1, 1)
+                                    ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
+    per_lane = 32 if fp8 else 8                 # operand elements per lane (32 bytes / 16 bytes)
+    src = torch.empty(blocks * 8 * 256 * per_lane, dtype=torch.float32, device="cuda")
+    src = src.uniform_(-1, 1).to(torch.float8_e4m3fn if fp8 else torch.float16)
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     ticks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
     st = stream.cuda_stream
 
     def run(n):
-        rc = lib.probe_mfma_rate(src.data_ptr(), src.numel() * 2, out.data_ptr(), ticks.data_ptr(),
-                                 blocks, n, st)
+        rc = lib.probe_mfma_rate(src.data_ptr(), src.numel() * src.element_size(), out.data_ptr(),
+                                 ticks.data_ptr(), blocks, n, 1 if fp8 else 0, st)
         if rc != 0:
             raise RuntimeError("probe_mfma_rate failed: %d" % rc)
 
@@ -170,10 +193,11 @@ def mfma_ceiling(gr, stream, blocks=1024, steps=2048):
     t = ticks.view(blocks, 2).double()
     cycles = t[:, 0].mean().item()
     clock_mhz = (t[:, 0] / t[:, 1]).mean().item() * 100.0
-    flops = blocks * 4 * steps * 32 * (32 * 32 * 16 * 2)
+    flops = blocks * 4 * steps * 32 * (32 * 32 * (64 if fp8 else 16) * 2)
     return {"tflops": round(flops / sec / 1e12, 1), "clock_mhz": round(clock_mhz),
             "cycles_per_mfma": round(cycles / (steps * 32), 2),
-            "kind": "MFMA-only, random fp16 operands, no memory traffic (probe_mfma_rate)"}
+            "kind": "MFMA-only, random %s operands, no memory traffic (probe_mfma_rate)"
+                    % ("E4M3" if fp8 else "fp16")}
 
 
 def table(gr):
@@ -184,17 +208,19 @@ def table(gr):
     import statistics
     import torch
     stream = torch.cuda.current_stream()
-    tdt = {wl.F16: torch.float16, wl.BF16: torch.bfloat16, wl.F32: torch.float32}
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
-    ceiling = mfma_ceiling(gr, stream)
-    print(json.dumps({"mfma_ceiling": ceiling}), flush=True)
+    ceilings = {False: mfma_ceiling(gr, stream), True: mfma_ceiling(gr, stream, fp8=True)}
+    print(json.dumps({"mfma_ceiling": ceilings[False], "mfma_ceiling_fp8": ceilings[True]}),
+          flush=True)
     for name in sorted(wl.WORKLOADS, key=lambda n: wl.WORKLOADS[n]["index"]):
         w = wl.WORKLOADS[name]
         M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
         A, B = wl.workload_inputs(name)
-        Ad = torch.from_numpy(A.reshape(M, K).view(np.int16)).cuda().view(tdt[ic])
-        Bd = torch.from_numpy(B.reshape(wl.b_shape(M, N, K, tb)).view(np.int16)).cuda().view(tdt[ic])
-        Cd = torch.empty((M, N), dtype=tdt[oc], device="cuda")
+        Ad = to_device(A, ic, (M, K))
+        Bd = to_device(B, ic, wl.b_shape(M, N, K, tb))
+        Cd = torch.empty((M, N), dtype=torch_dtype(oc), device="cuda")
+        ceiling = ceilings[ic in wl.FP8]
+        peak = peak_tflops(ic)
 
         def call():
             gr.gemm_relu(Ad, Bd, Cd, M, N, K, ic, oc, tb, stream)
@@ -224,14 +250,14 @@ def table(gr):
         t = statistics.median(trials)
         tc = statistics.median(cold)
         flops = 2.0 * M * N * K
-        nbytes = 2 * M * K + 2 * K * N + M * N * (4 if oc == wl.F32 else 2)
+        nbytes = wl.elem_bytes(ic) * (M * K + K * N) + M * N * wl.elem_bytes(oc)
         print(json.dumps({
             "workload": name, "M": M, "N": N, "K": K, "in": wl.DTYPE_NAMES[ic],
             "out": wl.DTYPE_NAMES[oc], "transB": tb,
             "tile_config": gr.gemm_relu_plan(Ad, Bd, Cd, M, N, K, ic, oc, tb),
             "t_median_us": round(t, 2), "t_trials_us": [round(x, 2) for x in trials],
             "tflops": round(flops / t / 1e6, 1),
-            "pct_peak": round(100 * flops / t / 1e6 / PEAK_TFLOPS_F16, 2),
+            "pct_peak": round(100 * flops / t / 1e6 / peak, 2), "peak_tflops": peak,
             "pct_of_mfma_ceiling": (round(100 * flops / t / 1e6 / ceiling["tflops"], 1)
                                     if ceiling else None),
             "algorithmic_GBps": round(nbytes / t / 1e3, 1),
@@ -284,10 +310,10 @@ def main():
     w = dict(wl.WORKLOADS[args.workload], name=args.workload)
     M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
     A, B = wl.workload_inputs(args.workload)
-    tdt = {wl.F16: torch.float16, wl.BF16: torch.bfloat16, wl.F32: torch.float32}
-    Ad = torch.from_numpy(A.reshape(M, K).view(np.int16)).cuda().view(tdt[ic])
-    Bd = torch.from_numpy(B.reshape(wl.b_shape(M, N, K, tb)).view(np.int16)).cuda().view(tdt[ic])
-    Cd = torch.empty((M, N), dtype=tdt[oc], device="cuda")
+    Ad = to_device(A, ic, (M, K))
+    Bd = to_device(B, ic, wl.b_shape(M, N, K, tb))
+    Cd = torch.empty((M, N), dtype=torch_dtype(oc), device="cuda")
+    peak = peak_tflops(ic)
     plan = gr.gemm_relu_plan(Ad, Bd, Cd, M, N, K, ic, oc, tb)
     stream = torch.cuda.current_stream()
 
@@ -316,11 +342,14 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kernel_ms * 1e-3) / 1e12
+    metric = METRIC if args.workload == "gemm_relu_f16_8192" else (
+        "TFLOP/s and %% of MI355X %s MFMA peak, %s" %
+        ("fp8" if ic in wl.FP8 else "fp16/bf16", args.workload))
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
-        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS_F16, 2),
+        "pct_of_peak": round(100.0 * value / peak, 2),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -333,14 +362,14 @@ def main():
         "config": {"workload": args.workload, "M": M, "N": N, "K": K,
                    "in": wl.DTYPE_NAMES[ic], "out": wl.DTYPE_NAMES[oc], "transB": tb,
                    "accumulate": "f32", "inputs": w["dist"], "tile_config": plan},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS_F16,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS_F16, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(args.workload),
-                     "algorithmic_bytes": int(2 * M * K + 2 * K * N +
-                                              M * N * (4 if oc == wl.F32 else 2)),
+                     "algorithmic_bytes": int(wl.elem_bytes(ic) * (M * K + K * N) +
+                                              M * N * wl.elem_bytes(oc)),
                      "kernel_ms": round(kernel_ms, 5)},
     }
-    ceiling = mfma_ceiling(gr, stream)
+    ceiling = mfma_ceiling(gr, stream, fp8=ic in wl.FP8)
     if ceiling is not None:
         out["mfma_ceiling"] = dict(ceiling, frac=round(achieved / ceiling["tflops"], 4))
     if not args.no_cpu_baseline:

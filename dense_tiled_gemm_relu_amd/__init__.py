@@ -15,6 +15,8 @@ import os
 F16 = 0
 BF16 = 1
 F32 = 2
+F8E4M3 = 3     # OCP 8-bit E4M3 (inputs only)
+F8E5M2 = 4     # OCP 8-bit E5M2 (inputs only)
 
 OK = 0
 EINVAL = -1
@@ -107,21 +109,25 @@ def gemm_relu_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB):
 
 def _torch_dtype_code(dt):
     import torch
-    return {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}[dt]
+    return {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32,
+            torch.float8_e4m3fn: F8E4M3, torch.float8_e5m2: F8E5M2}[dt]
 
 
 def matmul_relu(A, B, transB=False, out_dtype=None, out=None, stream=None):
     """Tensor front end: returns C = max(A·B, 0) (or max(A·Bᵀ, 0) with transB).
 
-    A: (M, K) fp16/bf16 CUDA tensor; B: (K, N), or (N, K) with transB, same
-    dtype.  C is allocated (like the page's T.empty) unless ``out`` is given;
-    its dtype defaults to A's.
+    A: (M, K) fp16/bf16/float8_e4m3fn/float8_e5m2 CUDA tensor; B: (K, N), or
+    (N, K) with transB, same dtype.  C is allocated (like the page's T.empty)
+    unless ``out`` is given; its dtype defaults to A's for 16-bit inputs and
+    to float16 for 8-bit ones.
     """
     import torch
     if A.dim() != 2 or B.dim() != 2:
         raise ValueError("A and B must be 2-D")
-    if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
-        raise TypeError("A and B must share dtype float16 or bfloat16")
+    inputs = (torch.float16, torch.bfloat16, torch.float8_e4m3fn, torch.float8_e5m2)
+    if A.dtype != B.dtype or A.dtype not in inputs:
+        raise TypeError("A and B must share dtype float16, bfloat16, float8_e4m3fn or "
+                        "float8_e5m2")
     if not (A.is_cuda and B.is_cuda) or A.device != B.device:
         raise ValueError("A and B must be on the same GPU")
     if not (A.is_contiguous() and B.is_contiguous()):
@@ -134,7 +140,8 @@ def matmul_relu(A, B, transB=False, out_dtype=None, out=None, stream=None):
     if Kb != K:
         raise ValueError("inner dimensions differ: %d vs %d" % (K, Kb))
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype or A.dtype, device=A.device)
+        default = A.dtype if A.dtype in (torch.float16, torch.bfloat16) else torch.float16
+        out = torch.empty((M, N), dtype=out_dtype or default, device=A.device)
     elif out.shape != (M, N) or not out.is_contiguous() or out.device != A.device:
         raise ValueError("out must be a contiguous (M, N) tensor on A's device")
     gemm_relu(A, B, out, M, N, K, _torch_dtype_code(A.dtype), _torch_dtype_code(out.dtype),

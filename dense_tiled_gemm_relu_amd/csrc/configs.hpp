@@ -7,9 +7,11 @@
 
 namespace gemm_relu_hip {
 
-// Tile shapes.  "d" = direct global->LDS copies (needs K % 8 == 0, N % 8 == 0
-// and 16-byte aligned operands); "g" = register-staged copies with element-wise
-// bounds checks (any shape and alignment).
+// Tile shapes.  "d" = direct global->LDS copies (any shape and alignment; a
+// (K,N) B needs one full tile of columns); "g" = register-staged copies with
+// element-wise bounds checks (any shape).  BK in a name counts 16-bit
+// elements: the 8-bit instantiation of a configuration takes 2 BK elements per
+// step, so that a step moves the same bytes.
 enum ConfigId : int {
     CFG_D256x256x64_S2 = 0,
     CFG_D256x256x32_S4,
@@ -51,44 +53,48 @@ inline const ConfigInfo& config_info(int id)
     return table[id];
 }
 
+// K elements per step of a configuration whose 16-bit step is BK16 elements.
+template <int IN, int BK16>
+inline constexpr int bk_of = (IN == DT_F8E4M3 || IN == DT_F8E5M2) ? 2 * BK16 : BK16;
+
 template <int IN, int OUT, bool TB, int id> struct CfgOf;
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x64_S2> {
-    using type = Cfg<IN, OUT, TB, 256, 256, 64, 2, 2, 2, true>;
+    using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 64>, 2, 2, 2, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4> {
-    using type = Cfg<IN, OUT, TB, 256, 256, 32, 2, 2, 4, true>;
+    using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 4, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S5> {
-    using type = Cfg<IN, OUT, TB, 256, 256, 32, 2, 2, 5, true>;
+    using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 5, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I> {
-    using type = Cfg<IN, OUT, TB, 256, 256, 32, 2, 2, 4, true, true>;
+    using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 4, true, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_W8I> {
-    using type = Cfg<IN, OUT, TB, 256, 256, 32, 2, 4, 4, true, true>;
+    using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 4, 4, true, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S5_W8I> {
-    using type = Cfg<IN, OUT, TB, 256, 256, 32, 2, 4, 5, true, true>;
+    using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 4, 5, true, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_W8> {
-    using type = Cfg<IN, OUT, TB, 256, 256, 64, 2, 4, 2, true>;
+    using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 64>, 2, 4, 2, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D128x128x64_S3> {
-    using type = Cfg<IN, OUT, TB, 128, 128, 64, 2, 2, 3, true>;
+    using type = Cfg<IN, OUT, TB, 128, 128, bk_of<IN, 64>, 2, 2, 3, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D64x64x64_S4> {
-    using type = Cfg<IN, OUT, TB, 64, 64, 64, 2, 2, 4, true>;
+    using type = Cfg<IN, OUT, TB, 64, 64, bk_of<IN, 64>, 2, 2, 4, true>;
 };
 // Skinny / memory-bound problems: 2 waves, a long BK and 96 KiB of LDS, so one
 // workgroup per CU and twice as many workgroups as the 64x64 tile.
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D64x32x128_S4> {
-    using type = Cfg<IN, OUT, TB, 64, 32, 128, 2, 1, 4, true>;
+    using type = Cfg<IN, OUT, TB, 64, 32, bk_of<IN, 128>, 2, 1, 4, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_G128x128x64> {
-    using type = Cfg<IN, OUT, TB, 128, 128, 64, 2, 2, 2, false>;
+    using type = Cfg<IN, OUT, TB, 128, 128, bk_of<IN, 64>, 2, 2, 2, false>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_G64x64x64> {
-    using type = Cfg<IN, OUT, TB, 64, 64, 64, 2, 2, 2, false>;
+    using type = Cfg<IN, OUT, TB, 64, 64, bk_of<IN, 64>, 2, 2, 2, false>;
 };
 
 typedef hipError_t (*LaunchFn)(const KernelArgs& args, int grid, hipStream_t stream);
@@ -106,6 +112,18 @@ LaunchFn launcher_f16_nn(int out_dt, int cfg);
 LaunchFn launcher_f16_nt(int out_dt, int cfg);
 LaunchFn launcher_bf16_nn(int out_dt, int cfg);
 LaunchFn launcher_bf16_nt(int out_dt, int cfg);
+LaunchFn launcher_f8e4m3_nn(int out_dt, int cfg);
+LaunchFn launcher_f8e4m3_nt(int out_dt, int cfg);
+LaunchFn launcher_f8e5m2_nn(int out_dt, int cfg);
+LaunchFn launcher_f8e5m2_nt(int out_dt, int cfg);
+
+// Configurations built for 8-bit inputs: the ones plan selection can choose
+// (the 16-bit comparison variants are not instantiated for them).
+inline bool fp8_config(int cfg)
+{
+    return cfg == CFG_D256x256x32_S4_I || cfg == CFG_D128x128x64_S3 || cfg == CFG_D64x64x64_S4 ||
+           cfg == CFG_D64x32x128_S4 || cfg == CFG_G128x128x64 || cfg == CFG_G64x64x64;
+}
 
 }  // namespace gemm_relu_hip
 
@@ -131,6 +149,40 @@ LaunchFn launcher_bf16_nt(int out_dt, int cfg);
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S5_W8I>::type>; \
         case CFG_D256x256x64_S2_W8:                                                        \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_W8>::type>;  \
+        case CFG_D128x128x64_S3:                                                           \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D128x128x64_S3>::type>;     \
+        case CFG_D64x64x64_S4:                                                             \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x64x64_S4>::type>;       \
+        case CFG_D64x32x128_S4:                                                            \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x32x128_S4>::type>;      \
+        case CFG_G128x128x64:                                                              \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_G128x128x64>::type>;        \
+        case CFG_G64x64x64:                                                                \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_G64x64x64>::type>;          \
+        default:                                                                           \
+            return nullptr;                                                                \
+        }                                                                                  \
+    }                                                                                      \
+    LaunchFn FN(int out_dt, int cfg)                                                       \
+    {                                                                                      \
+        switch (out_dt) {                                                                  \
+        case DT_F16: return FN##_out<DT_F16>(cfg);                                         \
+        case DT_BF16: return FN##_out<DT_BF16>(cfg);                                       \
+        case DT_F32: return FN##_out<DT_F32>(cfg);                                         \
+        default: return nullptr;                                                           \
+        }                                                                                  \
+    }                                                                                      \
+    }
+
+// Body of an 8-bit instantiation unit: the configurations fp8_config() names.
+#define GEMM_RELU_DEFINE_LAUNCHER_FP8(FN, IN, TB)                                          \
+    namespace gemm_relu_hip {                                                              \
+    template <int OUT>                                                                     \
+    static LaunchFn FN##_out(int cfg)                                                      \
+    {                                                                                      \
+        switch (cfg) {                                                                     \
+        case CFG_D256x256x32_S4_I:                                                         \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I>::type>;   \
         case CFG_D128x128x64_S3:                                                           \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D128x128x64_S3>::type>;     \
         case CFG_D64x64x64_S4:                                                             \

@@ -70,7 +70,12 @@ int check_device()
     return d.ok ? GEMM_RELU_OK : GEMM_RELU_EUNSUPPORTED;
 }
 
-int elem_bytes(int dt) { return dt == GEMM_RELU_F32 ? 4 : 2; }
+int elem_bytes(int dt)
+{
+    return dt == GEMM_RELU_F32 ? 4 : (dt == GEMM_RELU_F8_E4M3 || dt == GEMM_RELU_F8_E5M2) ? 1 : 2;
+}
+
+bool fp8_input(int dt) { return dt == GEMM_RELU_F8_E4M3 || dt == GEMM_RELU_F8_E5M2; }
 
 bool overlaps(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb)
 {
@@ -108,7 +113,7 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
         p.status = GEMM_RELU_EINVAL;
         return p;
     }
-    if ((in_dt != GEMM_RELU_F16 && in_dt != GEMM_RELU_BF16) ||
+    if ((in_dt != GEMM_RELU_F16 && in_dt != GEMM_RELU_BF16 && !fp8_input(in_dt)) ||
         (out_dt != GEMM_RELU_F16 && out_dt != GEMM_RELU_BF16 && out_dt != GEMM_RELU_F32) ||
         (transB != 0 && transB != 1)) {
         p.status = GEMM_RELU_EINVAL;
@@ -118,14 +123,16 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
         p.empty = true;
         return p;
     }
-    const uint64_t a_bytes = uint64_t(M) * uint64_t(K) * 2u;
-    const uint64_t b_bytes = uint64_t(K) * uint64_t(N) * 2u;
+    const uint64_t in_bytes = uint64_t(elem_bytes(in_dt));
+    const uint64_t a_bytes = uint64_t(M) * uint64_t(K) * in_bytes;
+    const uint64_t b_bytes = uint64_t(K) * uint64_t(N) * in_bytes;
     const uint64_t c_bytes = uint64_t(M) * uint64_t(N) * uint64_t(elem_bytes(out_dt));
     if ((a_bytes && !A) || (b_bytes && !B) || !C) {
         p.status = GEMM_RELU_EINVAL;
         return p;
     }
-    if ((reinterpret_cast<uintptr_t>(A) & 1) || (reinterpret_cast<uintptr_t>(B) & 1) ||
+    if ((reinterpret_cast<uintptr_t>(A) & uintptr_t(in_bytes - 1)) ||
+        (reinterpret_cast<uintptr_t>(B) & uintptr_t(in_bytes - 1)) ||
         (reinterpret_cast<uintptr_t>(C) & uintptr_t(elem_bytes(out_dt) - 1))) {
         p.status = GEMM_RELU_EINVAL;
         return p;
@@ -138,7 +145,9 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     }
 
     auto tiles = [&](int id) { return ceil_div(M, config_info(id).bm) * ceil_div(N, config_info(id).bn); };
-    auto usable = [&](int id) { return direct_fits(id, N, K, transB); };
+    auto usable = [&](int id) {
+        return direct_fits(id, N, K, transB) && (!fp8_input(in_dt) || fp8_config(id));
+    };
     // Estimated time of a direct configuration, per K: rounds of workgroups
     // over the CUs, each round the longer of the tile's MFMA time (tile area
     // over its efficiency relative to the 256x256 tile, measured on MI355X:
@@ -173,8 +182,15 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
 
 LaunchFn pick_launcher(int in_dt, int out_dt, int transB, int cfg)
 {
-    if (in_dt == GEMM_RELU_F16) return transB ? launcher_f16_nt(out_dt, cfg) : launcher_f16_nn(out_dt, cfg);
-    return transB ? launcher_bf16_nt(out_dt, cfg) : launcher_bf16_nn(out_dt, cfg);
+    switch (in_dt) {
+    case GEMM_RELU_F16: return transB ? launcher_f16_nt(out_dt, cfg) : launcher_f16_nn(out_dt, cfg);
+    case GEMM_RELU_BF16: return transB ? launcher_bf16_nt(out_dt, cfg) : launcher_bf16_nn(out_dt, cfg);
+    case GEMM_RELU_F8_E4M3:
+        return transB ? launcher_f8e4m3_nt(out_dt, cfg) : launcher_f8e4m3_nn(out_dt, cfg);
+    case GEMM_RELU_F8_E5M2:
+        return transB ? launcher_f8e5m2_nt(out_dt, cfg) : launcher_f8e5m2_nn(out_dt, cfg);
+    default: return nullptr;
+    }
 }
 
 }  // namespace

@@ -10,15 +10,21 @@
 // (transpose_B) and an fp32 C.  Page "从 TVM 到 TileLang…", §三, adds the
 // thread-block rasterisation swizzle (panel of tile rows) for L2 reuse.
 //
+// The same kernel takes 8-bit inputs (OCP E4M3 / E5M2): the FP8 GEMM that
+// §4.1 of the first page lists among the kernels the DSL covers.  The pages
+// give it no scale factors, so it is the same definition over the 8-bit values.
+//
 // What is specific to gfx950 here (none of it is on the pages):
 //   * v_mfma_f32_32x32x16_{f16,bf16}: each lane feeds 8 consecutive k of one
 //     row (or column) and owns 16 fp32 results of a 32x32 block;
+//     v_mfma_f32_32x32x64_f8f6f4 (8-bit inputs, no block scales): the same
+//     result layout, each lane feeding 32 consecutive k;
 //   * global_load_lds_dwordx4: a wave writes 64 x 16 B straight into LDS, lane
 //     i at base + 16 i, with no register round trip; the XOR swizzle of the LDS
 //     layout is realised by choosing which global 16 B chunk each lane fetches;
-//   * ds_read_b64_tr_b16: the LDS transpose read that turns an n-contiguous B
-//     tile into k-contiguous MFMA operands, so row-major B needs no transpose
-//     pass;
+//   * ds_read_b64_tr_b16 / _b8: the LDS transpose reads that turn an
+//     n-contiguous B tile into k-contiguous MFMA operands, so row-major B needs
+//     no transpose pass;
 //   * 256 CUs in 8 XCDs with one L2 each: workgroup w is placed on XCD w mod 8,
 //     so the tile order is remapped to give each XCD a contiguous run of tiles
 //     before the panel swizzle is applied.
@@ -31,7 +37,7 @@
 
 namespace gemm_relu_hip {
 
-enum : int { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2 };
+enum : int { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2, DT_F8E4M3 = 3, DT_F8E5M2 = 4 };
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -40,11 +46,13 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 #define GR_LDS __attribute__((address_space(3)))
 
 struct KernelArgs {
-    const unsigned char* A;   // (M, K) row-major, 16-bit elements
+    const unsigned char* A;   // (M, K) row-major, 16- or 8-bit elements
     const unsigned char* B;   // (K, N) row-major, or (N, K) row-major when transposed
     unsigned char* C;         // (M, N) row-major, 2- or 4-byte elements
     int M, N, K;
@@ -89,20 +97,9 @@ __device__ __forceinline__ uint32_t lds_addr(const GR_LDS unsigned char* p)
     return (uint32_t)(uintptr_t)p;
 }
 
-template <int IN_DT>
-__device__ __forceinline__ f32x16_t mfma_32x32x16(i16x8_t a, i16x8_t b, f32x16_t c)
+__device__ __forceinline__ u32x4_t lds_read_b128(const GR_LDS unsigned char* p)
 {
-    if constexpr (IN_DT == DT_F16)
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
-                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ i16x8_t lds_read_b128(const GR_LDS unsigned char* p)
-{
-    return *reinterpret_cast<const GR_LDS i16x8_t*>(p);
+    return *reinterpret_cast<const GR_LDS u32x4_t*>(p);
 }
 
 __device__ __forceinline__ i16x4_t lds_read_tr16(const GR_LDS unsigned char* p)
@@ -110,6 +107,69 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const GR_LDS unsigned char* p)
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         reinterpret_cast<GR_LDS i16x4_t*>(const_cast<GR_LDS unsigned char*>(p)));
 }
+
+__device__ __forceinline__ i32x2_t lds_read_tr8(const GR_LDS unsigned char* p)
+{
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        reinterpret_cast<GR_LDS i32x2_t*>(const_cast<GR_LDS unsigned char*>(p)));
+}
+
+// Input element types.  A lane's MFMA operand holds the OPB bytes of KMF / 2
+// consecutive k of one row (or column): OPB / 16 chunks of 16 bytes from a
+// k-contiguous LDS row, or OPB / 8 transpose reads of TRK k rows each from an
+// n-contiguous one.
+template <int IN_DT> struct InTraits {
+    static constexpr int EB = 2, KMF = 16, OPB = 16, TRK = 4;
+    using Op = i16x8_t;
+    __device__ static f32x16_t mfma(Op a, Op b, f32x16_t c)
+    {
+        if constexpr (IN_DT == DT_F16)
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                          __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                           __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+    // part x (< OPB / 16) of an operand from one 16-byte LDS read
+    template <int X> __device__ static void set_chunk(Op& v, u32x4_t c)
+    {
+        v = __builtin_bit_cast(Op, c);
+    }
+    // part t (< OPB / 8) of an operand from one transpose read
+    __device__ static void set_tr(Op& v, int t, const GR_LDS unsigned char* p)
+    {
+        const i16x4_t r = lds_read_tr16(p);
+        if (t == 0)
+            v.lo = r;
+        else
+            v.hi = r;
+    }
+};
+template <int FMT> struct InTraitsF8 {
+    static constexpr int EB = 1, KMF = 64, OPB = 32, TRK = 8;
+    using Op = i32x8_t;
+    // format codes of the f8f6f4 MFMA: 0 = E4M3, 1 = E5M2; no block scales
+    __device__ static f32x16_t mfma(Op a, Op b, f32x16_t c)
+    {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, 0, 0, 0);
+    }
+    template <int X> __device__ static void set_chunk(Op& v, u32x4_t c)
+    {
+        if constexpr (X == 0)
+            v.lo = __builtin_bit_cast(i32x4_raw, c);
+        else
+            v.hi = __builtin_bit_cast(i32x4_raw, c);
+    }
+    __device__ static void set_tr(Op& v, int t, const GR_LDS unsigned char* p)
+    {
+        const i32x2_t r = lds_read_tr8(p);
+        v[2 * t] = r[0];
+        v[2 * t + 1] = r[1];
+    }
+    typedef int i32x4_raw __attribute__((ext_vector_type(4)));
+};
+template <> struct InTraits<DT_F8E4M3> : InTraitsF8<0> {};
+template <> struct InTraits<DT_F8E5M2> : InTraitsF8<1> {};
 
 // Output conversion after the ReLU.  max(x, 0) is written as a select so that
 // a negative (or -0) sum becomes +0.
@@ -144,25 +204,32 @@ struct Cfg {
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
     static constexpr int NWAVES = WAVES_M * WAVES_N;
     static constexpr int NTHREADS = 64 * NWAVES;
+    using In = InTraits<IN_DT>;
+    static constexpr int EB = In::EB;                              // bytes per input element
+    static constexpr int EPC = 16 / EB;                            // elements per 16 B chunk
+    static constexpr int FRAG_CH = In::OPB / 16;                   // 16 B reads per k-contiguous operand
+    static constexpr int TR_READS = In::OPB / 8;                   // transpose reads per n-contiguous operand
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
     static constexpr int TM = WM / 32, TN = WN / 32;               // 32x32 MFMA blocks per wave
-    static constexpr int KSUB = BK / 16;                           // MFMA k-steps per BK step
-    static constexpr int ROW_CH = BK / 8;                          // 16 B chunks per k-contiguous row
-    static constexpr int NROW_CH = BN / 8;                         // 16 B chunks per n-contiguous row
-    static constexpr int A_BYTES = BM * BK * 2;
-    static constexpr int B_BYTES = BN * BK * 2;
+    static constexpr int KSUB = BK / In::KMF;                      // MFMA k-steps per BK step
+    static constexpr int ROW_CH = BK * EB / 16;                    // 16 B chunks per k-contiguous row
+    static constexpr int NROW_CH = BN * EB / 16;                   // 16 B chunks per n-contiguous row
+    static constexpr int A_BYTES = BM * BK * EB;
+    static constexpr int B_BYTES = BN * BK * EB;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-    static constexpr int A_CH = BM * BK / 8;                       // 16 B chunks per stage
-    static constexpr int B_CH = BN * BK / 8;
+    static constexpr int A_CH = BM * ROW_CH;                       // 16 B chunks per stage
+    static constexpr int B_CH = BN * BK * EB / 16;
     static constexpr int A_PER_THREAD = A_CH / NTHREADS;
     static constexpr int B_PER_THREAD = B_CH / NTHREADS;
     static constexpr int LOADS_PER_STAGE = A_PER_THREAD + B_PER_THREAD;  // vm ops per wave per stage
 
     static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tiling");
-    static_assert(BK == 32 || BK == 64 || BK == 128, "BK");
+    static_assert(BK * EB == 64 || BK * EB == 128 || BK * EB == 256, "k-contiguous rows of 64, 128 or 256 bytes");
+    static_assert(KSUB >= 1 && BK % In::KMF == 0, "whole MFMA k-steps per BK step");
+    static_assert(KSUB % 2 == 0 || INTERLEAVE_, "an odd k-step count needs the step-parity tags of the interleaved loop");
     static_assert(A_CH % NTHREADS == 0 && B_CH % NTHREADS == 0, "loader tiling");
-    static_assert(TRANS_B || BN >= 32, "n-contiguous B rows of at least 4 chunks");
+    static_assert(TRANS_B || NROW_CH >= (EB == 2 ? 4 : 2), "n-contiguous B rows of at least 64 (16-bit) or 32 (8-bit) bytes");
         static_assert(STAGES >= 2 && STAGES <= 5, "stages");
     static_assert((STAGES - 2) * LOADS_PER_STAGE < 64, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity of a gfx950 CU");
@@ -172,7 +239,7 @@ struct Cfg {
     // scheduling region; each region also carries a share of the next
     // k-step's fragment reads and of the current k-step's MFMAs.
     static constexpr int NM = TM * TN;                          // MFMAs per k-step
-    static constexpr int NR = TM + (TRANS_B ? TN : 2 * TN);     // LDS read ops per k-step
+    static constexpr int NR = TM * FRAG_CH + TN * (TRANS_B ? FRAG_CH : TR_READS);  // LDS read ops per k-step
     static constexpr int REGIONS = LOADS_PER_STAGE / KSUB;      // = copies per k-step
     static_assert(!INTERLEAVE || (DIRECT && STAGES >= 3), "interleave needs >= 3 direct stages");
     static_assert(!INTERLEAVE || (LOADS_PER_STAGE % KSUB == 0 && REGIONS >= 1 &&
@@ -204,20 +271,19 @@ __device__ __forceinline__ int swz_krow(int r)
 }
 
 // XOR swizzle of an n-contiguous B row (B stored (K,N)) of NROW_CH chunks.
-// A transpose read serves 32 lanes per cycle: 4 consecutive k rows x 4
-// consecutive chunks (64 bytes of n).  XOR-ing the chunk index with
-// 4 (k mod 4) puts the 4 rows on 4 disjoint chunk quads of the bank window;
-// with 8-chunk rows two rows share a window, so 4 ((k / 2) mod 2) suffices;
-// 4-chunk rows already place 4 consecutive rows in one window.
-template <int NROW_CH>
+// A transpose read serves 32 lanes per cycle: TRK consecutive k rows x W =
+// 16 / TRK consecutive chunks (16-bit: 4 rows x 4 chunks; 8-bit: 8 rows x 2
+// chunks).  With RPW = 16 / NROW_CH rows sharing a 256-byte bank window (1
+// when the row fills it), XOR-ing the chunk index with W ((k / RPW) mod
+// (NROW_CH / W)) puts those TRK rows on disjoint chunk groups of the window.
+// The swizzle repeats every TRK rows, so rows k and k + TRK share it.
+template <int NROW_CH, int TRK>
 __device__ __forceinline__ int swz_nrow(int k)
 {
-    if constexpr (NROW_CH >= 16)
-        return 4 * (k & 3);
-    else if constexpr (NROW_CH == 8)
-        return 4 * ((k >> 1) & 1);
-    else
-        return 0;
+    constexpr int W = 16 / TRK;
+    constexpr int WIN = NROW_CH < 16 ? NROW_CH : 16;
+    constexpr int RPW = 16 / WIN;
+    return W * ((k / RPW) % (WIN / W));
 }
 
 // ------------------------------------------------------------ tile order
@@ -250,6 +316,9 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     constexpr int TM = C::TM, TN = C::TN, KSUB = C::KSUB;
     constexpr int ROW_CH = C::ROW_CH, NROW_CH = C::NROW_CH;
     constexpr int APT = C::A_PER_THREAD, BPT = C::B_PER_THREAD;
+    constexpr int EB = C::EB, EPC = C::EPC, FRAG_CH = C::FRAG_CH, TR_READS = C::TR_READS;
+    using In = typename C::In;
+    using Op = typename In::Op;
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[C::LDS_BYTES];
     GR_LDS unsigned char* smem = (GR_LDS unsigned char*)(smem_raw);
@@ -283,7 +352,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     };
     auto nrow_slot = [&](int q, int& k, int& c) {
         k = q / NROW_CH;
-        c = (q % NROW_CH) ^ swz_nrow<NROW_CH>(k);
+        c = (q % NROW_CH) ^ swz_nrow<NROW_CH, In::TRK>(k);
     };
     uint32_t a_src[APT];
 #pragma unroll
@@ -291,7 +360,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         int r, c;
         krow_slot(i * C::NTHREADS + tid, r, c);
         const int row = min(m0 + r, M - 1) - m0;           // clamp: finite data, output discarded
-        a_src[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)c * 16u;
+        a_src[i] = (uint32_t)row * (uint32_t)K * (uint32_t)EB + (uint32_t)c * 16u;
     }
     uint32_t b_src[BPT];
 #pragma unroll
@@ -300,16 +369,16 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         if constexpr (C::TRANS_B) {
             krow_slot(i * C::NTHREADS + tid, r, c);
             const int row = min(n0 + r, N - 1) - n0;
-            b_src[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)c * 16u;
+            b_src[i] = (uint32_t)row * (uint32_t)K * (uint32_t)EB + (uint32_t)c * 16u;
         } else {
             nrow_slot(i * C::NTHREADS + tid, r, c);
-            b_src[i] = (uint32_t)r * (uint32_t)N * 2u + (uint32_t)c * 16u;
+            b_src[i] = (uint32_t)r * (uint32_t)N * (uint32_t)EB + (uint32_t)c * 16u;
         }
     }
 
-    const unsigned char* a_tile = args.A + (size_t)m0 * (size_t)K * 2u;
-    const unsigned char* b_tile = C::TRANS_B ? args.B + (size_t)n0 * (size_t)K * 2u
-                                             : args.B + (size_t)n0 * 2u;
+    const unsigned char* a_tile = args.A + (size_t)m0 * (size_t)K * EB;
+    const unsigned char* b_tile = C::TRANS_B ? args.B + (size_t)n0 * (size_t)K * EB
+                                             : args.B + (size_t)n0 * EB;
 
     // ---- direct loader: global -> LDS without registers.
     const uint32_t smem_addr = lds_addr(smem);
@@ -317,9 +386,9 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         const int k0 = t * BK;
         const uint32_t sa = smem_addr + stage * C::STAGE_BYTES;
         const uint32_t sb = sa + C::A_BYTES;
-        const unsigned char* ga = a_tile + (size_t)k0 * 2u;
-        const unsigned char* gb = C::TRANS_B ? b_tile + (size_t)k0 * 2u
-                                             : b_tile + (size_t)k0 * (size_t)N * 2u;
+        const unsigned char* ga = a_tile + (size_t)k0 * EB;
+        const unsigned char* gb = C::TRANS_B ? b_tile + (size_t)k0 * EB
+                                             : b_tile + (size_t)k0 * (size_t)N * EB;
         // every pipelined step lies inside K and every chunk inside its row
 #pragma unroll
         for (int i = 0; i < APT; ++i) dma16(ga, a_src[i], sa + (i * C::NWAVES + wave) * 1024);
@@ -335,19 +404,26 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     u32x4_t ra[APT], rb[BPT];
     auto load_chunk = [&](const unsigned char* base, size_t row_off, int e0, int e_lim,
                           bool row_ok) -> u32x4_t {
-        // 8 consecutive 16-bit elements e0 .. e0+7 of one row; valid if e < e_lim.
+        // EPC consecutive elements e0 .. e0+EPC-1 of one row; valid if e < e_lim.
         u32x4_t v = {0u, 0u, 0u, 0u};
         if (!row_ok) return v;
-        const unsigned short* p =
-            reinterpret_cast<const unsigned short*>(base + row_off) + e0;
-        if (e0 + 8 <= e_lim) {
-            __builtin_memcpy(&v, p, 16);
-        } else {
+        if (e0 + EPC <= e_lim) {
+            __builtin_memcpy(&v, base + row_off + (size_t)e0 * EB, 16);
+        } else if constexpr (EB == 2) {
+            const unsigned short* p =
+                reinterpret_cast<const unsigned short*>(base + row_off) + e0;
             unsigned short h[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) h[e] = (e0 + e < e_lim) ? p[e] : (unsigned short)0;
             v = u32x4_t{h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16),
                         h[4] | ((unsigned)h[5] << 16), h[6] | ((unsigned)h[7] << 16)};
+        } else {
+            const unsigned char* p = base + row_off + e0;
+            unsigned w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (e0 + e < e_lim) w[e >> 2] |= (unsigned)p[e] << (8 * (e & 3));
+            v = u32x4_t{w[0], w[1], w[2], w[3]};
         }
         return v;
     };
@@ -356,17 +432,17 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     auto a_chunk = [&](int t, int q) -> u32x4_t {
         int r, c;
         krow_slot(q, r, c);
-        return load_chunk(args.A, (size_t)(m0 + r) * (size_t)K * 2u, t * BK + 8 * c, K, m0 + r < M);
+        return load_chunk(args.A, (size_t)(m0 + r) * (size_t)K * EB, t * BK + EPC * c, K, m0 + r < M);
     };
     auto b_chunk = [&](int t, int q) -> u32x4_t {
         int r, c;
         if constexpr (C::TRANS_B) {
             krow_slot(q, r, c);
-            return load_chunk(args.B, (size_t)(n0 + r) * (size_t)K * 2u, t * BK + 8 * c, K,
+            return load_chunk(args.B, (size_t)(n0 + r) * (size_t)K * EB, t * BK + EPC * c, K,
                               n0 + r < N);
         } else {
             nrow_slot(q, r, c);
-            return load_chunk(args.B, (size_t)(t * BK + r) * (size_t)N * 2u, n0 + 8 * c, N,
+            return load_chunk(args.B, (size_t)(t * BK + r) * (size_t)N * EB, n0 + EPC * c, N,
                               t * BK + r < K);
         }
     };
@@ -408,34 +484,43 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     const int wave_m = wave / C::WAVES_N, wave_n = wave % C::WAVES_N;
     const int wm0 = wave_m * C::WM, wn0 = wave_n * C::WN;
     const int l32 = lane & 31, g = lane >> 5;
-    // k-contiguous rows: lane reads row (w0 + 32 i + l32), chunk (2 s + g).
-    uint32_t a_rd[KSUB];
+    // k-contiguous rows: for k-step s the lane reads row (w0 + 32 i + l32),
+    // chunks (2 s + g) FRAG_CH + x, x < FRAG_CH (its KMF / 2 consecutive k).
+    uint32_t a_rd[KSUB][FRAG_CH];
 #pragma unroll
-    for (int s = 0; s < KSUB; ++s) {
-        const int r = wm0 + l32;
-        a_rd[s] = (uint32_t)(r * BK * 2 + (((2 * s + g) ^ swz_krow<ROW_CH>(r)) * 16));
-    }
-    uint32_t b_rd[C::TRANS_B ? KSUB : TN];
+    for (int s = 0; s < KSUB; ++s)
+#pragma unroll
+        for (int x = 0; x < FRAG_CH; ++x) {
+            const int r = wm0 + l32;
+            a_rd[s][x] = (uint32_t)(r * BK * EB +
+                                    ((((2 * s + g) * FRAG_CH + x) ^ swz_krow<ROW_CH>(r)) * 16));
+        }
+    uint32_t b_rd[C::TRANS_B ? KSUB : TN][C::TRANS_B ? FRAG_CH : 1];
     if constexpr (C::TRANS_B) {
 #pragma unroll
-        for (int s = 0; s < KSUB; ++s) {
-            const int r = wn0 + l32;
-            b_rd[s] = (uint32_t)(r * BK * 2 + (((2 * s + g) ^ swz_krow<ROW_CH>(r)) * 16));
-        }
+        for (int s = 0; s < KSUB; ++s)
+#pragma unroll
+            for (int x = 0; x < FRAG_CH; ++x) {
+                const int r = wn0 + l32;
+                b_rd[s][x] = (uint32_t)(r * BK * EB +
+                                        ((((2 * s + g) * FRAG_CH + x) ^ swz_krow<ROW_CH>(r)) * 16));
+            }
     } else {
-        // Transpose read: 16-lane group h reads a 4 (k) x 16 (n) block; lane i16 of
-        // the group supplies row kk = 8 (h / 2) + i16 / 4 (+ 4 t + 16 s) and the
-        // 4 columns 16 (h % 2) + 4 (i16 % 4) of the 32-column MFMA block j, and
-        // receives the 4 k values of column 16 (h % 2) + i16.  The swizzle of
-        // row kk equals that of kk + 4 t + 16 s, so one offset per block serves
-        // every (s, t).
+        // Transpose reads: 16-lane group h holds the k-group h / 2 and the
+        // n-half h % 2 of an MFMA block; each read covers TRK k rows, LPR lanes
+        // per row each supplying 8 bytes.  Lane i16 supplies row
+        // (KMF / 2) (h / 2) + i16 / LPR (+ TRK t + KMF s) and the 8 bytes from
+        // column 16 (h % 2) + (i16 % LPR) (8 / EB) of the block, and receives
+        // the TRK k values of column 16 (h % 2) + i16.  The swizzle repeats
+        // every TRK rows, so one offset per block serves every (s, t).
+        constexpr int TRK = In::TRK, LPR = 16 / TRK;
         const int h = lane >> 4, i16 = lane & 15;
-        const int kk = 8 * (h >> 1) + (i16 >> 2);
+        const int kk = (In::KMF / 2) * (h >> 1) + i16 / LPR;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int n = wn0 + 32 * j + 16 * (h & 1) + 4 * (i16 & 3);
-            const int phys = (n >> 3) ^ swz_nrow<NROW_CH>(kk);
-            b_rd[j] = (uint32_t)(kk * BN * 2 + phys * 16 + (n & 7) * 2);
+            const int n = wn0 + 32 * j + 16 * (h & 1) + (i16 % LPR) * (8 / EB);
+            const int phys = ((n * EB) >> 4) ^ swz_nrow<NROW_CH, TRK>(kk);
+            b_rd[j][0] = (uint32_t)(kk * BN * EB + phys * 16 + ((n * EB) & 15));
         }
     }
 
@@ -447,46 +532,39 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Fragments of one MFMA k-step: TM A blocks and TN B blocks of 32 x 16.
+    // Fragments of one MFMA k-step: TM A blocks and TN B blocks of 32 x (KMF).
     struct Frags {
-        i16x8_t a[TM], b[TN];
+        Op a[TM], b[TN];
     };
-    // One LDS read op q of k-step s: q < TM reads A block q; the rest read B
-    // block j (transposed B: one 16-byte read; (K,N) B: two transpose reads,
-    // the k halves 0..3 and 4..7 of the block).
+    // One LDS read op q of k-step s: the first TM FRAG_CH read A block
+    // q / FRAG_CH, part q % FRAG_CH; the rest read B block j (transposed B:
+    // FRAG_CH 16-byte reads; (K,N) B: TR_READS transpose reads of TRK k rows).
     auto read_op = [&](int stage, int s, int q, Frags& f) {
         const GR_LDS unsigned char* sa = smem + stage * C::STAGE_BYTES;
         const GR_LDS unsigned char* sb = sa + C::A_BYTES;
-        if (q < TM) {
-            f.a[q] = lds_read_b128(sa + a_rd[s] + q * 32 * BK * 2);
-        } else if constexpr (C::TRANS_B) {
-            const int j = q - TM;
-            f.b[j] = lds_read_b128(sb + b_rd[s] + j * 32 * BK * 2);
-        } else {
-            const int j = (q - TM) >> 1, half = (q - TM) & 1;
-            const i16x4_t v = lds_read_tr16(sb + b_rd[j] + s * 16 * BN * 2 + half * 4 * BN * 2);
-            if (half == 0)
-                f.b[j].lo = v;
+        constexpr int QA = TM * FRAG_CH;
+        if (q < QA) {
+            const int i = q / FRAG_CH, x = q % FRAG_CH;
+            const u32x4_t v = lds_read_b128(sa + a_rd[s][x] + i * 32 * BK * EB);
+            if (x == 0)
+                In::template set_chunk<0>(f.a[i], v);
             else
-                f.b[j].hi = v;
+                In::template set_chunk<1>(f.a[i], v);
+        } else if constexpr (C::TRANS_B) {
+            const int j = (q - QA) / FRAG_CH, x = (q - QA) % FRAG_CH;
+            const u32x4_t v = lds_read_b128(sb + b_rd[s][x] + j * 32 * BK * EB);
+            if (x == 0)
+                In::template set_chunk<0>(f.b[j], v);
+            else
+                In::template set_chunk<1>(f.b[j], v);
+        } else {
+            const int j = (q - QA) / TR_READS, t = (q - QA) % TR_READS;
+            In::set_tr(f.b[j], t, sb + b_rd[j][0] + (s * In::KMF + t * In::TRK) * BN * EB);
         }
     };
     auto read_frags = [&](int stage, int s, Frags& f) {
-        const GR_LDS unsigned char* sa = smem + stage * C::STAGE_BYTES;
-        const GR_LDS unsigned char* sb = sa + C::A_BYTES;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) f.a[i] = lds_read_b128(sa + a_rd[s] + i * 32 * BK * 2);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            if constexpr (C::TRANS_B) {
-                f.b[j] = lds_read_b128(sb + b_rd[s] + j * 32 * BK * 2);
-            } else {
-                const GR_LDS unsigned char* p = sb + b_rd[j] + s * 16 * BN * 2;
-                const i16x4_t lo4 = lds_read_tr16(p);
-                const i16x4_t hi4 = lds_read_tr16(p + 4 * BN * 2);
-                f.b[j] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-        }
+        for (int q = 0; q < C::NR; ++q) read_op(stage, s, q, f);
     };
     // Operands swapped (B block as the MFMA's first source) so that each lane
     // ends up owning 4 consecutive n of one output row.
@@ -495,7 +573,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                acc[i][j] = mfma_32x32x16<C::IN_DT>(f.b[j], f.a[i], acc[i][j]);
+                acc[i][j] = In::mfma(f.b[j], f.a[i], acc[i][j]);
     };
 
     Frags fr[2];
@@ -506,9 +584,9 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
             const int k0 = t * BK;
             const uint32_t sa = smem_addr + stage * C::STAGE_BYTES;
             const uint32_t sb = sa + C::A_BYTES;
-            const unsigned char* ga = a_tile + (size_t)k0 * 2u;
-            const unsigned char* gb = C::TRANS_B ? b_tile + (size_t)k0 * 2u
-                                                 : b_tile + (size_t)k0 * (size_t)N * 2u;
+            const unsigned char* ga = a_tile + (size_t)k0 * EB;
+            const unsigned char* gb = C::TRANS_B ? b_tile + (size_t)k0 * EB
+                                                 : b_tile + (size_t)k0 * (size_t)N * EB;
             if (l < APT)
                 dma16(ga, a_src[l], sa + (l * C::NWAVES + wave) * 1024);
             else
@@ -517,7 +595,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         // MFMA p of a k-step: B block p / TM against A block p % TM
         auto mfma_op = [&](const Frags& f, int p) {
             const int j = p / TM, i = p % TM;
-            acc[i][j] = mfma_32x32x16<C::IN_DT>(f.b[j], f.a[i], acc[i][j]);
+            acc[i][j] = In::mfma(f.b[j], f.a[i], acc[i][j]);
         };
 
 #pragma unroll
@@ -533,16 +611,19 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
             for (int q = 0; q < NR; ++q) read_op(0, 0, q, fr[0]);
         }
         // One BK step.  STEADY: the stage S-1 ahead exists, so the step needs
-        // no run-time checks.
-        auto step = [&](int t, auto steady_tag) {
+        // no run-time checks.  PARITY = t mod 2: with an odd number of k-steps
+        // per BK step the two fragment sets swap roles from one step to the
+        // next (k-step s of step t contracts set (t KSUB + s) mod 2).
+        auto step = [&](int t, auto steady_tag, auto parity_tag) {
             constexpr bool STEADY = decltype(steady_tag)::value;
+            constexpr int PARITY = decltype(parity_tag)::value;
             const int stage = t % S;
             const bool loads = STEADY || t + S - 1 < nk;
             const int ld_stage = (t + S - 1) % S;
             const int ld_k0 = (t + S - 1) * BK;
-            const unsigned char* ga = a_tile + (size_t)ld_k0 * 2u;
-            const unsigned char* gb = C::TRANS_B ? b_tile + (size_t)ld_k0 * 2u
-                                                 : b_tile + (size_t)ld_k0 * (size_t)N * 2u;
+            const unsigned char* ga = a_tile + (size_t)ld_k0 * EB;
+            const unsigned char* gb = C::TRANS_B ? b_tile + (size_t)ld_k0 * EB
+                                                 : b_tile + (size_t)ld_k0 * (size_t)N * EB;
             const uint32_t lsa = smem_addr + ld_stage * C::STAGE_BYTES;
             const uint32_t lsb = lsa + C::A_BYTES;
 #pragma unroll
@@ -573,18 +654,38 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
                     if (reads) {
 #pragma unroll
                         for (int q = r * NR / R; q < (r + 1) * NR / R; ++q)
-                            read_op(rd_stage, rd_s, q, fr[(s + 1) & 1]);
+                            read_op(rd_stage, rd_s, q, fr[(PARITY * KSUB + s + 1) & 1]);
                     }
 #pragma unroll
-                    for (int p = r * NM / R; p < (r + 1) * NM / R; ++p) mfma_op(fr[s & 1], p);
+                    for (int p = r * NM / R; p < (r + 1) * NM / R; ++p)
+                        mfma_op(fr[(PARITY * KSUB + s) & 1], p);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
         // steady steps: stage t+S-1 < nk
         const int t_steady = max(0, nk - (S - 1));
-        for (int t = 0; t < t_steady; ++t) step(t, std::integral_constant<bool, true>{});
-        for (int t = t_steady; t < nk; ++t) step(t, std::integral_constant<bool, false>{});
+        using Steady = std::integral_constant<bool, true>;
+        using Checked = std::integral_constant<bool, false>;
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        if constexpr (KSUB % 2 == 0) {
+            for (int t = 0; t < t_steady; ++t) step(t, Steady{}, P0{});
+            for (int t = t_steady; t < nk; ++t) step(t, Checked{}, P0{});
+        } else {
+            // steps in pairs, so that every step's parity is known at compile
+            // time; a steady step left over before the checked ones runs checked
+            int t = 0;
+            for (; t + 1 < t_steady; t += 2) {
+                step(t, Steady{}, P0{});
+                step(t + 1, Steady{}, P1{});
+            }
+            for (; t + 1 < nk; t += 2) {
+                step(t, Checked{}, P0{});
+                step(t + 1, Checked{}, P1{});
+            }
+            if (t < nk) step(t, Checked{}, P0{});
+        }
     } else if constexpr (C::DIRECT) {
         // Pipeline: S-1 stages in flight ahead of the one being contracted.
         // At the last k-step of stage t the wave waits for stage t+1, meets the

@@ -1,5 +1,6 @@
 // Test-only probes of the gfx950 8-bit data paths, with raw per-lane I/O so
-// that the host can check the lane layouts it assumes:
+// that the host can check the lane layouts the kernel assumes, through the
+// kernel's own helpers (InTraits<>::mfma, lds_read_tr8, dma16):
 //   * probe_mfma_f8_raw — one v_mfma_f32_32x32x64_f8f6f4 (no block scales):
 //     lane l supplies 32 bytes of each operand and returns its 16 results;
 //   * probe_tr8_raw — one ds_read_b64_tr_b8 per lane at caller-chosen LDS
@@ -17,21 +18,18 @@ using namespace gemm_relu_hip;
 
 namespace {
 
-typedef int i32x8_raw __attribute__((ext_vector_type(8)));
-typedef int i32x2_raw __attribute__((ext_vector_type(2)));
-
 // a, b: 64 x 32 bytes (lane-major); d: 64 x 16 floats (lane-major).
-// fmt 0: both operands E4M3, 1: both E5M2.
-template <int FMT>
+// IN_DT: both operands E4M3 or both E5M2.
+template <int IN_DT>
 __global__ void k_mfma_f8_raw(const uint8_t* a, const uint8_t* b, float* d)
 {
     const int l = threadIdx.x;
-    i32x8_raw av, bv;
+    i32x8_t av, bv;
     __builtin_memcpy(&av, a + 32 * l, 32);
     __builtin_memcpy(&bv, b + 32 * l, 32);
     f32x16_t acc;
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, FMT, FMT, 0, 0, 0, 0);
+    acc = InTraits<IN_DT>::mfma(av, bv, acc);
     for (int r = 0; r < 16; ++r) d[16 * l + r] = acc[r];
 }
 
@@ -42,10 +40,8 @@ __global__ void k_tr8_raw(const uint8_t* src, const uint32_t* off, uint8_t* out)
     __shared__ __attribute__((aligned(16))) uint8_t lds[4096];
     for (int i = threadIdx.x; i < 4096; i += 64) lds[i] = src[i];
     __syncthreads();
-    typedef __attribute__((address_space(3))) i32x2_raw lds_i32x2;
     const uint32_t o = off[threadIdx.x] & 0xFF8u;
-    const i32x2_raw v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-        (lds_i32x2*)((GR_LDS unsigned char*)lds + o));
+    const i32x2_t v = lds_read_tr8((const GR_LDS unsigned char*)lds + o);
     __builtin_memcpy(out + 8 * threadIdx.x, &v, 8);
 }
 
@@ -80,9 +76,9 @@ int finish(hipError_t e)
 extern "C" int probe_mfma_f8_raw(const void* a, const void* b, void* d, int fmt)
 {
     if (fmt == 0)
-        k_mfma_f8_raw<0><<<1, 64>>>((const uint8_t*)a, (const uint8_t*)b, (float*)d);
+        k_mfma_f8_raw<DT_F8E4M3><<<1, 64>>>((const uint8_t*)a, (const uint8_t*)b, (float*)d);
     else if (fmt == 1)
-        k_mfma_f8_raw<1><<<1, 64>>>((const uint8_t*)a, (const uint8_t*)b, (float*)d);
+        k_mfma_f8_raw<DT_F8E5M2><<<1, 64>>>((const uint8_t*)a, (const uint8_t*)b, (float*)d);
     else
         return -1;
     return finish(hipGetLastError());

@@ -30,7 +30,7 @@ __global__ void k_mfma(const uint16_t* X, const uint16_t* Y, float* D)
     }
     f32x16_t acc;
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    acc = mfma_32x32x16<IN_DT>(a, b, acc);
+    acc = InTraits<IN_DT>::mfma(a, b, acc);
     for (int r = 0; r < 16; ++r) D[(8 * (r / 4) + 4 * g + r % 4) * 32 + r32] = acc[r];
 }
 

@@ -2,10 +2,11 @@
 // contraction step on a power-limited chip.
 //
 // Each workgroup is 4 waves (one per SIMD, 512 registers each, one workgroup per
-// CU).  Every wave repeats `steps` rounds of 32 independent
-// v_mfma_f32_32x32x16_f16 over 16 accumulators and 4 + 4 operand registers: the
-// MFMA stream of one BK=32 step of a 128x128 wave tile, with no memory traffic
-// and no LDS.  The operands are the caller's random fp16 data, so the multiplier
+// CU).  Every wave repeats `steps` rounds of 32 independent MFMAs over 16
+// accumulators and 4 + 4 operand registers: the MFMA stream of one step of a
+// 128x128 wave tile, with no memory traffic and no LDS.  kind 0:
+// v_mfma_f32_32x32x16_f16 (16-byte operands); kind 1:
+// v_mfma_f32_32x32x64_f8f6f4 on E4M3 data (32-byte operands).  The operands are the caller's random fp16 data, so the multiplier
 // arrays toggle as they do in the GEMM; on MI355X this, not the instruction
 // rate, sets the shader clock.  Wave 0 of each workgroup records the shader
 // cycles (s_memtime) and 100 MHz reference ticks (s_memrealtime) of its loop.
@@ -15,23 +16,28 @@
 #include <cstddef>
 #include <cstdint>
 
-namespace {
+#include "gemm_relu_kernel.hpp"
 
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+using namespace gemm_relu_hip;
+
+namespace {
 
 constexpr int kThreads = 256;
 constexpr int kOperandRegs = 8;     // 4 A + 4 B fragments per lane
 
+template <int IN_DT>
 __global__ void __launch_bounds__(kThreads, 1)
-k_mfma_rate(const f16x8_t* src, float* out, unsigned long long* ticks, int steps)
+k_mfma_rate(const unsigned char* src, float* out, unsigned long long* ticks, int steps)
 {
+    using In = InTraits<IN_DT>;
+    using Op = typename In::Op;
     const int tid = threadIdx.x;
+    const Op* ops = reinterpret_cast<const Op*>(src);
     const size_t base = (size_t)blockIdx.x * kOperandRegs * kThreads + tid;
-    f16x8_t a[4], b[4];
+    Op a[4], b[4];
     for (int i = 0; i < 4; ++i) {
-        a[i] = src[base + (size_t)i * kThreads];
-        b[i] = src[base + (size_t)(4 + i) * kThreads];
+        a[i] = ops[base + (size_t)i * kThreads];
+        b[i] = ops[base + (size_t)(4 + i) * kThreads];
     }
     f32x16_t acc[16];
     for (int i = 0; i < 16; ++i)
@@ -44,7 +50,7 @@ k_mfma_rate(const f16x8_t* src, float* out, unsigned long long* ticks, int steps
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int p = 0; p < 16; ++p)
-                acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[p / 4], a[p % 4], acc[p], 0, 0, 0);
+                acc[p] = In::mfma(b[p / 4], a[p % 4], acc[p]);
         __builtin_amdgcn_s_barrier();
     }
     const unsigned long long c1 = __builtin_amdgcn_s_memtime();
@@ -61,17 +67,26 @@ k_mfma_rate(const f16x8_t* src, float* out, unsigned long long* ticks, int steps
 
 }  // namespace
 
-// src: at least blocks * 8 * 256 * 16 bytes of fp16 data; out: blocks * 256
-// floats; ticks: 2 * blocks values (shader cycles, reference ticks per
-// workgroup).  Launches on `stream` without synchronising.  Returns 0, -1 on
-// bad sizes, -3 on a launch failure.
+// src: at least blocks * 8 * 256 * OPB bytes of input data (OPB = 16 for
+// kind 0, fp16; 32 for kind 1, E4M3); out: blocks * 256 floats; ticks:
+// 2 * blocks values (shader cycles, reference ticks per workgroup).  Launches
+// on `stream` without synchronising.  Returns 0, -1 on bad arguments, -3 on a
+// launch failure.
 extern "C" int probe_mfma_rate(const void* src, size_t src_bytes, void* out, void* ticks,
-                               int blocks, int steps, void* stream)
+                               int blocks, int steps, int kind, void* stream)
 {
+    if (kind != 0 && kind != 1) return -1;
+    const size_t opb = kind == 0 ? 16 : 32;
     if (!src || !out || !ticks || blocks <= 0 || steps <= 0 ||
-        src_bytes < (size_t)blocks * kOperandRegs * kThreads * sizeof(f16x8_t))
+        src_bytes < (size_t)blocks * kOperandRegs * kThreads * opb)
         return -1;
-    hipLaunchKernelGGL(k_mfma_rate, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream,
-                       (const f16x8_t*)src, (float*)out, (unsigned long long*)ticks, steps);
+    const hipStream_t st = (hipStream_t)stream;
+    const unsigned char* s = (const unsigned char*)src;
+    if (kind == 0)
+        hipLaunchKernelGGL(k_mfma_rate<DT_F16>, dim3(blocks), dim3(kThreads), 0, st, s,
+                           (float*)out, (unsigned long long*)ticks, steps);
+    else
+        hipLaunchKernelGGL(k_mfma_rate<DT_F8E4M3>, dim3(blocks), dim3(kThreads), 0, st, s,
+                           (float*)out, (unsigned long long*)ticks, steps);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }

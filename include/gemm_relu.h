@@ -28,6 +28,11 @@ extern "C" {
 #define GEMM_RELU_F16  0 /* IEEE binary16 (inputs or output) */
 #define GEMM_RELU_BF16 1 /* bfloat16 (inputs or output) */
 #define GEMM_RELU_F32  2 /* IEEE binary32 (output only) */
+/* OCP 8-bit floating point (inputs only).  The first page's §4.1 lists an FP8
+ * GEMM among the kernels the DSL covers but gives it no scale factors: the
+ * product is the same definition over the exact values of the 8-bit inputs. */
+#define GEMM_RELU_F8_E4M3 3 /* E4M3 ("FN"): bias 7, largest finite 448, no infinities */
+#define GEMM_RELU_F8_E5M2 4 /* E5M2: bias 15, IEEE-style infinities and NaNs */
 
 /* Status codes.  The library never aborts, throws or prints. */
 #define GEMM_RELU_OK            0
@@ -47,19 +52,20 @@ extern "C" {
  *   M, N, K    sizes, >= 0 and <= INT32_MAX.  M == 0 or N == 0: nothing to do,
  *              returns GEMM_RELU_OK without touching the device.  K == 0: every
  *              element of C becomes +0 (an empty sum).
- *   in_dtype   GEMM_RELU_F16 or GEMM_RELU_BF16 (A and B share it).
+ *   in_dtype   GEMM_RELU_F16, GEMM_RELU_BF16, GEMM_RELU_F8_E4M3 or
+ *              GEMM_RELU_F8_E5M2 (A and B share it).
  *   out_dtype  GEMM_RELU_F16, GEMM_RELU_BF16 or GEMM_RELU_F32.
  *   transB     0 or 1, as above.
  *   stream     a hipStream_t, or NULL for the null stream.
  *
- * Layout: dense rows, no leading-dimension arguments.  A and B need 2-byte
- * alignment, C the alignment of its element type; any shape is accepted (the
- * fastest path is taken when K and N are multiples of 8 and all three pointers
- * are 16-byte aligned).
+ * Layout: dense rows, no leading-dimension arguments.  A, B and C need the
+ * alignment of their element type (1 byte for the 8-bit inputs); any shape is
+ * accepted.
  *
- * Numerics: products of the 16-bit inputs are summed in fp32 on the matrix
- * units (order unspecified); the fp32 sum goes through max(x, 0) — a negative
- * or zero sum gives +0 — and is rounded to nearest-even into out_dtype.
+ * Numerics: products of the inputs (exact in fp32 for every input type) are
+ * summed in fp32 on the matrix units (order unspecified); the fp32 sum goes
+ * through max(x, 0) — a negative or zero sum gives +0 — and is rounded to
+ * nearest-even into out_dtype.
  *
  * Ownership: the caller owns A, B and C; the library keeps no pointer after the
  * call returns and allocates no device memory.

@@ -46,9 +46,14 @@ def fp32_sum_bound(absum, ref, K, out_unit_roundoff):
 
 # ------------------------------------------------------------------ GPU side
 def to_device(bits, dtype_code, shape):
-    """uint16 storage patterns -> contiguous CUDA tensor of fp16/bf16."""
+    """Storage patterns (uint16 for fp16/bf16, uint8 for the 8-bit formats) ->
+    contiguous CUDA tensor of the input type."""
     import torch
-    t = torch.from_numpy(np.ascontiguousarray(bits).reshape(shape).view(np.int16)).cuda()
+    bits = np.ascontiguousarray(bits).reshape(shape)
+    if dtype_code in (3, 4):
+        t = torch.from_numpy(bits.view(np.uint8)).cuda()
+        return t.view(torch.float8_e4m3fn if dtype_code == 3 else torch.float8_e5m2)
+    t = torch.from_numpy(bits.view(np.int16)).cuda()
     return t.view(torch.float16 if dtype_code == 0 else torch.bfloat16)
 
 

@@ -51,7 +51,9 @@ A, B, C = 1 << 32, 2 << 32, 3 << 32
     (A, B, C, 4, 4, -1, 0, 0, 0),            # negative K
     (A, B, C, 2 ** 31, 4, 4, 0, 0, 0),       # beyond INT32_MAX
     (A, B, C, 4, 4, 4, 2, 0, 0),             # fp32 input not supported
-    (A, B, C, 4, 4, 4, 0, 3, 0),             # unknown output code
+    (A, B, C, 4, 4, 4, 0, 3, 0),             # 8-bit output not supported
+    (A, B, C, 4, 4, 4, 5, 0, 0),             # unknown input code
+    (A, B, C, 4, 4, 4, 3, 4, 0),             # 8-bit output not supported
     (A, B, C, 4, 4, 4, 0, 0, 2),             # transB not in {0, 1}
     (0, B, C, 4, 4, 4, 0, 0, 0),             # NULL A with elements
     (A, 0, C, 4, 4, 4, 0, 0, 0),             # NULL B with elements
@@ -95,6 +97,28 @@ def test_null_operands_allowed_when_K_is_zero():
 def test_plan_selection(M, N, K, transB, aligned, want):
     off = 0 if aligned else 2
     assert gr.gemm_relu_plan(A + off, B, C, M, N, K, 0, 0, transB) == want
+
+
+@pytest.mark.parametrize("M,N,K,transB,want", [
+    (8192, 8192, 8192, 0, "d256x256x32_s4_i"),
+    (4096, 7168, 4096, 1, "d256x256x32_s4_i"),
+    (64, 8192, 8192, 0, "d64x32x128_s4"),
+    (100, 16, 100, 0, "g64x64x64"),                   # fewer than 16 columns of (K,N) B
+    (100, 16, 100, 1, "d64x32x128_s4"),
+])
+@pytest.mark.parametrize("in_code", [3, 4])
+def test_plan_selection_fp8(M, N, K, transB, want, in_code):
+    assert gr.gemm_relu_plan(A, B, C, M, N, K, in_code, 0, transB) == want
+    # 8-bit operands may start at any byte
+    assert gr.gemm_relu_plan(A + 1, B + 3, C, M, N, K, in_code, 0, transB) == want
+
+
+def test_fp8_forced_comparison_configuration_falls_back(monkeypatch):
+    # the 16-bit comparison variants are not built for 8-bit inputs
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x256x32_s4_w8i")
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 3, 0, 0) == "d256x256x32_s4_i"
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "g128x128x64")
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 3, 0, 0) == "g128x128x64"
 
 
 def test_forced_configuration(monkeypatch):

@@ -126,6 +126,101 @@ def test_coded_mapping(cfg, transB, monkeypatch):
     assert np.array_equal(got, np.maximum(bkn[pi, :], 0.0))
 
 
+# ----------------------------------------------------------- 8-bit inputs
+FP8_CONFIGS = ["d256x256x32_s4_i", "d128x128x64_s3", "d64x64x64_s4", "d64x32x128_s4",
+               "g128x128x64", "g64x64x64"]
+FP8 = [wl.F8E4M3, wl.F8E5M2]
+
+
+@pytest.mark.parametrize("cfg", FP8_CONFIGS)
+@pytest.mark.parametrize("in_code", FP8)
+@pytest.mark.parametrize("out_code", [wl.F16, wl.BF16, wl.F32])
+@pytest.mark.parametrize("transB", [0, 1])
+@pytest.mark.parametrize("shape", [(264, 520, 400), (301, 517, 203)], ids=["k16", "ragged"])
+def test_fp8_configs_integer_bitexact(cfg, in_code, out_code, transB, shape, monkeypatch):
+    # 8-bit rows of odd length start at every byte offset; K % BK != 0 in both
+    M, N, K = shape
+    A, B = int_inputs(M, N, K, in_code, transB, 600, out_code)
+    ref = oracle.gemm_relu_ref(A, B, M, N, K, in_code, transB)
+    assert np.abs(ref).max() < exact_limit(out_code)
+    got = run(A, B, M, N, K, in_code, out_code, transB, cfg, monkeypatch)
+    assert np.array_equal(got, ref)
+    assert not np.any(np.signbit(got))
+
+
+@pytest.mark.parametrize("cfg", FP8_CONFIGS)
+@pytest.mark.parametrize("in_code", FP8)
+@pytest.mark.parametrize("transB", [0, 1])
+def test_fp8_configs_uniform_tolerance(cfg, in_code, transB, monkeypatch):
+    M, N, K = (331, 263, 461)
+    A, B = wl.make_inputs(M, N, K, in_code, transB, "uniform", 210)
+    got = run(A, B, M, N, K, in_code, wl.F16, transB, cfg, monkeypatch)
+    ref = oracle.gemm_relu_ref(A, B, M, N, K, in_code, transB)
+    check_close(got, ref, K, wl.F16)
+    rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    _, absum = oracle.gemm_relu_ref_at(A, B, rows.ravel(), cols.ravel(), M, N, K, in_code, transB)
+    bound = fp32_sum_bound(absum.reshape(M, N), ref, K, unit_roundoff(wl.F16))
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+@pytest.mark.parametrize("cfg", FP8_CONFIGS)
+@pytest.mark.parametrize("transB", [0, 1])
+def test_fp8_coded_mapping(cfg, transB, monkeypatch):
+    """As test_coded_mapping, with E4M3 operands."""
+    M, N, K = (203, 333, 269)
+    rng = np.random.default_rng(4)
+    pi = rng.permutation(K)[:M]
+    a = np.zeros((M, K))
+    a[np.arange(M), pi] = 1.0
+    k = np.arange(K)[:, None]
+    j = np.arange(N)[None, :]
+    bkn = ((131 * k + 7 * j) % 5 - 2).astype(np.float64)
+    b = bkn.T if transB else bkn
+    A, B = wl.encode(a, wl.F8E4M3), wl.encode(b, wl.F8E4M3)
+    got = run(A, B, M, N, K, wl.F8E4M3, wl.F16, transB, cfg, monkeypatch)
+    assert np.array_equal(got, np.maximum(bkn[pi, :], 0.0))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 8), (65, 72, 136), (33, 200, 520), (300, 16, 64),
+                                   (70, 300, 24), (257, 263, 1), (5, 259, 37), (129, 264, 200)])
+@pytest.mark.parametrize("transB", [0, 1])
+@pytest.mark.parametrize("in_code", FP8)
+def test_fp8_tail_shapes(M, N, K, transB, in_code):
+    A, B = int_inputs(M, N, K, in_code, transB, 700 + M, wl.F32)
+    ref = oracle.gemm_relu_ref(A, B, M, N, K, in_code, transB)
+    got = run(A, B, M, N, K, in_code, wl.F32, transB)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("off_a,off_b", [(1, 0), (0, 3), (5, 7), (15, 1)])
+@pytest.mark.parametrize("transB", [0, 1])
+def test_fp8_unaligned_pointers(off_a, off_b, transB):
+    """8-bit operands that start 1..15 bytes past an aligned allocation."""
+    import torch
+    M, N, K = 300, 520, 264
+    A, B = int_inputs(M, N, K, wl.F8E4M3, transB, 750, wl.F16)
+    Ab = torch.zeros(M * K + 16, dtype=torch.uint8, device="cuda")
+    Bb = torch.zeros(K * N + 16, dtype=torch.uint8, device="cuda")
+    Ab[off_a:off_a + M * K] = torch.from_numpy(A.reshape(-1)).cuda()
+    Bb[off_b:off_b + K * N] = torch.from_numpy(B.reshape(-1)).cuda()
+    Cd = out_tensor(M, N, wl.F16)
+    gr.gemm_relu(Ab[off_a:], Bb[off_b:], Cd, M, N, K, wl.F8E4M3, wl.F16, transB)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_device(Cd),
+                          oracle.gemm_relu_ref(A, B, M, N, K, wl.F8E4M3, transB))
+
+
+def test_fp8_matmul_relu_front_end():
+    import torch
+    M, N, K = 130, 260, 200
+    A, B = int_inputs(M, N, K, wl.F8E5M2, 0, 760, wl.F16)
+    Ad, Bd = to_device(A, wl.F8E5M2, (M, K)), to_device(B, wl.F8E5M2, (K, N))
+    C = gr.matmul_relu(Ad, Bd)
+    torch.cuda.synchronize()
+    assert C.dtype == torch.float16
+    assert np.array_equal(from_device(C), oracle.gemm_relu_ref(A, B, M, N, K, wl.F8E5M2, 0))
+
+
 # ----------------------------------------------------------- tail sweep
 SIZES = [1, 2, 7, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 258]
 TAIL_SHAPES = [(SIZES[i], SIZES[(i + 5) % 19], SIZES[(i + 11) % 19]) for i in range(19)] + \

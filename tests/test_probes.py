@@ -97,27 +97,35 @@ def test_unaligned_16_byte_loads(probe):
     assert np.array_equal(got[0], want), "direct global->LDS copy"
 
 
-def test_mfma_rate_probe(probe):
-    """The MFMA-only diagnostic (random fp16 operands, no memory traffic) runs,
-    issues one 32x32x16 MFMA per 32 shader cycles per SIMD, and keeps its
-    accumulators finite; size errors are rejected before launch."""
+@pytest.mark.parametrize("kind,opb,cycles", [(0, 16, 32), (1, 32, 64)], ids=["f16", "e4m3"])
+def test_mfma_rate_probe(probe, kind, opb, cycles):
+    """The MFMA-only diagnostic (random operands, no memory traffic) runs, issues
+    one 32x32x16 fp16 MFMA per 32 shader cycles (one 32x32x64 E4M3 MFMA per
+    64) per SIMD, and keeps its accumulators finite; size errors are rejected
+    before launch."""
     import torch
     lib = probe
     lib.probe_mfma_rate.restype = ctypes.c_int
     lib.probe_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                    ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+                                    ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
     blocks, steps = 256, 256
-    src = torch.empty(blocks * 8 * 256 * 8, dtype=torch.float16, device="cuda").uniform_(-1, 1)
+    per_lane = opb // 2 if kind == 0 else opb           # elements per operand per lane
+    src = torch.empty(blocks * 8 * 256 * per_lane, dtype=torch.float32, device="cuda")
+    src = src.uniform_(-1, 1).to(torch.float16 if kind == 0 else torch.float8_e4m3fn)
+    nbytes = src.numel() * src.element_size()
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     ticks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
     st = torch.cuda.current_stream().cuda_stream
-    assert lib.probe_mfma_rate(src.data_ptr(), src.numel() * 2 - 2, out.data_ptr(),
-                               ticks.data_ptr(), blocks, steps, st) == -1
-    assert lib.probe_mfma_rate(src.data_ptr(), src.numel() * 2, out.data_ptr(),
-                               ticks.data_ptr(), blocks, steps, st) == 0
+    assert lib.probe_mfma_rate(src.data_ptr(), nbytes - 1, out.data_ptr(),
+                               ticks.data_ptr(), blocks, steps, kind, st) == -1
+    assert lib.probe_mfma_rate(src.data_ptr(), nbytes, out.data_ptr(),
+                               ticks.data_ptr(), blocks, steps, 2, st) == -1
+    assert lib.probe_mfma_rate(src.data_ptr(), nbytes, out.data_ptr(),
+                               ticks.data_ptr(), blocks, steps, kind, st) == 0
     torch.cuda.synchronize()
     cyc = ticks.view(blocks, 2)[:, 0].double().mean().item() / (steps * 32)
-    assert 31.9 <= cyc <= 40.0, cyc
+    assert cycles - 0.1 <= cyc <= cycles * 1.25, cyc
     assert torch.isfinite(out).all()
 
 

@@ -88,6 +88,9 @@ WORKLOADS = {
                                          out_dtype=F16, transB=0, dist="uniform"),
     "gemm_relu_f16_64x8192x8192": dict(index=6, M=64, N=8192, K=8192, in_dtype=F16,
                                        out_dtype=F16, transB=0, dist="uniform"),
+    # the FP8 GEMM of the first page's capability list at the headline shape
+    "gemm_relu_f8e4m3_8192": dict(index=7, M=8192, N=8192, K=8192, in_dtype=F8E4M3,
+                                  out_dtype=F16, transB=0, dist="uniform"),
 }
 
 
