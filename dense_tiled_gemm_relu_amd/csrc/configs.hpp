@@ -17,6 +17,7 @@ enum ConfigId : int {
     CFG_D256x256x32_S4,
     CFG_D256x256x32_S5,
     CFG_D256x256x32_S4_I,
+    CFG_D256x256x64_S2_16,
     CFG_D256x256x32_S4_W8I,
     CFG_D256x256x32_S5_W8I,
     CFG_D256x256x64_S2_W8,
@@ -41,6 +42,7 @@ inline const ConfigInfo& config_info(int id)
         {"d256x256x32_s4", 256, 256, true},
         {"d256x256x32_s5", 256, 256, true},
         {"d256x256x32_s4_i", 256, 256, true},
+        {"d256x256x64_s2_16", 256, 256, true},
         {"d256x256x32_s4_w8i", 256, 256, true},
         {"d256x256x32_s5_w8i", 256, 256, true},
         {"d256x256x64_s2_w8", 256, 256, true},
@@ -69,6 +71,14 @@ template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S5
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I> {
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 4, true, true>;
+};
+// d256x256x64_s2 contracted with 16x16x32 MFMAs (8 x 8 blocks per wave instead
+// of 4 x 4): 16-bit inputs only.  A comparison variant: the 16x16 form draws
+// less power per MAC, but the interleaved pipeline needs one MFMA k-step per
+// 32-k step with it, and the compiler then shuffles its 64 accumulator
+// tuples every step.
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_16> {
+    using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 64>, 2, 2, 2, true, false, 16>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_W8I> {
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 4, 4, true, true>;
@@ -143,6 +153,8 @@ inline bool fp8_config(int cfg)
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S5>::type>;     \
         case CFG_D256x256x32_S4_I:                                                         \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I>::type>;   \
+        case CFG_D256x256x64_S2_16:                                                        \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_16>::type>;  \
         case CFG_D256x256x32_S4_W8I:                                                       \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_W8I>::type>; \
         case CFG_D256x256x32_S5_W8I:                                                       \

@@ -19,6 +19,10 @@
 //     row (or column) and owns 16 fp32 results of a 32x32 block;
 //     v_mfma_f32_32x32x64_f8f6f4 (8-bit inputs, no block scales): the same
 //     result layout, each lane feeding 32 consecutive k;
+//     v_mfma_f32_16x16x32_{f16,bf16}: each lane feeds 8 consecutive k of one of
+//     16 rows (4 k groups) and owns 4 fp32 results of a 16x16 block — per MAC
+//     it moves less accumulator data than the 32x32 form, and on random data
+//     the power-limited chip clocks it higher;
 //   * global_load_lds_dwordx4: a wave writes 64 x 16 B straight into LDS, lane
 //     i at base + 16 i, with no register round trip; the XOR swizzle of the LDS
 //     layout is realised by choosing which global 16 B chunk each lane fetches;
@@ -44,6 +48,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
@@ -114,21 +119,35 @@ __device__ __forceinline__ i32x2_t lds_read_tr8(const GR_LDS unsigned char* p)
         reinterpret_cast<GR_LDS i32x2_t*>(const_cast<GR_LDS unsigned char*>(p)));
 }
 
-// Input element types.  A lane's MFMA operand holds the OPB bytes of KMF / 2
-// consecutive k of one row (or column): OPB / 16 chunks of 16 bytes from a
-// k-contiguous LDS row, or OPB / 8 transpose reads of TRK k rows each from an
-// n-contiguous one.
-template <int IN_DT> struct InTraits {
-    static constexpr int EB = 2, KMF = 16, OPB = 16, TRK = 4;
+// Input element types and MFMA shapes.  MB is the MFMA block (32: 32x32 C
+// block; 16: 16x16), NG = 64 / MB lane groups along k.  A lane's operand holds
+// the OPB bytes of KMF / NG consecutive k of one row (or column): OPB / 16
+// chunks of 16 bytes from a k-contiguous LDS row, or OPB / 8 transpose reads
+// of TRK k rows each from an n-contiguous one.  Acc is a lane's share of one
+// C block (NACC fp32 values).
+template <int IN_DT, int MB = 32> struct InTraits {
+    static_assert(MB == 32 || MB == 16, "MFMA block");
+    static constexpr int EB = 2, KMF = MB == 32 ? 16 : 32, OPB = 16, TRK = 4;
+    static constexpr int NACC = MB * MB / 64;
     using Op = i16x8_t;
-    __device__ static f32x16_t mfma(Op a, Op b, f32x16_t c)
+    using Acc = std::conditional_t<MB == 32, f32x16_t, f32x4_t>;
+    __device__ static Acc mfma(Op a, Op b, Acc c)
     {
-        if constexpr (IN_DT == DT_F16)
-            return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
-                                                          __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-        else
-            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                           __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+        if constexpr (MB == 32) {
+            if constexpr (IN_DT == DT_F16)
+                return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                              __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+            else
+                return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                               __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+        } else {
+            if constexpr (IN_DT == DT_F16)
+                return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                              __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+            else
+                return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                               __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+        }
     }
     // part x (< OPB / 16) of an operand from one 16-byte LDS read
     template <int X> __device__ static void set_chunk(Op& v, u32x4_t c)
@@ -146,10 +165,11 @@ template <int IN_DT> struct InTraits {
     }
 };
 template <int FMT> struct InTraitsF8 {
-    static constexpr int EB = 1, KMF = 64, OPB = 32, TRK = 8;
+    static constexpr int EB = 1, KMF = 64, OPB = 32, TRK = 8, NACC = 16;
     using Op = i32x8_t;
+    using Acc = f32x16_t;
     // format codes of the f8f6f4 MFMA: 0 = E4M3, 1 = E5M2; no block scales
-    __device__ static f32x16_t mfma(Op a, Op b, f32x16_t c)
+    __device__ static Acc mfma(Op a, Op b, Acc c)
     {
         return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, 0, 0, 0);
     }
@@ -168,8 +188,12 @@ template <int FMT> struct InTraitsF8 {
     }
     typedef int i32x4_raw __attribute__((ext_vector_type(4)));
 };
-template <> struct InTraits<DT_F8E4M3> : InTraitsF8<0> {};
-template <> struct InTraits<DT_F8E5M2> : InTraitsF8<1> {};
+template <int MB> struct InTraits<DT_F8E4M3, MB> : InTraitsF8<0> {
+    static_assert(MB == 32, "8-bit inputs use the 32x32 block");
+};
+template <int MB> struct InTraits<DT_F8E5M2, MB> : InTraitsF8<1> {
+    static_assert(MB == 32, "8-bit inputs use the 32x32 block");
+};
 
 // Output conversion after the ReLU.  max(x, 0) is written as a select so that
 // a negative (or -0) sum becomes +0.
@@ -196,7 +220,7 @@ template <> struct OutTraits<DT_F32> {
 
 // ---------------------------------------------------------- configuration
 template <int IN_DT_, int OUT_DT_, bool TRANS_B_, int BM_, int BN_, int BK_, int WAVES_M_,
-          int WAVES_N_, int STAGES_, bool DIRECT_, bool INTERLEAVE_ = false>
+          int WAVES_N_, int STAGES_, bool DIRECT_, bool INTERLEAVE_ = false, int MB_ = 32>
 struct Cfg {
     static constexpr int IN_DT = IN_DT_, OUT_DT = OUT_DT_;
     static constexpr bool TRANS_B = TRANS_B_, DIRECT = DIRECT_, INTERLEAVE = INTERLEAVE_;
@@ -204,13 +228,15 @@ struct Cfg {
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
     static constexpr int NWAVES = WAVES_M * WAVES_N;
     static constexpr int NTHREADS = 64 * NWAVES;
-    using In = InTraits<IN_DT>;
+    static constexpr int MB = MB_;                                 // MFMA C block (32 or 16)
+    static constexpr int NG = 64 / MB;                             // lane groups along k
+    using In = InTraits<IN_DT, MB>;
     static constexpr int EB = In::EB;                              // bytes per input element
     static constexpr int EPC = 16 / EB;                            // elements per 16 B chunk
     static constexpr int FRAG_CH = In::OPB / 16;                   // 16 B reads per k-contiguous operand
     static constexpr int TR_READS = In::OPB / 8;                   // transpose reads per n-contiguous operand
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;   // wave tile
-    static constexpr int TM = WM / 32, TN = WN / 32;               // 32x32 MFMA blocks per wave
+    static constexpr int TM = WM / MB, TN = WN / MB;               // MFMA blocks per wave
     static constexpr int KSUB = BK / In::KMF;                      // MFMA k-steps per BK step
     static constexpr int ROW_CH = BK * EB / 16;                    // 16 B chunks per k-contiguous row
     static constexpr int NROW_CH = BN * EB / 16;                   // 16 B chunks per n-contiguous row
@@ -224,7 +250,8 @@ struct Cfg {
     static constexpr int B_PER_THREAD = B_CH / NTHREADS;
     static constexpr int LOADS_PER_STAGE = A_PER_THREAD + B_PER_THREAD;  // vm ops per wave per stage
 
-    static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tiling");
+    static_assert(BM % (MB * WAVES_M) == 0 && BN % (MB * WAVES_N) == 0, "wave tiling");
+    static_assert(MB == 32 || TRANS_B || BN * EB >= 256, "16x16 blocks read (K,N) B rows of >= 16 chunks");
     static_assert(BK * EB == 64 || BK * EB == 128 || BK * EB == 256, "k-contiguous rows of 64, 128 or 256 bytes");
     static_assert(KSUB >= 1 && BK % In::KMF == 0, "whole MFMA k-steps per BK step");
     static_assert(KSUB % 2 == 0 || INTERLEAVE_, "an odd k-step count needs the step-parity tags of the interleaved loop");
@@ -277,13 +304,23 @@ __device__ __forceinline__ int swz_krow(int r)
 // when the row fills it), XOR-ing the chunk index with W ((k / RPW) mod
 // (NROW_CH / W)) puts those TRK rows on disjoint chunk groups of the window.
 // The swizzle repeats every TRK rows, so rows k and k + TRK share it.
-template <int NROW_CH, int TRK>
+//
+// With 16x16 blocks (16-bit inputs, rows of >= 16 chunks) the 32 lanes are two
+// k groups of one block: rows 4 t + (0..3) and 8 + 4 t + (0..3), 2 chunks each;
+// XOR-ing with 2 (k mod 4) + 8 ((k / 8) mod 2) spreads those 8 rows over the 8
+// chunk pairs of the window.  This swizzle repeats every 16 rows only.
+template <int NROW_CH, int TRK, int MB = 32>
 __device__ __forceinline__ int swz_nrow(int k)
 {
-    constexpr int W = 16 / TRK;
-    constexpr int WIN = NROW_CH < 16 ? NROW_CH : 16;
-    constexpr int RPW = 16 / WIN;
-    return W * ((k / RPW) % (WIN / W));
+    if constexpr (MB == 16) {
+        static_assert(NROW_CH >= 16, "16x16 blocks: rows of >= 16 chunks");
+        return 2 * (k & 3) + 8 * ((k >> 3) & 1);
+    } else {
+        constexpr int W = 16 / TRK;
+        constexpr int WIN = NROW_CH < 16 ? NROW_CH : 16;
+        constexpr int RPW = 16 / WIN;
+        return W * ((k / RPW) % (WIN / W));
+    }
 }
 
 // ------------------------------------------------------------ tile order
@@ -352,7 +389,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     };
     auto nrow_slot = [&](int q, int& k, int& c) {
         k = q / NROW_CH;
-        c = (q % NROW_CH) ^ swz_nrow<NROW_CH, In::TRK>(k);
+        c = (q % NROW_CH) ^ swz_nrow<NROW_CH, In::TRK, C::MB>(k);
     };
     uint32_t a_src[APT];
 #pragma unroll
@@ -483,56 +520,65 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     // ---- fragment read geometry (per lane, relative to a stage's A / B region).
     const int wave_m = wave / C::WAVES_N, wave_n = wave % C::WAVES_N;
     const int wm0 = wave_m * C::WM, wn0 = wave_n * C::WN;
-    const int l32 = lane & 31, g = lane >> 5;
-    // k-contiguous rows: for k-step s the lane reads row (w0 + 32 i + l32),
-    // chunks (2 s + g) FRAG_CH + x, x < FRAG_CH (its KMF / 2 consecutive k).
+    constexpr int MB = C::MB, NG = C::NG;
+    const int lr = lane % MB, g = lane / MB;     // row (column) of the block, k group
+    // k-contiguous rows: for k-step s the lane reads row (w0 + MB i + lr),
+    // chunks (NG s + g) FRAG_CH + x, x < FRAG_CH (its KMF / NG consecutive k).
     uint32_t a_rd[KSUB][FRAG_CH];
 #pragma unroll
     for (int s = 0; s < KSUB; ++s)
 #pragma unroll
         for (int x = 0; x < FRAG_CH; ++x) {
-            const int r = wm0 + l32;
+            const int r = wm0 + lr;
             a_rd[s][x] = (uint32_t)(r * BK * EB +
-                                    ((((2 * s + g) * FRAG_CH + x) ^ swz_krow<ROW_CH>(r)) * 16));
+                                    ((((NG * s + g) * FRAG_CH + x) ^ swz_krow<ROW_CH>(r)) * 16));
         }
-    uint32_t b_rd[C::TRANS_B ? KSUB : TN][C::TRANS_B ? FRAG_CH : 1];
+    // (K,N) B offsets per block j and transpose read t (per t only where the
+    // swizzle does not repeat every TRK rows: 16x16 blocks)
+    constexpr int B_RD_T = C::TRANS_B ? FRAG_CH : (MB == 16 ? TR_READS : 1);
+    uint32_t b_rd[C::TRANS_B ? KSUB : TN][B_RD_T];
     if constexpr (C::TRANS_B) {
 #pragma unroll
         for (int s = 0; s < KSUB; ++s)
 #pragma unroll
             for (int x = 0; x < FRAG_CH; ++x) {
-                const int r = wn0 + l32;
+                const int r = wn0 + lr;
                 b_rd[s][x] = (uint32_t)(r * BK * EB +
-                                        ((((2 * s + g) * FRAG_CH + x) ^ swz_krow<ROW_CH>(r)) * 16));
+                                        ((((NG * s + g) * FRAG_CH + x) ^ swz_krow<ROW_CH>(r)) * 16));
             }
     } else {
-        // Transpose reads: 16-lane group h holds the k-group h / 2 and the
-        // n-half h % 2 of an MFMA block; each read covers TRK k rows, LPR lanes
-        // per row each supplying 8 bytes.  Lane i16 supplies row
-        // (KMF / 2) (h / 2) + i16 / LPR (+ TRK t + KMF s) and the 8 bytes from
-        // column 16 (h % 2) + (i16 % LPR) (8 / EB) of the block, and receives
-        // the TRK k values of column 16 (h % 2) + i16.  The swizzle repeats
-        // every TRK rows, so one offset per block serves every (s, t).
+        // Transpose reads: 16-lane group h holds k group gk and n-half nh of an
+        // MFMA block (32x32: gk = h / 2, nh = h % 2; 16x16: gk = h, nh = 0);
+        // each read covers TRK k rows, LPR lanes per row each supplying 8
+        // bytes.  Lane i16 supplies row (KMF / NG) gk + i16 / LPR (+ TRK t +
+        // KMF s) and the 8 bytes from column 16 nh + (i16 % LPR) (8 / EB) of
+        // the block, and receives the TRK k values of column 16 nh + i16.
         constexpr int TRK = In::TRK, LPR = 16 / TRK;
         const int h = lane >> 4, i16 = lane & 15;
-        const int kk = (In::KMF / 2) * (h >> 1) + i16 / LPR;
+        const int gk = MB == 32 ? (h >> 1) : h, nh = MB == 32 ? (h & 1) : 0;
+        const int kk = (In::KMF / NG) * gk + i16 / LPR;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = wn0 + 32 * j + 16 * (h & 1) + (i16 % LPR) * (8 / EB);
-            const int phys = ((n * EB) >> 4) ^ swz_nrow<NROW_CH, TRK>(kk);
-            b_rd[j][0] = (uint32_t)(kk * BN * EB + phys * 16 + ((n * EB) & 15));
-        }
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int t = 0; t < B_RD_T; ++t) {
+                const int n = wn0 + MB * j + 16 * nh + (i16 % LPR) * (8 / EB);
+                const int k = kk + t * TRK;
+                const int phys = ((n * EB) >> 4) ^ swz_nrow<NROW_CH, TRK, MB>(k);
+                b_rd[j][t] = (uint32_t)(k * BN * EB + phys * 16 + ((n * EB) & 15));
+            }
     }
 
-    f32x16_t acc[TM][TN];
+    using Acc = typename In::Acc;
+    constexpr int NACC = In::NACC;
+    Acc acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < NACC; ++r) acc[i][j][r] = 0.0f;
 
-    // Fragments of one MFMA k-step: TM A blocks and TN B blocks of 32 x (KMF).
+    // Fragments of one MFMA k-step: TM A blocks and TN B blocks of MB x (KMF).
     struct Frags {
         Op a[TM], b[TN];
     };
@@ -545,21 +591,23 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         constexpr int QA = TM * FRAG_CH;
         if (q < QA) {
             const int i = q / FRAG_CH, x = q % FRAG_CH;
-            const u32x4_t v = lds_read_b128(sa + a_rd[s][x] + i * 32 * BK * EB);
+            const u32x4_t v = lds_read_b128(sa + a_rd[s][x] + i * MB * BK * EB);
             if (x == 0)
                 In::template set_chunk<0>(f.a[i], v);
             else
                 In::template set_chunk<1>(f.a[i], v);
         } else if constexpr (C::TRANS_B) {
             const int j = (q - QA) / FRAG_CH, x = (q - QA) % FRAG_CH;
-            const u32x4_t v = lds_read_b128(sb + b_rd[s][x] + j * 32 * BK * EB);
+            const u32x4_t v = lds_read_b128(sb + b_rd[s][x] + j * MB * BK * EB);
             if (x == 0)
                 In::template set_chunk<0>(f.b[j], v);
             else
                 In::template set_chunk<1>(f.b[j], v);
         } else {
             const int j = (q - QA) / TR_READS, t = (q - QA) % TR_READS;
-            In::set_tr(f.b[j], t, sb + b_rd[j][0] + (s * In::KMF + t * In::TRK) * BN * EB);
+            const uint32_t off = B_RD_T == 1 ? b_rd[j][0] + t * In::TRK * BN * EB
+                                             : b_rd[j][B_RD_T == 1 ? 0 : t];
+            In::set_tr(f.b[j], t, sb + off + s * In::KMF * BN * EB);
         }
     };
     auto read_frags = [&](int stage, int s, Frags& f) {
@@ -760,8 +808,8 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     }
 
     // ---- epilogue: ReLU on the fp32 accumulators, convert, store.
-    // Lane owns C[m][n .. n+3] with m = m0 + wm0 + 32 i + l32 and
-    // n = n0 + wn0 + 32 j + 8 q + 4 g, for q = 0..3 (registers 4q .. 4q+3).
+    // Lane owns C[m][n .. n+3] with m = m0 + wm0 + MB i + lr and
+    // n = n0 + wn0 + MB j + 4 NG q + 4 g, for q < NACC / 4 (registers 4q .. 4q+3).
     constexpr int OB = OutTraits<C::OUT_DT>::bytes;
     if constexpr (OB == 2 && BM * BN * 2 <= C::LDS_BYTES) {
         // 16-bit C: the tile goes through the (now idle) LDS ring so that the
@@ -775,12 +823,12 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         barrier_lds();
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int r = wm0 + 32 * i + l32;
+            const int r = wm0 + MB * i + lr;
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int c = wn0 + 32 * j + 8 * q + 4 * g;
+                for (int q = 0; q < NACC / 4; ++q) {
+                    const int c = wn0 + MB * j + 4 * NG * q + 4 * g;
                     unsigned short h[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -816,14 +864,14 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     // unaligned-access mode); a row's last partial group element-wise.
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int m = m0 + wm0 + 32 * i + l32;
+        const int m = m0 + wm0 + MB * i + lr;
         if (m >= M) continue;
         unsigned char* crow = args.C + (size_t)m * (size_t)N * OB;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn0 + 32 * j + 8 * q + 4 * g;
+            for (int q = 0; q < NACC / 4; ++q) {
+                const int n = n0 + wn0 + MB * j + 4 * NG * q + 4 * g;
                 if (n >= N) continue;
                 float v[4];
 #pragma unroll

@@ -1,8 +1,8 @@
 // Test-only probes of the gfx950 data movements the GEMM kernel relies on.
 // Each runs one wave (64 threads) on tiny in-bounds buffers and reports what
 // the hardware did, through the same helpers the kernel uses:
-//   * probe_mfma_32x32x16 — one MFMA with the operand / result lane layouts the
-//     kernel assumes; the host compares D with X·Y;
+//   * probe_mfma_32x32x16, probe_mfma_16x16x32 — one MFMA with the operand /
+//     result lane layouts the kernel assumes; the host compares D with X·Y;
 //   * probe_tr16 — one transpose read per lane at caller-chosen LDS offsets;
 //   * probe_dma16 — one 16-byte direct global->LDS copy per lane.
 // Built into its own library; the product library does not contain these.
@@ -81,6 +81,24 @@ __global__ void k_unaligned16(const uint16_t* src, const uint32_t* off, uint32_t
     *reinterpret_cast<u32x4_t*>(out + 512 + 8 * threadIdx.x) = v;
 }
 
+// X: 16 x 32 row-major, Y: 32 x 16 row-major (16-bit patterns), D: 16 x 16 fp32.
+// Lane l feeds X[l % 16][8 (l / 16) + e] and Y[8 (l / 16) + e][l % 16], e = 0..7,
+// and owns D[4 (l / 16) + r][l % 16] in result register r.
+template <int IN_DT>
+__global__ void k_mfma16(const uint16_t* X, const uint16_t* Y, float* D)
+{
+    const int l = threadIdx.x, r16 = l & 15, g = l >> 4;
+    i16x8_t a, b;
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (short)X[r16 * 32 + 8 * g + e];
+        b[e] = (short)Y[(8 * g + e) * 16 + r16];
+    }
+    f32x4_t acc;
+    for (int r = 0; r < 4; ++r) acc[r] = 0.0f;
+    acc = InTraits<IN_DT, 16>::mfma(a, b, acc);
+    for (int r = 0; r < 4; ++r) D[(4 * g + r) * 16 + r16] = acc[r];
+}
+
 int finish(hipError_t e)
 {
     if (e != hipSuccess) return -3;
@@ -95,6 +113,15 @@ extern "C" int probe_mfma_32x32x16(const void* X, const void* Y, void* D, int in
         k_mfma<DT_F16><<<1, 64>>>((const uint16_t*)X, (const uint16_t*)Y, (float*)D);
     else
         k_mfma<DT_BF16><<<1, 64>>>((const uint16_t*)X, (const uint16_t*)Y, (float*)D);
+    return finish(hipGetLastError());
+}
+
+extern "C" int probe_mfma_16x16x32(const void* X, const void* Y, void* D, int in_dtype)
+{
+    if (in_dtype == 0)
+        k_mfma16<DT_F16><<<1, 64>>>((const uint16_t*)X, (const uint16_t*)Y, (float*)D);
+    else
+        k_mfma16<DT_BF16><<<1, 64>>>((const uint16_t*)X, (const uint16_t*)Y, (float*)D);
     return finish(hipGetLastError());
 }
 

@@ -19,9 +19,11 @@ def probe():
     import torch
     assert torch.cuda.is_available()
     lib = ctypes.CDLL(gr.PROBE_LIB_PATH)
-    for name in ("probe_mfma_32x32x16", "probe_tr16", "probe_dma16", "probe_unaligned16"):
+    for name in ("probe_mfma_32x32x16", "probe_mfma_16x16x32", "probe_tr16", "probe_dma16",
+                 "probe_unaligned16"):
         getattr(lib, name).restype = ctypes.c_int
     lib.probe_mfma_32x32x16.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int]
+    lib.probe_mfma_16x16x32.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int]
     lib.probe_tr16.argtypes = [ctypes.c_void_p] * 3
     lib.probe_dma16.argtypes = [ctypes.c_void_p] * 3
     lib.probe_unaligned16.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_uint, ctypes.c_void_p]
@@ -43,6 +45,21 @@ def test_mfma_32x32x16_layout(probe, dtype):
     Y = _dev(wl.encode(y, dtype).view(np.int16))
     D = torch.zeros((32, 32), dtype=torch.float32, device="cuda")
     assert probe.probe_mfma_32x32x16(X.data_ptr(), Y.data_ptr(), D.data_ptr(), dtype) == 0
+    assert np.array_equal(D.cpu().numpy().astype(np.float64), x @ y)
+
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+def test_mfma_16x16x32_layout(probe, dtype):
+    """Lane l feeds row/column l % 16 with k group l / 16 (8 consecutive k) and
+    owns D[4 (l / 16) + r][l % 16] in result register r."""
+    import torch
+    rng = np.random.default_rng(8)
+    x = rng.integers(-3, 4, size=(16, 32)).astype(np.float64)
+    y = rng.integers(-3, 4, size=(32, 16)).astype(np.float64)
+    X = _dev(wl.encode(x, dtype).view(np.int16))
+    Y = _dev(wl.encode(y, dtype).view(np.int16))
+    D = torch.zeros((16, 16), dtype=torch.float32, device="cuda")
+    assert probe.probe_mfma_16x16x32(X.data_ptr(), Y.data_ptr(), D.data_ptr(), dtype) == 0
     assert np.array_equal(D.cpu().numpy().astype(np.float64), x @ y)
 
 
