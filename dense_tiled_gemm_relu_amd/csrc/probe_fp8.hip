@@ -95,3 +95,37 @@ extern "C" int probe_unaligned8(const void* src, const void* off, unsigned n, vo
     k_unaligned8<<<1, 64>>>((const uint8_t*)src, (const uint32_t*)off, n, (uint8_t*)out);
     return finish(hipGetLastError());
 }
+
+// ---- block-scaled (MX) form: v_mfma_scale_f32_32x32x64_f8f6f4 with per-lane
+// E8M0 scales.  a, b: 64 x 32 bytes; sa, sb: 64 scale words (byte 0 used);
+// d: 64 x 16 floats.  fmt 0: both E4M3; 4: both FP4 E2M1.
+namespace {
+template <int FMT>
+__global__ void k_mfma_mx_raw(const uint8_t* a, const uint8_t* b, const uint32_t* sa,
+                              const uint32_t* sb, float* d)
+{
+    const int l = threadIdx.x;
+    i32x8_t av, bv;
+    __builtin_memcpy(&av, a + 32 * l, 32);
+    __builtin_memcpy(&bv, b + 32 * l, 32);
+    f32x16_t acc;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, FMT, FMT, 0, (int)sa[l], 0,
+                                                          (int)sb[l]);
+    for (int r = 0; r < 16; ++r) d[16 * l + r] = acc[r];
+}
+}  // namespace
+
+extern "C" int probe_mfma_mx_raw(const void* a, const void* b, const void* sa, const void* sb,
+                                 void* d, int fmt)
+{
+    if (fmt == 0)
+        k_mfma_mx_raw<0><<<1, 64>>>((const uint8_t*)a, (const uint8_t*)b, (const uint32_t*)sa,
+                                    (const uint32_t*)sb, (float*)d);
+    else if (fmt == 4)
+        k_mfma_mx_raw<4><<<1, 64>>>((const uint8_t*)a, (const uint8_t*)b, (const uint32_t*)sa,
+                                    (const uint32_t*)sb, (float*)d);
+    else
+        return -1;
+    return finish(hipGetLastError());
+}

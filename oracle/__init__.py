@@ -24,6 +24,11 @@ bfloat16, or the OCP 8-bit formats E4M3 and E5M2 (the FP8 GEMM of that page's
 
 Inputs are storage patterns (numpy ``uint16`` arrays for the 16-bit types,
 ``uint8`` for the 8-bit ones); outputs are binary64 numpy arrays.
+
+Block-scaled (MX) products (the MXFP8 / MXFP4 of that page's §4.1 timeline)
+follow the OCP Microscaling definition: ``gemm_relu_mx_ref`` (C) and
+``gemm_relu_mx_fraction`` (exact rationals, its own E2M1 table) take A (M, K)
+and B stored (N, K) with E8M0 scales per 32 elements along K.
 """
 import ctypes
 import os
@@ -38,6 +43,10 @@ BF16 = 1
 F8E4M3 = 3
 F8E5M2 = 4
 FP8 = (F8E4M3, F8E5M2)
+MX_E4M3 = 5      # MXFP8, E4M3 elements
+MX_E5M2 = 6      # MXFP8, E5M2 elements
+MX_E2M1 = 7      # MXFP4, E2M1 elements packed two per byte (even k in the low nibble)
+MX = (MX_E4M3, MX_E5M2, MX_E2M1)
 
 _lib = None
 
@@ -61,6 +70,10 @@ def _load():
     lib.oracle_dec_e4m3.restype = ctypes.c_double
     lib.oracle_dec_e5m2.argtypes = [ctypes.c_uint8]
     lib.oracle_dec_e5m2.restype = ctypes.c_double
+    lib.oracle_dec_e2m1.argtypes = [ctypes.c_uint8]
+    lib.oracle_dec_e2m1.restype = ctypes.c_double
+    lib.oracle_dec_e8m0.argtypes = [ctypes.c_uint8]
+    lib.oracle_dec_e8m0.restype = ctypes.c_double
     vp = ctypes.c_void_p
     lib.oracle_decode.argtypes = [vp, f64p, i64, ctypes.c_int]
     lib.oracle_decode.restype = None
@@ -72,6 +85,9 @@ def _load():
                                             i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int]
     lib.oracle_gemm_relu_f64_at.restype = ctypes.c_int
+    lib.oracle_gemm_relu_mx.argtypes = [vp, vp, vp, vp, i64p, i64p, i64, f64p, f64p,
+                                        i64, i64, i64, ctypes.c_int, ctypes.c_int]
+    lib.oracle_gemm_relu_mx.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -203,3 +219,93 @@ def gemm_relu_ref_matmul(A, B, M, N, K, dtype, transB=0, relu=True):
     if not relu:
         return x
     return np.where(x > 0.0, x, 0.0)
+
+
+# ------------------------------------------------------ block-scaled (MX)
+def dec_e2m1(nibble):
+    return _load().oracle_dec_e2m1(int(nibble))
+
+
+def dec_e8m0(e):
+    return _load().oracle_dec_e8m0(int(e))
+
+
+def _mx_check(A, SA, B, SB, M, N, K, fmt):
+    if fmt not in MX:
+        raise ValueError("MX element format %d" % fmt)
+    if K % 32:
+        raise ValueError("K must be a multiple of 32 (whole scale blocks)")
+    row = K // 2 if fmt == MX_E2M1 else K
+    arrs = []
+    for x, n in ((A, M * row), (SA, M * (K // 32)), (B, N * row), (SB, N * (K // 32))):
+        x = np.ascontiguousarray(x).reshape(-1)
+        if x.dtype != np.uint8 or x.size != n:
+            raise ValueError("MX operands are uint8 arrays of the documented sizes")
+        arrs.append(x)
+    return arrs
+
+
+def gemm_relu_mx_ref(A, SA, B, SB, M, N, K, fmt, relu=True, rows=None, cols=None):
+    """Block-scaled max(A·Bᵀ, 0) in binary64: the full (M, N) product, or the
+    values and absum at positions (rows[t], cols[t]).  A: M x K elements, B
+    stored N x K, SA / SB: (M, K/32) / (N, K/32) E8M0 bytes."""
+    lib = _load()
+    A, SA, B, SB = _mx_check(A, SA, B, SB, M, N, K, fmt)
+    if rows is None:
+        out = np.empty((M, N), dtype=np.float64)
+        rc = lib.oracle_gemm_relu_mx(_vptr(A), _vptr(SA), _vptr(B), _vptr(SB), None, None, 0,
+                                     _ptr(out, ctypes.c_double), None, M, N, K, fmt,
+                                     1 if relu else 0)
+        if rc != 0:
+            raise ValueError("oracle_gemm_relu_mx failed (%d)" % rc)
+        return out
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    out = np.empty(rows.shape, dtype=np.float64)
+    absum = np.empty(rows.shape, dtype=np.float64)
+    rc = lib.oracle_gemm_relu_mx(_vptr(A), _vptr(SA), _vptr(B), _vptr(SB),
+                                 _ptr(rows, ctypes.c_int64), _ptr(cols, ctypes.c_int64), rows.size,
+                                 _ptr(out, ctypes.c_double), _ptr(absum, ctypes.c_double),
+                                 M, N, K, fmt, 1 if relu else 0)
+    if rc != 0:
+        raise ValueError("oracle_gemm_relu_mx failed (%d)" % rc)
+    return out, absum
+
+
+# E2M1 magnitudes as the OCP table lists them (codes 0..7), for the rational twin
+_E2M1_TABLE = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2),
+               Fraction(3), Fraction(4), Fraction(6)]
+
+
+def _mx_elems_exact(row_bytes, K, fmt):
+    if fmt == MX_E2M1:
+        out = []
+        for k in range(K):
+            nib = (int(row_bytes[k // 2]) >> (4 * (k % 2))) & 0xF
+            v = _E2M1_TABLE[nib & 7]
+            out.append(-v if nib & 8 else v)
+        return out
+    return _exact(np.ascontiguousarray(row_bytes[:K]), F8E4M3 if fmt == MX_E4M3 else F8E5M2)
+
+
+def gemm_relu_mx_fraction(A, SA, B, SB, M, N, K, fmt, relu=True):
+    """Exact rational block-scaled product (tiny shapes): its own E2M1 table,
+    torch's float8 types for E4M3 / E5M2, and 2^(e-127) as a Fraction."""
+    A, SA, B, SB = _mx_check(A, SA, B, SB, M, N, K, fmt)
+    rb = K // 2 if fmt == MX_E2M1 else K
+    nb = K // 32
+    a = [_mx_elems_exact(A[i * rb:(i + 1) * rb], K, fmt) for i in range(M)]
+    b = [_mx_elems_exact(B[j * rb:(j + 1) * rb], K, fmt) for j in range(N)]
+    out = []
+    for i in range(M):
+        row = []
+        for j in range(N):
+            s = Fraction(0)
+            for blk in range(nb):
+                xa = Fraction(2) ** (int(SA[i * nb + blk]) - 127)
+                xb = Fraction(2) ** (int(SB[j * nb + blk]) - 127)
+                for k in range(32 * blk, 32 * blk + 32):
+                    s += xa * a[i][k] * xb * b[j][k]
+            row.append(max(s, Fraction(0)) if relu else s)
+        out.append(row)
+    return out

@@ -27,6 +27,18 @@
  * give FP8 no scale factors, so an FP8 product here is the same definition
  * over the exact values of the 8-bit inputs.
  *
+ * Block-scaled (MX) inputs — the "MXFP8 block-scaled GEMM" and "CDNA4 MXFP4"
+ * of that page's §4.1 capability timeline — follow the OCP Microscaling
+ * definition: every 32 consecutive elements of a row along K share one E8M0
+ * scale X = 2^(e - 127), and an element's value is X times its own value.
+ * Here A is (M, K), B is stored (N, K), and their scales are (M, K/32) and
+ * (N, K/32) row-major byte arrays, so
+ *
+ *     ref[i][j] = max( sum_b XA[i][b] XB[j][b] sum_{k in block b} a(i,k) b(j,k), 0 )
+ *
+ * with 4-bit E2M1 elements packed two to a byte, element k of a row in the
+ * low nibble of byte k/2 when k is even and in the high nibble when odd.
+ *
  * Readings where the pages are silent (listed with the others in the design
  * notes): a negative sum maps to +0.0; K = 0 gives an empty sum, so every
  * output is +0.0; M = 0 or N = 0 is a no-op.
@@ -40,6 +52,8 @@
 #endif
 
 enum { ORACLE_F16 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 3, ORACLE_FP8_E5M2 = 4 };
+/* element formats of the block-scaled product */
+enum { ORACLE_MX_E4M3 = 5, ORACLE_MX_E5M2 = 6, ORACLE_MX_E2M1 = 7 };
 
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
 double oracle_dec_f16(uint16_t h)
@@ -109,6 +123,24 @@ double oracle_dec_e5m2(uint8_t h)
 }
 
 /* Exact value of element idx of a storage array of the given type. */
+/* OCP 4-bit E2M1: 1 sign bit, 2 exponent bits (bias 1), 1 fraction bit; all
+ * 16 patterns finite (largest 1.5 * 2^2 = 6). */
+double oracle_dec_e2m1(uint8_t h)
+{
+    int sign = (h >> 3) & 1;
+    int e = (h >> 1) & 0x3;
+    int f = h & 0x1;
+    double v = e == 0 ? ldexp((double)f, -1)            /* subnormal: f * 2^-1 * 2^0 */
+                      : ldexp((double)(2 + f), e - 2);  /* (1 + f/2) * 2^(e-1) */
+    return sign ? -v : v;
+}
+
+/* OCP E8M0 scale: 2^(e - 127); e = 255 is NaN. */
+double oracle_dec_e8m0(uint8_t e)
+{
+    return e == 255 ? NAN : ldexp(1.0, (int)e - 127);
+}
+
 static double dec_at(const void* x, int64_t idx, int dtype)
 {
     switch (dtype) {
@@ -231,6 +263,58 @@ int oracle_gemm_relu_f64_at(const void* A, const void* B,
             double p = dec_at(A, i * K + k, dtype) * dec_at(B, b_index(k, j, N, K, transB), dtype);
             s += p;
             sa += fabs(p);
+        }
+        out[t] = relu ? (s > 0.0 ? s : 0.0) : s;
+        if (absum) absum[t] = sa;
+    }
+    return 0;
+}
+
+/* Element k of a row of an MX operand (row stride in elements = K). */
+static double mx_elem(const uint8_t* row, int64_t k, int fmt)
+{
+    if (fmt == ORACLE_MX_E2M1) {
+        uint8_t byte = row[k / 2];
+        return oracle_dec_e2m1((k % 2) ? (byte >> 4) : (byte & 0xf));
+    }
+    return fmt == ORACLE_MX_E4M3 ? oracle_dec_e4m3(row[k]) : oracle_dec_e5m2(row[k]);
+}
+
+/*
+ * Block-scaled product at n positions (rows[t], cols[t]), or the full (M, N)
+ * product when rows == NULL (then n is ignored and out is M x N row-major).
+ * A: M x K elements, B: N x K elements (both rows along K), SA: M x K/32 and
+ * SB: N x K/32 E8M0 bytes.  K must be a multiple of 32.  absum (optional)
+ * receives sum_k |scaled a * scaled b|.  Returns 0 or -1 on bad arguments.
+ */
+int oracle_gemm_relu_mx(const void* A, const void* SA, const void* B, const void* SB,
+                        const int64_t* rows, const int64_t* cols, int64_t n,
+                        double* out, double* absum, int64_t M, int64_t N, int64_t K,
+                        int fmt, int relu)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return -1;
+    if (fmt != ORACLE_MX_E4M3 && fmt != ORACLE_MX_E5M2 && fmt != ORACLE_MX_E2M1) return -1;
+    if (!out || (K > 0 && M > 0 && (!A || !SA)) || (K > 0 && N > 0 && (!B || !SB))) return -1;
+    const int64_t row_bytes = fmt == ORACLE_MX_E2M1 ? K / 2 : K;
+    const int64_t nb = K / 32;
+    const int64_t total = rows ? n : M * N;
+    if (rows)
+        for (int64_t t = 0; t < n; ++t)
+            if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < total; ++t) {
+        const int64_t i = rows ? rows[t] : t / N, j = rows ? cols[t] : t % N;
+        const uint8_t* arow = (const uint8_t*)A + i * row_bytes;
+        const uint8_t* brow = (const uint8_t*)B + j * row_bytes;
+        double s = 0.0, sa = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            const double xa = oracle_dec_e8m0(((const uint8_t*)SA)[i * nb + b]);
+            const double xb = oracle_dec_e8m0(((const uint8_t*)SB)[j * nb + b]);
+            for (int64_t k = 32 * b; k < 32 * b + 32; ++k) {
+                const double p = (xa * mx_elem(arow, k, fmt)) * (xb * mx_elem(brow, k, fmt));
+                s += p;
+                sa += fabs(p);
+            }
         }
         out[t] = relu ? (s > 0.0 ? s : 0.0) : s;
         if (absum) absum[t] = sa;

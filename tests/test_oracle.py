@@ -363,3 +363,112 @@ def test_fp8_transB_and_matmul_form(dtype):
 def test_fp8_inputs_must_be_bytes():
     with pytest.raises(TypeError):
         oracle.gemm_relu_ref(np.zeros(4, np.uint16), np.zeros(4, np.uint16), 2, 2, 2, F8E4M3)
+
+
+# ------------------------------------------------ block-scaled (MX) inputs
+MX_E4M3, MX_E5M2, MX_E2M1 = oracle.MX_E4M3, oracle.MX_E5M2, oracle.MX_E2M1
+# the OCP E2M1 value table, codes 0..7 (sign in bit 3)
+E2M1_SPEC = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_decode_e2m1_against_the_spec_table():
+    for code in range(16):
+        v = E2M1_SPEC[code & 7]
+        got = oracle.dec_e2m1(code)
+        assert got == (-v if code & 8 else v)
+        assert np.signbit(got) == bool(code & 8)
+
+
+def test_decode_e8m0():
+    import math
+    for e in range(255):
+        assert oracle.dec_e8m0(e) == math.ldexp(1.0, e - 127)
+    assert math.isnan(oracle.dec_e8m0(255))
+
+
+def _random_mx(M, N, K, fmt, rng, scale_spread=6):
+    rb = K // 2 if fmt == MX_E2M1 else K
+    if fmt == MX_E2M1:
+        A = rng.integers(0, 256, size=(M, rb)).astype(np.uint8)
+        B = rng.integers(0, 256, size=(N, rb)).astype(np.uint8)
+    else:
+        vals = oracle.decode(np.arange(256, dtype=np.uint8), F8E4M3 if fmt == MX_E4M3 else F8E5M2)
+        with np.errstate(invalid="ignore"):
+            ok = np.flatnonzero((vals == 0) | ((np.abs(vals) >= 2.0 ** -6) & (np.abs(vals) <= 64)))
+        A = rng.choice(ok, size=(M, rb)).astype(np.uint8)
+        B = rng.choice(ok, size=(N, rb)).astype(np.uint8)
+    SA = rng.integers(127 - scale_spread, 128 + scale_spread, size=(M, K // 32)).astype(np.uint8)
+    SB = rng.integers(127 - scale_spread, 128 + scale_spread, size=(N, K // 32)).astype(np.uint8)
+    return A, SA, B, SB
+
+
+@pytest.mark.parametrize("fmt", [MX_E4M3, MX_E5M2, MX_E2M1])
+def test_mx_bruteforce_small_shapes(fmt):
+    """Exact rational brute force with per-block scales (its own E2M1 table,
+    torch's float8 types, Fraction powers of two)."""
+    rng = np.random.default_rng(31 + fmt)
+    for M, N, K in [(1, 1, 32), (2, 3, 64), (3, 2, 96), (4, 4, 32)]:
+        A, SA, B, SB = _random_mx(M, N, K, fmt, rng)
+        got = oracle.gemm_relu_mx_ref(A, SA, B, SB, M, N, K, fmt)
+        want = oracle.gemm_relu_mx_fraction(A, SA, B, SB, M, N, K, fmt)
+        assert [[Fraction(float(x)) for x in row] for row in got] == want
+
+
+@pytest.mark.parametrize("fmt,plain", [(MX_E4M3, F8E4M3), (MX_E5M2, F8E5M2)])
+def test_mx8_with_unit_scales_is_the_plain_fp8_product(fmt, plain):
+    rng = np.random.default_rng(41)
+    M, N, K = 7, 9, 96
+    A, _, B, _ = _random_mx(M, N, K, fmt, rng)
+    one_a = np.full((M, K // 32), 127, np.uint8)
+    one_b = np.full((N, K // 32), 127, np.uint8)
+    got = oracle.gemm_relu_mx_ref(A, one_a, B, one_b, M, N, K, fmt)
+    assert np.array_equal(got, oracle.gemm_relu_ref(A, B, M, N, K, plain, 1))
+
+
+def test_mxfp4_with_unit_scales_is_the_plain_product_of_its_values():
+    """E2M1 values are exact in binary16: the same product through the
+    16-bit definition, with the nibbles unpacked by hand (even k low)."""
+    rng = np.random.default_rng(43)
+    M, N, K = 5, 6, 64
+    A, _, B, _ = _random_mx(M, N, K, MX_E2M1, rng)
+
+    def unpack(x):
+        nib = np.stack([x & 0xF, x >> 4], axis=-1).reshape(x.shape[0], -1)
+        mag = np.array(E2M1_SPEC)[nib & 7]
+        return np.where(nib & 8, -mag, mag)
+
+    a16 = enc(unpack(A), F16)
+    b16 = enc(unpack(B), F16)
+    ones = (np.full((M, K // 32), 127, np.uint8), np.full((N, K // 32), 127, np.uint8))
+    got = oracle.gemm_relu_mx_ref(A, ones[0], B, ones[1], M, N, K, MX_E2M1)
+    assert np.array_equal(got, oracle.gemm_relu_ref(a16, b16, M, N, K, F16, 1))
+
+
+@pytest.mark.parametrize("fmt", [MX_E4M3, MX_E2M1])
+def test_mx_block_scale_pulls_out(fmt):
+    """Raising every scale of A's row i by d multiplies row i by 2^d; raising
+    the scale of one block only scales that block's partial sum."""
+    rng = np.random.default_rng(47)
+    M, N, K = 4, 5, 64
+    A, SA, B, SB = _random_mx(M, N, K, fmt, rng, scale_spread=3)
+    base = oracle.gemm_relu_mx_ref(A, SA, B, SB, M, N, K, fmt)
+    SA2 = SA.copy()
+    SA2[2, :] += 3
+    got = oracle.gemm_relu_mx_ref(A, SA2, B, SB, M, N, K, fmt)
+    assert np.array_equal(got[2], base[2] * 8.0)
+    assert np.array_equal(np.delete(got, 2, axis=0), np.delete(base, 2, axis=0))
+    # one block: the no-ReLU sums split into per-block parts
+    full = oracle.gemm_relu_mx_ref(A, SA, B, SB, M, N, K, fmt, relu=False)
+    SA3 = SA.copy()
+    SA3[:, 1] += 1
+    bumped = oracle.gemm_relu_mx_ref(A, SA3, B, SB, M, N, K, fmt, relu=False)
+    SA0 = SA.copy()
+    SA0[:, 1] = 0                                  # block 1 scaled to 2^-127: negligible
+    part0 = oracle.gemm_relu_mx_ref(A, SA0, B, SB, M, N, K, fmt, relu=False)
+    assert np.allclose(bumped, full + (full - part0), rtol=0, atol=1e-30)
+
+
+def test_mx_rejects_partial_blocks():
+    with pytest.raises(ValueError):
+        oracle.gemm_relu_mx_ref(np.zeros(40, np.uint8), np.zeros(2, np.uint8),
+                                np.zeros(40, np.uint8), np.zeros(2, np.uint8), 1, 1, 40, MX_E4M3)

@@ -13,7 +13,12 @@ Recipe (the pages fix the shapes and dtypes but no generator):
 * 8-bit inputs (OCP E4M3 / E5M2): the same binary64 draws rounded to nearest
   even by torch's CPU float8 conversion (uniform[-1, 1] never reaches either
   format's overflow);
-* integer variants draw from {lo..hi} and are exact in every input format.
+* integer variants draw from {lo..hi} and are exact in every input format;
+* block-scaled (MX) inputs: the same binary64 draws, quantised per 32 elements
+  along K as the OCP Microscaling recipe does (shared scale 2^(floor(log2
+  max|x|) - emax of the element format), elements rounded to nearest even
+  with saturation); E2M1 elements are packed two per byte, even k in the low
+  nibble.
 """
 import numpy as np
 
@@ -23,7 +28,12 @@ F32 = 2
 F8E4M3 = 3
 F8E5M2 = 4
 FP8 = (F8E4M3, F8E5M2)
-DTYPE_NAMES = {F16: "f16", BF16: "bf16", F32: "f32", F8E4M3: "f8e4m3", F8E5M2: "f8e5m2"}
+MX_E4M3 = 5
+MX_E5M2 = 6
+MX_E2M1 = 7
+MX = (MX_E4M3, MX_E5M2, MX_E2M1)
+DTYPE_NAMES = {F16: "f16", BF16: "bf16", F32: "f32", F8E4M3: "f8e4m3", F8E5M2: "f8e5m2",
+               MX_E4M3: "mxfp8e4m3", MX_E5M2: "mxfp8e5m2", MX_E2M1: "mxfp4"}
 
 
 def elem_bytes(dtype):
@@ -116,3 +126,69 @@ def workload_inputs(name, int_values=False):
     w = WORKLOADS[name]
     return make_inputs(w["M"], w["N"], w["K"], w["in_dtype"], w["transB"], w["dist"],
                        w["index"], int_values)
+
+
+# ----------------------------------------------- block-scaled (MX) inputs
+_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_MX_EMAX = {MX_E4M3: 8, MX_E5M2: 15, MX_E2M1: 2}
+
+
+def e2m1_codes(values):
+    """binary64 values -> E2M1 nibbles, nearest (ties to the even code), saturating at 6."""
+    v = np.asarray(values, dtype=np.float64)
+    mag = np.minimum(np.abs(v), 6.0)
+    d = np.abs(mag[..., None] - _E2M1_MAG)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    # among equally near codes take the even one (fraction bit 0)
+    even = cand & (np.arange(8) % 2 == 0)
+    code = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    return (code | np.where(np.signbit(v) & (code != 0), 8, 0)).astype(np.uint8)
+
+
+def pack_e2m1(codes):
+    """(rows, K) nibbles -> (rows, K/2) bytes, even k in the low nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def mx_quantize(values, fmt):
+    """(rows, K) binary64 values, K % 32 == 0 -> (elements, scales) as uint8
+    arrays: elements (rows, K) (E4M3 / E5M2) or (rows, K/2) (packed E2M1),
+    scales (rows, K/32) E8M0."""
+    v = np.asarray(values, dtype=np.float64)
+    rows, K = v.shape
+    blocks = v.reshape(rows, K // 32, 32)
+    amax = np.abs(blocks).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))), 0.0)
+    shared = np.clip(e - _MX_EMAX[fmt], -127, 127).astype(np.int64)
+    scales = (shared + 127).astype(np.uint8)
+    x = blocks / np.ldexp(1.0, shared)[..., None]
+    if fmt == MX_E2M1:
+        elems = pack_e2m1(e2m1_codes(x).reshape(rows, K))
+    else:
+        import torch
+        tfmt = torch.float8_e4m3fn if fmt == MX_E4M3 else torch.float8_e5m2
+        lim = 448.0 if fmt == MX_E4M3 else 57344.0
+        t = torch.from_numpy(np.clip(x, -lim, lim).reshape(rows, K)).to(tfmt)
+        elems = t.view(torch.uint8).numpy().copy()
+    return elems, scales
+
+
+def mx_inputs(M, N, K, fmt, index, dist="uniform", int_values=False):
+    """(A, SA, B, SB) for a block-scaled product: A (M, K), B stored (N, K)."""
+    sa, sb = seeds(index)
+    ra, rb = np.random.default_rng(sa), np.random.default_rng(sb)
+    if int_values:
+        # small integers with unit scales (E8M0 127): exact in every element format
+        a = ra.integers(-2, 3, size=(M, K)).astype(np.float64)
+        b = rb.integers(-2, 3, size=(N, K)).astype(np.float64)
+        qa = (pack_e2m1(e2m1_codes(a)) if fmt == MX_E2M1 else encode(a, F8E4M3 if fmt == MX_E4M3 else F8E5M2))
+        qb = (pack_e2m1(e2m1_codes(b)) if fmt == MX_E2M1 else encode(b, F8E4M3 if fmt == MX_E4M3 else F8E5M2))
+        return (qa, np.full((M, K // 32), 127, np.uint8), qb, np.full((N, K // 32), 127, np.uint8))
+    a = ra.uniform(-1.0, 1.0, size=(M, K))
+    b = rb.uniform(-1.0, 1.0, size=(N, K))
+    qa, xa = mx_quantize(a, fmt)
+    qb, xb = mx_quantize(b, fmt)
+    return qa, xa, qb, xb
