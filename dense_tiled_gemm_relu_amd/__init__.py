@@ -17,6 +17,9 @@ BF16 = 1
 F32 = 2
 F8E4M3 = 3     # OCP 8-bit E4M3 (inputs only)
 F8E5M2 = 4     # OCP 8-bit E5M2 (inputs only)
+MX_E4M3 = 5    # block-scaled (gemm_relu_mx): MXFP8, E4M3 elements
+MX_E5M2 = 6    # MXFP8, E5M2 elements
+MX_E2M1 = 7    # MXFP4, E2M1 elements packed two per byte
 
 OK = 0
 EINVAL = -1
@@ -27,7 +30,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgemm_relu.so")
 PROBE_LIB_PATH = os.path.join(_PKG, "libgemm_relu_probe.so")
 
-EXPORTS = ("gemm_relu", "gemm_relu_strerror", "gemm_relu_plan")
+EXPORTS = ("gemm_relu", "gemm_relu_strerror", "gemm_relu_plan", "gemm_relu_mx",
+           "gemm_relu_mx_plan")
 
 _lib = None
 
@@ -56,6 +60,11 @@ def library():
     lib.gemm_relu_plan.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int]
     lib.gemm_relu_plan.restype = ctypes.c_char_p
+    lib.gemm_relu_mx.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp]
+    lib.gemm_relu_mx.restype = ctypes.c_int
+    lib.gemm_relu_mx_plan.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int,
+                                      ctypes.c_int]
+    lib.gemm_relu_mx_plan.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -104,6 +113,26 @@ def gemm_relu_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB):
     """Configuration name gemm_relu would launch (None if the call is invalid)."""
     r = library().gemm_relu_plan(_addr(A), _addr(B), _addr(C), int(M), int(N), int(K),
                                  int(in_dtype), int(out_dtype), int(transB))
+    return None if r is None else r.decode()
+
+
+def gemm_relu_mx_status(A, SA, B, SB, C, M, N, K, fmt, out_dtype, stream=None):
+    """Call the block-scaled C-ABI entry and return its status code."""
+    return library().gemm_relu_mx(_addr(A), _addr(SA), _addr(B), _addr(SB), _addr(C), int(M),
+                                  int(N), int(K), int(fmt), int(out_dtype), _stream_handle(stream))
+
+
+def gemm_relu_mx(A, SA, B, SB, C, M, N, K, fmt, out_dtype, stream=None):
+    """Block-scaled C = max(sum_b XA XB (A·Bᵀ)_b, 0) through the C-ABI (B stored
+    (N, K), E8M0 scales per 32 elements along K); raises GemmReluError."""
+    rc = gemm_relu_mx_status(A, SA, B, SB, C, M, N, K, fmt, out_dtype, stream)
+    if rc != OK:
+        raise GemmReluError(rc, gemm_relu_strerror(rc))
+
+
+def gemm_relu_mx_plan(A, SA, B, SB, C, M, N, K, fmt, out_dtype):
+    r = library().gemm_relu_mx_plan(_addr(A), _addr(SA), _addr(B), _addr(SB), _addr(C), int(M),
+                                    int(N), int(K), int(fmt), int(out_dtype))
     return None if r is None else r.decode()
 
 

@@ -25,7 +25,8 @@ PROBE_LIB = os.path.join(PKG, "libgemm_relu_probe.so")
 
 LIB_SOURCES = ["gemm_relu_api.hip", "inst_f16_nn.hip", "inst_f16_nt.hip",
                "inst_bf16_nn.hip", "inst_bf16_nt.hip", "inst_f8e4m3_nn.hip",
-               "inst_f8e4m3_nt.hip", "inst_f8e5m2_nn.hip", "inst_f8e5m2_nt.hip"]
+               "inst_f8e4m3_nt.hip", "inst_f8e5m2_nn.hip", "inst_f8e5m2_nt.hip",
+               "inst_mx_e4m3.hip", "inst_mx_e5m2.hip", "inst_mx_e2m1.hip"]
 PROBE_SOURCES = ["probe_layouts.hip", "probe_mfma_rate.hip", "probe_fp8.hip"]
 HEADERS = ["gemm_relu_kernel.hpp", "configs.hpp"]
 

@@ -22,6 +22,7 @@ enum ConfigId : int {
     CFG_D256x256x32_S5_W8I,
     CFG_D256x256x64_S2_W8,
     CFG_D128x128x64_S3,
+    CFG_D128x128x64_S2,
     CFG_D64x64x64_S4,
     CFG_D64x32x128_S4,
     CFG_G128x128x64,
@@ -47,6 +48,7 @@ inline const ConfigInfo& config_info(int id)
         {"d256x256x32_s5_w8i", 256, 256, true},
         {"d256x256x64_s2_w8", 256, 256, true},
         {"d128x128x64_s3", 128, 128, true},
+        {"d128x128x64_s2", 128, 128, true},
         {"d64x64x64_s4", 64, 64, true},
         {"d64x32x128_s4", 64, 32, true},
         {"g128x128x64", 128, 128, false},
@@ -56,8 +58,12 @@ inline const ConfigInfo& config_info(int id)
 }
 
 // K elements per step of a configuration whose 16-bit step is BK16 elements.
+// Block-scaled inputs count K in storage bytes (an E2M1 byte holds 2 elements).
 template <int IN, int BK16>
-inline constexpr int bk_of = (IN == DT_F8E4M3 || IN == DT_F8E5M2) ? 2 * BK16 : BK16;
+inline constexpr int bk_of = (IN == DT_F8E4M3 || IN == DT_F8E5M2 || IN == DT_MX_E4M3 ||
+                              IN == DT_MX_E5M2 || IN == DT_MX_E2M1)
+                                 ? 2 * BK16
+                                 : BK16;
 
 template <int IN, int OUT, bool TB, int id> struct CfgOf;
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x64_S2> {
@@ -91,6 +97,10 @@ template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x64_S2
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D128x128x64_S3> {
     using type = Cfg<IN, OUT, TB, 128, 128, bk_of<IN, 64>, 2, 2, 3, true>;
+};
+// Two-stage 128x128: the smaller tile of the block-scaled inputs.
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D128x128x64_S2> {
+    using type = Cfg<IN, OUT, TB, 128, 128, bk_of<IN, 64>, 2, 2, 2, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D64x64x64_S4> {
     using type = Cfg<IN, OUT, TB, 64, 64, bk_of<IN, 64>, 2, 2, 4, true>;
@@ -126,6 +136,9 @@ LaunchFn launcher_f8e4m3_nn(int out_dt, int cfg);
 LaunchFn launcher_f8e4m3_nt(int out_dt, int cfg);
 LaunchFn launcher_f8e5m2_nn(int out_dt, int cfg);
 LaunchFn launcher_f8e5m2_nt(int out_dt, int cfg);
+LaunchFn launcher_mx_e4m3(int out_dt, int cfg);
+LaunchFn launcher_mx_e5m2(int out_dt, int cfg);
+LaunchFn launcher_mx_e2m1(int out_dt, int cfg);
 
 // Configurations built for 8-bit inputs: the ones plan selection can choose
 // (the 16-bit comparison variants are not instantiated for them).
@@ -163,6 +176,8 @@ inline bool fp8_config(int cfg)
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_W8>::type>;  \
         case CFG_D128x128x64_S3:                                                           \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D128x128x64_S3>::type>;     \
+        case CFG_D128x128x64_S2:                                                           \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D128x128x64_S2>::type>;     \
         case CFG_D64x64x64_S4:                                                             \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x64x64_S4>::type>;       \
         case CFG_D64x32x128_S4:                                                            \
@@ -197,6 +212,8 @@ inline bool fp8_config(int cfg)
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I>::type>;   \
         case CFG_D128x128x64_S3:                                                           \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D128x128x64_S3>::type>;     \
+        case CFG_D128x128x64_S2:                                                           \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D128x128x64_S2>::type>;     \
         case CFG_D64x64x64_S4:                                                             \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x64x64_S4>::type>;       \
         case CFG_D64x32x128_S4:                                                            \
@@ -205,6 +222,33 @@ inline bool fp8_config(int cfg)
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_G128x128x64>::type>;        \
         case CFG_G64x64x64:                                                                \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_G64x64x64>::type>;          \
+        default:                                                                           \
+            return nullptr;                                                                \
+        }                                                                                  \
+    }                                                                                      \
+    LaunchFn FN(int out_dt, int cfg)                                                       \
+    {                                                                                      \
+        switch (out_dt) {                                                                  \
+        case DT_F16: return FN##_out<DT_F16>(cfg);                                         \
+        case DT_BF16: return FN##_out<DT_BF16>(cfg);                                       \
+        case DT_F32: return FN##_out<DT_F32>(cfg);                                         \
+        default: return nullptr;                                                           \
+        }                                                                                  \
+    }                                                                                      \
+    }
+
+// Body of a block-scaled instantiation unit: B stored (N,K), the two-stage
+// direct configurations.
+#define GEMM_RELU_DEFINE_LAUNCHER_MX(FN, IN)                                               \
+    namespace gemm_relu_hip {                                                              \
+    template <int OUT>                                                                     \
+    static LaunchFn FN##_out(int cfg)                                                      \
+    {                                                                                      \
+        switch (cfg) {                                                                     \
+        case CFG_D256x256x64_S2:                                                           \
+            return &launch_one<typename CfgOf<IN, OUT, true, CFG_D256x256x64_S2>::type>;   \
+        case CFG_D128x128x64_S2:                                                           \
+            return &launch_one<typename CfgOf<IN, OUT, true, CFG_D128x128x64_S2>::type>;   \
         default:                                                                           \
             return nullptr;                                                                \
         }                                                                                  \

@@ -3,6 +3,8 @@
 // Semantics (page "TileLang：GPU/NPU 通用算子 DSL", §3.2 and §3.3): C is
 // overwritten with max(A·op(B), 0); the grid has one workgroup per output tile
 // and a ceil-divided K loop, so every shape is covered, tails included.
+// gemm_relu_mx: the block-scaled (OCP MX) form of the same product (§4.1's
+// MXFP8 / MXFP4).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -180,6 +182,83 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     return p;
 }
 
+// ---- block-scaled (MX) inputs
+bool mx_format(int f) { return f == GEMM_RELU_MX_E4M3 || f == GEMM_RELU_MX_E5M2 || f == GEMM_RELU_MX_E2M1; }
+
+Plan make_plan_mx(const void* A, const void* SA, const void* B, const void* SB, const void* C,
+                  int64_t M, int64_t N, int64_t K, int fmt, int out_dt, const Env& e)
+{
+    Plan p;
+    const int64_t lim = INT32_MAX;
+    if (M < 0 || N < 0 || K < 0 || M > lim || N > lim || K > lim || K % 32 != 0 ||
+        !mx_format(fmt) ||
+        (out_dt != GEMM_RELU_F16 && out_dt != GEMM_RELU_BF16 && out_dt != GEMM_RELU_F32)) {
+        p.status = GEMM_RELU_EINVAL;
+        return p;
+    }
+    if (M == 0 || N == 0) {
+        p.empty = true;
+        return p;
+    }
+    const int64_t ks = fmt == GEMM_RELU_MX_E2M1 ? K / 2 : K;     // storage bytes per row
+    const uint64_t a_bytes = uint64_t(M) * uint64_t(ks), b_bytes = uint64_t(N) * uint64_t(ks);
+    const uint64_t sa_bytes = uint64_t(M) * uint64_t(K / 32), sb_bytes = uint64_t(N) * uint64_t(K / 32);
+    const uint64_t c_bytes = uint64_t(M) * uint64_t(N) * uint64_t(elem_bytes(out_dt));
+    if ((a_bytes && (!A || !SA)) || (b_bytes && (!B || !SB)) || !C ||
+        (reinterpret_cast<uintptr_t>(C) & uintptr_t(elem_bytes(out_dt) - 1))) {
+        p.status = GEMM_RELU_EINVAL;
+        return p;
+    }
+    const uintptr_t uc = reinterpret_cast<uintptr_t>(C);
+    if (overlaps(uc, c_bytes, reinterpret_cast<uintptr_t>(A), a_bytes) ||
+        overlaps(uc, c_bytes, reinterpret_cast<uintptr_t>(B), b_bytes) ||
+        overlaps(uc, c_bytes, reinterpret_cast<uintptr_t>(SA), sa_bytes) ||
+        overlaps(uc, c_bytes, reinterpret_cast<uintptr_t>(SB), sb_bytes)) {
+        p.status = GEMM_RELU_EINVAL;
+        return p;
+    }
+    auto tiles = [&](int id) { return ceil_div(M, config_info(id).bm) * ceil_div(N, config_info(id).bn); };
+    auto usable = [&](int id) {
+        return (id == CFG_D256x256x64_S2 || id == CFG_D128x128x64_S2) && direct_fits(id, N, ks, 1);
+    };
+    // rounds of workgroups over the CUs, each the tile's area over its
+    // efficiency relative to the 256x256 tile (128x128: ~0.57)
+    auto cost = [&](int id) {
+        const ConfigInfo& ci = config_info(id);
+        return double(ceil_div(tiles(id), kNumCUs)) * ci.bm * ci.bn / (ci.bm >= 256 ? 1.0 : 0.57);
+    };
+    int cfg = -1;
+    if (e.force_cfg >= 0 && usable(e.force_cfg)) {
+        cfg = e.force_cfg;
+    } else {
+        for (int id : {CFG_D256x256x64_S2, CFG_D128x128x64_S2})
+            if (usable(id) && (cfg < 0 || cost(id) < cost(cfg))) cfg = id;
+    }
+    if (cfg < 0) {
+        p.status = GEMM_RELU_EUNSUPPORTED;     // K beyond the 32-bit copy offsets
+        return p;
+    }
+    const int64_t tm = ceil_div(M, config_info(cfg).bm), tn = ceil_div(N, config_info(cfg).bn);
+    if (tm * tn > lim) {
+        p.status = GEMM_RELU_EUNSUPPORTED;
+        return p;
+    }
+    p.cfg = cfg;
+    p.tiles_m = int(tm);
+    p.tiles_n = int(tn);
+    return p;
+}
+
+LaunchFn pick_launcher_mx(int fmt, int out_dt, int cfg)
+{
+    switch (fmt) {
+    case GEMM_RELU_MX_E4M3: return launcher_mx_e4m3(out_dt, cfg);
+    case GEMM_RELU_MX_E5M2: return launcher_mx_e5m2(out_dt, cfg);
+    case GEMM_RELU_MX_E2M1: return launcher_mx_e2m1(out_dt, cfg);
+    default: return nullptr;
+    }
+}
+
 LaunchFn pick_launcher(int in_dt, int out_dt, int transB, int cfg)
 {
     switch (in_dt) {
@@ -217,6 +296,9 @@ extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64
     const int panel = e.panel > 0 ? e.panel : 8;
     args.panel = panel < p.tiles_m ? panel : p.tiles_m;
     args.nxcd = e.nxcd;
+    args.SA = nullptr;
+    args.SB = nullptr;
+    args.KB = 0;
 
     LaunchFn fn = pick_launcher(in_dtype, out_dtype, transB, p.cfg);
     if (!fn) return GEMM_RELU_EUNSUPPORTED;
@@ -245,6 +327,54 @@ extern "C" const char* gemm_relu_plan(const void* A, const void* B, const void* 
                                       int transB)
 {
     const Plan p = make_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB, env());
+    if (p.status == GEMM_RELU_EINVAL) return nullptr;
+    if (p.status != GEMM_RELU_OK) return "unsupported";
+    if (p.empty) return "none";
+    return config_info(p.cfg).name;
+}
+
+extern "C" int gemm_relu_mx(const void* A, const void* SA, const void* B, const void* SB, void* C,
+                            int64_t M, int64_t N, int64_t K, int fmt, int out_dtype, void* stream)
+{
+    const Env e = env();
+    const Plan p = make_plan_mx(A, SA, B, SB, C, M, N, K, fmt, out_dtype, e);
+    if (p.status != GEMM_RELU_OK) return p.status;
+    if (p.empty) return GEMM_RELU_OK;
+    const int dev = check_device();
+    if (dev != GEMM_RELU_OK) return dev;
+
+    KernelArgs args;
+    args.A = static_cast<const unsigned char*>(A);
+    args.B = static_cast<const unsigned char*>(B);
+    args.C = static_cast<unsigned char*>(C);
+    args.M = int(M);
+    args.N = int(N);
+    args.K = int(fmt == GEMM_RELU_MX_E2M1 ? K / 2 : K);     // storage bytes per row
+    args.tiles_m = p.tiles_m;
+    args.tiles_n = p.tiles_n;
+    const int panel = e.panel > 0 ? e.panel : 8;
+    args.panel = panel < p.tiles_m ? panel : p.tiles_m;
+    args.nxcd = e.nxcd;
+    args.SA = static_cast<const unsigned char*>(SA);
+    args.SB = static_cast<const unsigned char*>(SB);
+    args.KB = int(K / 32);
+
+    LaunchFn fn = pick_launcher_mx(fmt, out_dtype, p.cfg);
+    if (!fn) return GEMM_RELU_EUNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (fn(args, p.tiles_m * p.tiles_n, st) != hipSuccess) return GEMM_RELU_EHIP;
+    if (e.sync) {
+        if (hipStreamSynchronize(st) != hipSuccess) return GEMM_RELU_EHIP;
+        if (hipGetLastError() != hipSuccess) return GEMM_RELU_EHIP;
+    }
+    return GEMM_RELU_OK;
+}
+
+extern "C" const char* gemm_relu_mx_plan(const void* A, const void* SA, const void* B,
+                                         const void* SB, const void* C, int64_t M, int64_t N,
+                                         int64_t K, int fmt, int out_dtype)
+{
+    const Plan p = make_plan_mx(A, SA, B, SB, C, M, N, K, fmt, out_dtype, env());
     if (p.status == GEMM_RELU_EINVAL) return nullptr;
     if (p.status != GEMM_RELU_OK) return "unsupported";
     if (p.empty) return "none";

@@ -42,6 +42,10 @@
 namespace gemm_relu_hip {
 
 enum : int { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2, DT_F8E4M3 = 3, DT_F8E5M2 = 4 };
+// Block-scaled (MX) element formats: E4M3 / E5M2 bytes, or E2M1 nibbles packed
+// two per byte (even k in the low nibble).  Their K geometry is in storage
+// bytes: an E2M1 row of K elements is K / 2 bytes.
+enum : int { DT_MX_E4M3 = 5, DT_MX_E5M2 = 6, DT_MX_E2M1 = 7 };
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -63,6 +67,9 @@ struct KernelArgs {
     int M, N, K;
     int tiles_m, tiles_n;
     int panel;                // tile rows per rasterisation panel (>= 1)
+    const unsigned char* SA;  // block-scaled inputs: (M, KB) E8M0 scales of A, else unused
+    const unsigned char* SB;  // (N, KB) E8M0 scales of B (stored (N, K))
+    int KB;                   // scale blocks per row (K elements / 32)
     int nxcd;                 // XCDs the dispatcher round-robins over (1 = no remap)
 };
 
@@ -129,6 +136,8 @@ template <int IN_DT, int MB = 32> struct InTraits {
     static_assert(MB == 32 || MB == 16, "MFMA block");
     static constexpr int EB = 2, KMF = MB == 32 ? 16 : 32, OPB = 16, TRK = 4;
     static constexpr int NACC = MB * MB / 64;
+    static constexpr bool MX = false;
+    static constexpr int EPB = 1;                // elements per storage byte (unused: 2-byte elements)
     using Op = i16x8_t;
     using Acc = std::conditional_t<MB == 32, f32x16_t, f32x4_t>;
     __device__ static Acc mfma(Op a, Op b, Acc c)
@@ -166,6 +175,8 @@ template <int IN_DT, int MB = 32> struct InTraits {
 };
 template <int FMT> struct InTraitsF8 {
     static constexpr int EB = 1, KMF = 64, OPB = 32, TRK = 8, NACC = 16;
+    static constexpr bool MX = false;
+    static constexpr int EPB = 1;
     using Op = i32x8_t;
     using Acc = f32x16_t;
     // format codes of the f8f6f4 MFMA: 0 = E4M3, 1 = E5M2; no block scales
@@ -188,6 +199,42 @@ template <int FMT> struct InTraitsF8 {
     }
     typedef int i32x4_raw __attribute__((ext_vector_type(4)));
 };
+// Block-scaled (MX) inputs on v_mfma_scale_f32_32x32x64_f8f6f4.  Each lane
+// supplies, with its operand, the E8M0 scale of the 32-element block it holds
+// (lane 32 g + i: block g of row / column i of the MFMA's 64-k step).  The
+// geometry is in storage bytes (EPB elements per byte): a k step is KMF bytes
+// of a row.  E4M3 / E5M2: the 32 bytes of lane group g are k chunks g and
+// 2 + g (halves of both blocks, which is how the scaled MFMA pairs bytes with
+// blocks); E2M1: the 16 bytes of lane group g are chunk g (its block).
+template <int FMT> struct InTraitsMX {
+    static constexpr bool MX = true;
+    static constexpr int EB = 1, EPB = FMT == 4 ? 2 : 1;
+    static constexpr int KMF = 64 / EPB, OPB = 32 / EPB, TRK = 8, NACC = 16;
+    using Op = i32x8_t;
+    using Acc = f32x16_t;
+    __device__ static Acc mfma_scaled(Op a, Op b, Acc c, int scale_a, int scale_b)
+    {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, scale_a, 0,
+                                                               scale_b);
+    }
+    // 16-byte chunk of lane group g, part x, k step s, within a row
+    __device__ static constexpr int chunk(int s, int g, int x)
+    {
+        return EPB == 2 ? 2 * s + g : 4 * s + 2 * x + g;
+    }
+    template <int X> __device__ static void set_chunk(Op& v, u32x4_t c)
+    {
+        if constexpr (X == 0)
+            v.lo = __builtin_bit_cast(i32x4_raw, c);
+        else
+            v.hi = __builtin_bit_cast(i32x4_raw, c);
+    }
+    __device__ static void set_tr(Op&, int, const GR_LDS unsigned char*) {}
+    typedef int i32x4_raw __attribute__((ext_vector_type(4)));
+};
+template <int MB> struct InTraits<DT_MX_E4M3, MB> : InTraitsMX<0> {};
+template <int MB> struct InTraits<DT_MX_E5M2, MB> : InTraitsMX<1> {};
+template <int MB> struct InTraits<DT_MX_E2M1, MB> : InTraitsMX<4> {};
 template <int MB> struct InTraits<DT_F8E4M3, MB> : InTraitsF8<0> {
     static_assert(MB == 32, "8-bit inputs use the 32x32 block");
 };
@@ -255,6 +302,9 @@ struct Cfg {
     static_assert(BK * EB == 64 || BK * EB == 128 || BK * EB == 256, "k-contiguous rows of 64, 128 or 256 bytes");
     static_assert(KSUB >= 1 && BK % In::KMF == 0, "whole MFMA k-steps per BK step");
     static_assert(KSUB % 2 == 0 || INTERLEAVE_, "an odd k-step count needs the step-parity tags of the interleaved loop");
+    static constexpr bool MX = In::MX;
+    static_assert(!MX || (TRANS_B && DIRECT && !INTERLEAVE_ && STAGES_ == 2 && MB_ == 32),
+                  "block-scaled inputs: B stored (N,K), two-stage direct pipeline");
     static_assert(A_CH % NTHREADS == 0 && B_CH % NTHREADS == 0, "loader tiling");
     static_assert(TRANS_B || NROW_CH >= (EB == 2 ? 4 : 2), "n-contiguous B rows of at least 64 (16-bit) or 32 (8-bit) bytes");
         static_assert(STAGES >= 2 && STAGES <= 5, "stages");
@@ -523,15 +573,21 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     constexpr int MB = C::MB, NG = C::NG;
     const int lr = lane % MB, g = lane / MB;     // row (column) of the block, k group
     // k-contiguous rows: for k-step s the lane reads row (w0 + MB i + lr),
-    // chunks (NG s + g) FRAG_CH + x, x < FRAG_CH (its KMF / NG consecutive k).
+    // chunks (NG s + g) FRAG_CH + x, x < FRAG_CH (its KMF / NG consecutive k;
+    // block-scaled inputs place their chunks by the scaled MFMA's blocks).
+    auto chunk_of = [&](int s, int x) {
+        if constexpr (C::MX)
+            return In::chunk(s, g, x);
+        else
+            return (NG * s + g) * FRAG_CH + x;
+    };
     uint32_t a_rd[KSUB][FRAG_CH];
 #pragma unroll
     for (int s = 0; s < KSUB; ++s)
 #pragma unroll
         for (int x = 0; x < FRAG_CH; ++x) {
             const int r = wm0 + lr;
-            a_rd[s][x] = (uint32_t)(r * BK * EB +
-                                    ((((NG * s + g) * FRAG_CH + x) ^ swz_krow<ROW_CH>(r)) * 16));
+            a_rd[s][x] = (uint32_t)(r * BK * EB + ((chunk_of(s, x) ^ swz_krow<ROW_CH>(r)) * 16));
         }
     // (K,N) B offsets per block j and transpose read t (per t only where the
     // swizzle does not repeat every TRK rows: 16x16 blocks)
@@ -543,8 +599,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
 #pragma unroll
             for (int x = 0; x < FRAG_CH; ++x) {
                 const int r = wn0 + lr;
-                b_rd[s][x] = (uint32_t)(r * BK * EB +
-                                        ((((NG * s + g) * FRAG_CH + x) ^ swz_krow<ROW_CH>(r)) * 16));
+                b_rd[s][x] = (uint32_t)(r * BK * EB + ((chunk_of(s, x) ^ swz_krow<ROW_CH>(r)) * 16));
             }
     } else {
         // Transpose reads: 16-lane group h holds k group gk and n-half nh of an
@@ -617,11 +672,76 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     // Operands swapped (B block as the MFMA's first source) so that each lane
     // ends up owning 4 consecutive n of one output row.
     auto mma = [&](const Frags& f) {
+        if constexpr (!C::MX) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = In::mfma(f.b[j], f.a[i], acc[i][j]);
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = In::mfma(f.b[j], f.a[i], acc[i][j]);
+        }
+    };
+
+    // ---- block scales (block-scaled inputs only).  For one BK step the lane
+    // keeps the E8M0 scales of its TM rows of A and TN rows of B: BPS blocks
+    // per row, WPS words of 4.  k-step s uses block 2 s + g of the step.
+    constexpr int BPS = C::MX ? BK * In::EPB / 32 : 1;
+    constexpr int WPS = (BPS + 3) / 4;
+    constexpr int NSR = C::MX ? TM + TN : 1;
+    uint32_t sc_cur[NSR][WPS], sc_nxt[NSR][WPS];
+    int sc_row[NSR];
+    if constexpr (C::MX) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sc_row[i] = min(m0 + wm0 + MB * i + lr, M - 1);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) sc_row[TM + j] = min(n0 + wn0 + MB * j + lr, N - 1);
+    }
+    auto scale_base = [&](int q, int t) {
+        return (q < TM ? args.SA : args.SB) + (size_t)sc_row[q] * (size_t)args.KB + (size_t)t * BPS;
+    };
+    // scales of full step t (its blocks lie inside every row)
+    auto load_scales = [&](int t, uint32_t (&dst)[NSR][WPS]) {
+#pragma unroll
+        for (int q = 0; q < NSR; ++q)
+#pragma unroll
+            for (int w = 0; w < WPS; ++w) __builtin_memcpy(&dst[q][w], scale_base(q, t) + 4 * w, 4);
+    };
+    // scales of the partial tail step: blocks past the row read as 2^0
+    auto load_scales_tail = [&](int t, uint32_t (&dst)[NSR][WPS]) {
+        const int left = args.KB - t * BPS;
+#pragma unroll
+        for (int q = 0; q < NSR; ++q)
+#pragma unroll
+            for (int w = 0; w < WPS; ++w) {
+                uint32_t v = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int blk = 4 * w + b;
+                    const uint32_t e = blk < left ? scale_base(q, t)[blk] : 127u;
+                    v |= e << (8 * b);
+                }
+                dst[q][w] = v;
+            }
+    };
+    auto mma_scaled = [&](const Frags& f, int s) {
+        if constexpr (C::MX) {
+            const int sh = 16 * (s & 1) + 8 * g;      // byte of block 2 s + g in word s / 2
+            int sa[TM], sb[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) sa[i] = (int)(sc_cur[i][s >> 1] >> sh);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) sb[j] = (int)(sc_cur[TM + j][s >> 1] >> sh);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = In::mfma_scaled(f.b[j], f.a[i], acc[i][j], sb[j], sa[i]);
+        }
+    };
+    auto contract = [&](const Frags& f, int s) {
+        if constexpr (C::MX)
+            mma_scaled(f, s);
+        else
+            mma(f);
     };
 
     Frags fr[2];
@@ -740,6 +860,10 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         // others at a barrier (which also retires every read of stage t, so its
         // buffer may be refilled), and starts reading stage t+1 while the last
         // MFMAs of stage t run.
+        // Block-scaled inputs: step t+1's scales are loaded at the top of step
+        // t, before its copies, so the wait for stage t+1 covers them too.
+        if constexpr (C::MX)
+            if (nk > 0) load_scales(0, sc_cur);
 #pragma unroll
         for (int st = 0; st < S - 1; ++st)
             if (st < nk) issue_direct(st, st);
@@ -753,6 +877,8 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         }
         for (int t = 0; t < nk; ++t) {
             const int stage = t % S;
+            if constexpr (C::MX)
+                if (t + 1 < nk) load_scales(t + 1, sc_nxt);
             if (t + S - 1 < nk) issue_direct(t + S - 1, (t + S - 1) % S);
 #pragma unroll
             for (int s = 0; s < KSUB; ++s) {
@@ -767,8 +893,15 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
                     barrier_lds();
                     read_frags((t + 1) % S, 0, fr[(s + 1) & 1]);
                 }
-                mma(fr[s & 1]);
+                contract(fr[s & 1], s);
             }
+            if constexpr (C::MX)
+                if (t + 1 < nk) {
+#pragma unroll
+                    for (int q = 0; q < NSR; ++q)
+#pragma unroll
+                        for (int w = 0; w < WPS; ++w) sc_cur[q][w] = sc_nxt[q][w];
+                }
         }
     }
     if constexpr (C::DIRECT) {
@@ -777,13 +910,14 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         if (K % BK != 0) {
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             barrier_lds();
+            if constexpr (C::MX) load_scales_tail(nk, sc_cur);
             fill_staged(nk, 0);
             barrier_lds();
             read_frags(0, 0, fr[0]);
 #pragma unroll
             for (int s = 0; s < KSUB; ++s) {
                 if (s + 1 < KSUB) read_frags(0, s + 1, fr[(s + 1) & 1]);
-                mma(fr[s & 1]);
+                contract(fr[s & 1], s);
             }
         }
     } else {

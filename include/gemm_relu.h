@@ -33,6 +33,10 @@ extern "C" {
  * product is the same definition over the exact values of the 8-bit inputs. */
 #define GEMM_RELU_F8_E4M3 3 /* E4M3 ("FN"): bias 7, largest finite 448, no infinities */
 #define GEMM_RELU_F8_E5M2 4 /* E5M2: bias 15, IEEE-style infinities and NaNs */
+/* Block-scaled (OCP Microscaling) element formats, for gemm_relu_mx only. */
+#define GEMM_RELU_MX_E4M3 5 /* MXFP8: E4M3 elements */
+#define GEMM_RELU_MX_E5M2 6 /* MXFP8: E5M2 elements */
+#define GEMM_RELU_MX_E2M1 7 /* MXFP4: E2M1 elements, two per byte (even k in the low nibble) */
 
 /* Status codes.  The library never aborts, throws or prints. */
 #define GEMM_RELU_OK            0
@@ -95,6 +99,42 @@ const char* gemm_relu_strerror(int status);
  */
 const char* gemm_relu_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
                            int64_t K, int in_dtype, int out_dtype, int transB);
+
+/*
+ * gemm_relu_mx — the block-scaled product: the "MXFP8 block-scaled GEMM" and
+ * "CDNA4 MXFP4" items of the first page's §4.1 capability timeline, read as the
+ * OCP Microscaling (MX) definition.  Every 32 consecutive elements of a row
+ * along K share one E8M0 scale (2^(e - 127); e = 255 is NaN), and
+ *
+ *   C[i][j] = max( sum_b XA[i][b] XB[j][b] sum_{k in block b} A[i][k] B[j][k], 0 )
+ *
+ * Arguments
+ *   A    device pointer, M rows of K elements (row-major, element format fmt;
+ *        E2M1 rows are K / 2 bytes, element k in the low nibble of byte k / 2
+ *        when k is even, the high nibble when odd).
+ *   SA   device pointer, M x (K / 32) E8M0 bytes, row-major.
+ *   B    device pointer, N rows of K elements: B is stored (N, K), the
+ *        transposed layout of gemm_relu's transB = 1.
+ *   SB   device pointer, N x (K / 32) E8M0 bytes, row-major.
+ *   C    device pointer, M x N row-major, out_dtype; overwritten.
+ *   M, N, K   >= 0, <= INT32_MAX; K a multiple of 32 (whole scale blocks).
+ *   fmt  GEMM_RELU_MX_E4M3, GEMM_RELU_MX_E5M2 or GEMM_RELU_MX_E2M1.
+ *   out_dtype  GEMM_RELU_F16, GEMM_RELU_BF16 or GEMM_RELU_F32.
+ *   stream     a hipStream_t, or NULL.
+ *
+ * Numerics: each block product is formed on the scaled matrix units and summed
+ * in fp32 (order unspecified); ReLU and rounding as for gemm_relu.
+ * Ownership, execution and errors as for gemm_relu (EINVAL also for K not a
+ * multiple of 32, an unknown fmt, or C overlapping A, B, SA or SB;
+ * EUNSUPPORTED when K exceeds 2^22 storage bytes per row).
+ */
+int gemm_relu_mx(const void* A, const void* SA, const void* B, const void* SB, void* C,
+                 int64_t M, int64_t N, int64_t K, int fmt, int out_dtype, void* stream);
+
+/* Configuration name gemm_relu_mx would launch (as gemm_relu_plan). */
+const char* gemm_relu_mx_plan(const void* A, const void* SA, const void* B, const void* SB,
+                              const void* C, int64_t M, int64_t N, int64_t K, int fmt,
+                              int out_dtype);
 
 #ifdef __cplusplus
 }

@@ -148,3 +148,32 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
                 assert "oracle.c" not in text and "liboracle" not in text, fn
+
+
+# ------------------------------------------------ block-scaled entry point
+SA_, SB_ = 4 << 32, 5 << 32
+
+
+@pytest.mark.parametrize("args", [
+    (A, SA_, B, SB_, C, 4, 4, 48, 5, 0),      # K not a multiple of 32
+    (A, SA_, B, SB_, C, 4, 4, 64, 3, 0),      # a plain FP8 code is not an MX format
+    (A, SA_, B, SB_, C, 4, 4, 64, 8, 0),      # unknown format
+    (A, SA_, B, SB_, C, 4, 4, 64, 5, 3),      # unknown output
+    (A, 0, B, SB_, C, 4, 4, 64, 7, 0),        # NULL scales with elements
+    (A, SA_, B, SB_, SA_, 4, 4, 64, 7, 0),    # C overlaps SA
+    (A, SA_, B, SB_, C, -1, 4, 64, 7, 0),     # negative M
+])
+def test_mx_invalid_arguments(args):
+    assert gr.gemm_relu_mx_status(*args, stream=0) == gr.EINVAL
+    assert gr.gemm_relu_mx_plan(*args) is None
+
+
+@pytest.mark.parametrize("M,N,K,want", [
+    (8192, 8192, 8192, "d256x256x64_s2"),
+    (1024, 1024, 4096, "d128x128x64_s2"),
+    (64, 64, 64, "d128x128x64_s2"),
+])
+@pytest.mark.parametrize("fmt", [5, 6, 7])
+def test_mx_plan_selection(M, N, K, want, fmt):
+    assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, M, N, K, fmt, 0) == want
+    assert gr.gemm_relu_mx_plan(0, 0, 0, 0, C, 0, N, K, fmt, 0) == "none"
