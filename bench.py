@@ -29,6 +29,7 @@ import workloads as wl  # noqa: E402
 
 PEAK_TFLOPS_F16 = 2516.6      # MI355X dense fp16/bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_TFLOPS_F8 = 5033.2       # MI355X dense fp8 MFMA: 256 CU x 8192 flop/clk x 2.4 GHz
+PEAK_TFLOPS_F4 = 10066.3      # MI355X dense fp4 / fp6 MFMA: 256 CU x 16384 flop/clk x 2.4 GHz
 HBM_GBPS = 8000.0
 METRIC = "TFLOP/s and % of MI355X fp16 MFMA peak, fp16 GEMM+ReLU 8192³"
 KERNEL_SOURCES = ["dense_tiled_gemm_relu_amd/csrc/gemm_relu_kernel.hpp",
@@ -136,8 +137,73 @@ def cpu_baseline(w, A, B, target_s=15.0):
                       "binary64), %.2f s wall" % (R - 1, R, N, K, w["name"], dt)}
 
 
+def cpu_baseline_mx(w, target_s=15.0):
+    """The block-scaled oracle on the first R rows of A against all of B."""
+    import oracle
+    M, N, K, fmt = w["M"], w["N"], w["K"], w["in_dtype"]
+    A, SA, B, SB = wl.mx_inputs(M, N, K, fmt, w["index"], w["dist"])
+    R = 1
+    for _ in range(6):
+        rows = np.repeat(np.arange(R), N)
+        cols = np.tile(np.arange(N), R)
+        t = time.perf_counter()
+        oracle.gemm_relu_mx_ref(A, SA, B, SB, M, N, K, fmt, rows=rows, cols=cols)
+        dt = time.perf_counter() - t
+        if dt >= 0.6 * target_s or R >= M:
+            break
+        R = int(min(M, max(R + 1, R * target_s / max(dt, 1e-3))))
+    flops = 2.0 * R * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count())),
+            "kind": "oracle",
+            "sample": "rows 0..%d of A (%d x %d x %d block-scaled multiply-adds of the %s "
+                      "workload, binary64), %.2f s wall" % (R - 1, R, N, K, w["name"], dt)}
+
+
 def peak_tflops(in_dtype):
-    return PEAK_TFLOPS_F8 if in_dtype in wl.FP8 else PEAK_TFLOPS_F16
+    if in_dtype == wl.MX_E2M1:
+        return PEAK_TFLOPS_F4
+    if in_dtype in wl.FP8 or in_dtype in (wl.MX_E4M3, wl.MX_E5M2):
+        return PEAK_TFLOPS_F8
+    return PEAK_TFLOPS_F16
+
+
+def ceiling_kind(in_dtype):
+    """probe_mfma_rate kind matching an input type: 0 fp16, 1 E4M3, 2 E2M1
+    (scaled MFMA), 3 E4M3 on the scaled MFMA."""
+    if in_dtype == wl.MX_E2M1:
+        return 2
+    if in_dtype in (wl.MX_E4M3, wl.MX_E5M2):
+        return 3
+    return 1 if in_dtype in wl.FP8 else 0
+
+
+def workload_call(gr, name, stream):
+    """(call, C tensor, tile config, algorithmic bytes) for one workload, its
+    inputs uploaded: plain ones through gemm_relu, block-scaled ones through
+    gemm_relu_mx."""
+    import torch
+    w = wl.WORKLOADS[name]
+    M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
+    Cd = torch.empty((M, N), dtype=torch_dtype(oc), device="cuda")
+    if w.get("mx"):
+        arrs = wl.mx_inputs(M, N, K, ic, w["index"], w["dist"])
+        Ad, SAd, Bd, SBd = (torch.from_numpy(np.ascontiguousarray(x).reshape(-1)).cuda() for x in arrs)
+
+        def call():
+            gr.gemm_relu_mx(Ad, SAd, Bd, SBd, Cd, M, N, K, ic, oc, stream)
+        plan = gr.gemm_relu_mx_plan(Ad, SAd, Bd, SBd, Cd, M, N, K, ic, oc)
+        nbytes = sum(int(x.size) for x in arrs) + M * N * wl.elem_bytes(oc)
+        return call, Cd, plan, nbytes, (Ad, SAd, Bd, SBd)
+    A, B = wl.workload_inputs(name)
+    Ad = to_device(A, ic, (M, K))
+    Bd = to_device(B, ic, wl.b_shape(M, N, K, tb))
+
+    def call():
+        gr.gemm_relu(Ad, Bd, Cd, M, N, K, ic, oc, tb, stream)
+    plan = gr.gemm_relu_plan(Ad, Bd, Cd, M, N, K, ic, oc, tb)
+    nbytes = wl.elem_bytes(ic) * (M * K + K * N) + M * N * wl.elem_bytes(oc)
+    return call, Cd, plan, nbytes, (Ad, Bd)
 
 
 def torch_dtype(code):
@@ -154,13 +220,15 @@ def to_device(bits, code, shape):
     return torch.from_numpy(raw).cuda().view(torch_dtype(code))
 
 
-def mfma_ceiling(gr, stream, blocks=1024, steps=2048, fp8=False):
+def mfma_ceiling(gr, stream, blocks=1024, steps=2048, kind=0):
     """MFMA-only throughput on random operands with no memory traffic (the probe
     library's probe_mfma_rate: 4 waves per CU, each streaming the 32 MFMAs of
-    one step of a 128x128 wave tile; fp16 32x32x16, or with fp8=True E4M3
-    32x32x64).  The chip is power-limited, so this, not 2.4 GHz x the
-    instruction rate, is what the contraction step alone can reach on this machine
-    now.  None if the probe library is not built."""
+    one step of a 128x128 wave tile; kind 0: fp16 32x32x16, 1: E4M3 32x32x64,
+    2: E2M1 32x32x64 on the scaled MFMA with unit scales, 3: E4M3 on the scaled
+    MFMA).  The chip is
+    power-limited, so this, not 2.4 GHz x the instruction rate, is what the
+    contraction step alone can reach on this machine now.  None if the probe
+    library is not built."""
     import ctypes
     import torch
     if not os.path.exists(gr.PROBE_LIB_PATH):
@@ -169,16 +237,19 @@ def mfma_ceiling(gr, stream, blocks=1024, steps=2048, fp8=False):
     lib.probe_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_void_p]
-    per_lane = 32 if fp8 else 8                 # operand elements per lane (32 bytes / 16 bytes)
-    src = torch.empty(blocks * 8 * 256 * per_lane, dtype=torch.float32, device="cuda")
-    src = src.uniform_(-1, 1).to(torch.float8_e4m3fn if fp8 else torch.float16)
+    if kind == 2:                               # random E2M1 nibbles, 16 bytes per lane
+        src = torch.randint(0, 256, (blocks * 8 * 256 * 16,), dtype=torch.uint8, device="cuda")
+    else:
+        per_lane = 32 if kind in (1, 3) else 8  # operand elements per lane (32 bytes / 16 bytes)
+        src = torch.empty(blocks * 8 * 256 * per_lane, dtype=torch.float32, device="cuda")
+        src = src.uniform_(-1, 1).to(torch.float8_e4m3fn if kind in (1, 3) else torch.float16)
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     ticks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
     st = stream.cuda_stream
 
     def run(n):
         rc = lib.probe_mfma_rate(src.data_ptr(), src.numel() * src.element_size(), out.data_ptr(),
-                                 ticks.data_ptr(), blocks, n, 1 if fp8 else 0, st)
+                                 ticks.data_ptr(), blocks, n, kind, st)
         if rc != 0:
             raise RuntimeError("probe_mfma_rate failed: %d" % rc)
 
@@ -193,11 +264,11 @@ def mfma_ceiling(gr, stream, blocks=1024, steps=2048, fp8=False):
     t = ticks.view(blocks, 2).double()
     cycles = t[:, 0].mean().item()
     clock_mhz = (t[:, 0] / t[:, 1]).mean().item() * 100.0
-    flops = blocks * 4 * steps * 32 * (32 * 32 * (64 if fp8 else 16) * 2)
+    flops = blocks * 4 * steps * 32 * (32 * 32 * (16 if kind == 0 else 64) * 2)
     return {"tflops": round(flops / sec / 1e12, 1), "clock_mhz": round(clock_mhz),
             "cycles_per_mfma": round(cycles / (steps * 32), 2),
             "kind": "MFMA-only, random %s operands, no memory traffic (probe_mfma_rate)"
-                    % ("E4M3" if fp8 else "fp16")}
+                    % ("fp16", "E4M3", "E2M1 (unit block scales)", "E4M3 (unit block scales)")[kind]}
 
 
 def table(gr):
@@ -209,21 +280,16 @@ def table(gr):
     import torch
     stream = torch.cuda.current_stream()
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
-    ceilings = {False: mfma_ceiling(gr, stream), True: mfma_ceiling(gr, stream, fp8=True)}
-    print(json.dumps({"mfma_ceiling": ceilings[False], "mfma_ceiling_fp8": ceilings[True]}),
+    ceilings = {k: mfma_ceiling(gr, stream, kind=k) for k in (0, 1, 2, 3)}
+    print(json.dumps({"mfma_ceiling": ceilings[0], "mfma_ceiling_fp8": ceilings[1],
+                      "mfma_ceiling_mxfp4": ceilings[2], "mfma_ceiling_mxfp8": ceilings[3]}),
           flush=True)
     for name in sorted(wl.WORKLOADS, key=lambda n: wl.WORKLOADS[n]["index"]):
         w = wl.WORKLOADS[name]
         M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
-        A, B = wl.workload_inputs(name)
-        Ad = to_device(A, ic, (M, K))
-        Bd = to_device(B, ic, wl.b_shape(M, N, K, tb))
-        Cd = torch.empty((M, N), dtype=torch_dtype(oc), device="cuda")
-        ceiling = ceilings[ic in wl.FP8]
+        call, Cd, plan, nbytes, keep = workload_call(gr, name, stream)
+        ceiling = ceilings[ceiling_kind(ic)]
         peak = peak_tflops(ic)
-
-        def call():
-            gr.gemm_relu(Ad, Bd, Cd, M, N, K, ic, oc, tb, stream)
 
         for _ in range(10):
             call()
@@ -250,11 +316,10 @@ def table(gr):
         t = statistics.median(trials)
         tc = statistics.median(cold)
         flops = 2.0 * M * N * K
-        nbytes = wl.elem_bytes(ic) * (M * K + K * N) + M * N * wl.elem_bytes(oc)
         print(json.dumps({
             "workload": name, "M": M, "N": N, "K": K, "in": wl.DTYPE_NAMES[ic],
             "out": wl.DTYPE_NAMES[oc], "transB": tb,
-            "tile_config": gr.gemm_relu_plan(Ad, Bd, Cd, M, N, K, ic, oc, tb),
+            "tile_config": plan,
             "t_median_us": round(t, 2), "t_trials_us": [round(x, 2) for x in trials],
             "tflops": round(flops / t / 1e6, 1),
             "pct_peak": round(100 * flops / t / 1e6 / peak, 2), "peak_tflops": peak,
@@ -264,7 +329,7 @@ def table(gr):
             "pct_hbm": round(100 * nbytes / t / 1e3 / HBM_GBPS, 2),
             "t_cold_median_us": round(tc, 2), "tflops_cold": round(flops / tc / 1e6, 1)}),
             flush=True)
-        del Ad, Bd, Cd
+        del keep, Cd
 
 
 def main():
@@ -309,16 +374,9 @@ def main():
 
     w = dict(wl.WORKLOADS[args.workload], name=args.workload)
     M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
-    A, B = wl.workload_inputs(args.workload)
-    Ad = to_device(A, ic, (M, K))
-    Bd = to_device(B, ic, wl.b_shape(M, N, K, tb))
-    Cd = torch.empty((M, N), dtype=torch_dtype(oc), device="cuda")
-    peak = peak_tflops(ic)
-    plan = gr.gemm_relu_plan(Ad, Bd, Cd, M, N, K, ic, oc, tb)
     stream = torch.cuda.current_stream()
-
-    def step():
-        gr.gemm_relu(Ad, Bd, Cd, M, N, K, ic, oc, tb, stream)
+    step, Cd, plan, nbytes, keep = workload_call(gr, args.workload, stream)
+    peak = peak_tflops(ic)
 
     for _ in range(args.warmup):
         step()
@@ -344,7 +402,8 @@ def main():
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     metric = METRIC if args.workload == "gemm_relu_f16_8192" else (
         "TFLOP/s and %% of MI355X %s MFMA peak, %s" %
-        ("fp8" if ic in wl.FP8 else "fp16/bf16", args.workload))
+        ({PEAK_TFLOPS_F4: "fp4", PEAK_TFLOPS_F8: "fp8"}.get(peak_tflops(ic), "fp16/bf16"),
+         args.workload))
     out = {
         "metric": metric,
         "value": round(value, 2),
@@ -365,15 +424,18 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(args.workload),
-                     "algorithmic_bytes": int(wl.elem_bytes(ic) * (M * K + K * N) +
-                                              M * N * wl.elem_bytes(oc)),
+                     "algorithmic_bytes": int(nbytes),
                      "kernel_ms": round(kernel_ms, 5)},
     }
-    ceiling = mfma_ceiling(gr, stream, fp8=ic in wl.FP8)
+    ceiling = mfma_ceiling(gr, stream, kind=ceiling_kind(ic))
     if ceiling is not None:
         out["mfma_ceiling"] = dict(ceiling, frac=round(achieved / ceiling["tflops"], 4))
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, A, B)
+        if w.get("mx"):
+            out["cpu_baseline"] = cpu_baseline_mx(w)
+        else:
+            A, B = wl.workload_inputs(args.workload)
+            out["cpu_baseline"] = cpu_baseline(w, A, B)
     print(json.dumps(out), flush=True)
 
 

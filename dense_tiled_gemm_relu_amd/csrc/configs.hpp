@@ -23,6 +23,7 @@ enum ConfigId : int {
     CFG_D256x256x64_S2_W8,
     CFG_D128x128x64_S3,
     CFG_D128x128x64_S2,
+    CFG_D256x128x64_S2,
     CFG_D64x64x64_S4,
     CFG_D64x32x128_S4,
     CFG_G128x128x64,
@@ -49,6 +50,7 @@ inline const ConfigInfo& config_info(int id)
         {"d256x256x64_s2_w8", 256, 256, true},
         {"d128x128x64_s3", 128, 128, true},
         {"d128x128x64_s2", 128, 128, true},
+        {"d256x128x64_s2", 256, 128, true},
         {"d64x64x64_s4", 64, 64, true},
         {"d64x32x128_s4", 64, 32, true},
         {"g128x128x64", 128, 128, false},
@@ -101,6 +103,11 @@ template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D128x128x64_S3
 // Two-stage 128x128: the smaller tile of the block-scaled inputs.
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D128x128x64_S2> {
     using type = Cfg<IN, OUT, TB, 128, 128, bk_of<IN, 64>, 2, 2, 2, true>;
+};
+// Two-stage 256x128 (waves of 128x64): fewer fragment registers than 256x256
+// for the block-scaled inputs, whose per-lane scales need registers too.
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x128x64_S2> {
+    using type = Cfg<IN, OUT, TB, 256, 128, bk_of<IN, 64>, 2, 2, 2, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D64x64x64_S4> {
     using type = Cfg<IN, OUT, TB, 64, 64, bk_of<IN, 64>, 2, 2, 4, true>;
@@ -249,6 +256,8 @@ inline bool fp8_config(int cfg)
             return &launch_one<typename CfgOf<IN, OUT, true, CFG_D256x256x64_S2>::type>;   \
         case CFG_D128x128x64_S2:                                                           \
             return &launch_one<typename CfgOf<IN, OUT, true, CFG_D128x128x64_S2>::type>;   \
+        case CFG_D256x128x64_S2:                                                           \
+            return &launch_one<typename CfgOf<IN, OUT, true, CFG_D256x128x64_S2>::type>;   \
         default:                                                                           \
             return nullptr;                                                                \
         }                                                                                  \

@@ -6,7 +6,10 @@
 // accumulators and 4 + 4 operand registers: the MFMA stream of one step of a
 // 128x128 wave tile, with no memory traffic and no LDS.  kind 0:
 // v_mfma_f32_32x32x16_f16 (16-byte operands); kind 1:
-// v_mfma_f32_32x32x64_f8f6f4 on E4M3 data (32-byte operands).  The operands are the caller's random fp16 data, so the multiplier
+// v_mfma_f32_32x32x64_f8f6f4 on E4M3 data (32-byte operands); kind 2:
+// v_mfma_scale_f32_32x32x64_f8f6f4 on E2M1 data with unit E8M0 scales
+// (16-byte operands); kind 3: the same scaled MFMA on E4M3 data (32-byte
+// operands).  The operands are the caller's random fp16 data, so the multiplier
 // arrays toggle as they do in the GEMM; on MI355X this, not the instruction
 // rate, sets the shader clock.  Wave 0 of each workgroup records the shader
 // cycles (s_memtime) and 100 MHz reference ticks (s_memrealtime) of its loop.
@@ -32,12 +35,14 @@ k_mfma_rate(const unsigned char* src, float* out, unsigned long long* ticks, int
     using In = InTraits<IN_DT>;
     using Op = typename In::Op;
     const int tid = threadIdx.x;
-    const Op* ops = reinterpret_cast<const Op*>(src);
-    const size_t base = (size_t)blockIdx.x * kOperandRegs * kThreads + tid;
+    constexpr int OPB = In::OPB;      // operand bytes per lane
+    const size_t base = ((size_t)blockIdx.x * kOperandRegs * kThreads + tid) * OPB;
     Op a[4], b[4];
     for (int i = 0; i < 4; ++i) {
-        a[i] = ops[base + (size_t)i * kThreads];
-        b[i] = ops[base + (size_t)(4 + i) * kThreads];
+        a[i] = Op{};
+        b[i] = Op{};
+        __builtin_memcpy(&a[i], src + base + (size_t)i * kThreads * OPB, OPB);
+        __builtin_memcpy(&b[i], src + base + (size_t)(4 + i) * kThreads * OPB, OPB);
     }
     f32x16_t acc[16];
     for (int i = 0; i < 16; ++i)
@@ -49,8 +54,12 @@ k_mfma_rate(const unsigned char* src, float* out, unsigned long long* ticks, int
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int p = 0; p < 16; ++p)
-                acc[p] = In::mfma(b[p / 4], a[p % 4], acc[p]);
+            for (int p = 0; p < 16; ++p) {
+                if constexpr (In::MX)
+                    acc[p] = In::mfma_scaled(b[p / 4], a[p % 4], acc[p], 127, 127);
+                else
+                    acc[p] = In::mfma(b[p / 4], a[p % 4], acc[p]);
+            }
         __builtin_amdgcn_s_barrier();
     }
     const unsigned long long c1 = __builtin_amdgcn_s_memtime();
@@ -68,15 +77,15 @@ k_mfma_rate(const unsigned char* src, float* out, unsigned long long* ticks, int
 }  // namespace
 
 // src: at least blocks * 8 * 256 * OPB bytes of input data (OPB = 16 for
-// kind 0, fp16; 32 for kind 1, E4M3); out: blocks * 256 floats; ticks:
+// kind 0, fp16; 32 for kinds 1 and 3, E4M3; 16 for kind 2, packed E2M1); out: blocks * 256 floats; ticks:
 // 2 * blocks values (shader cycles, reference ticks per workgroup).  Launches
 // on `stream` without synchronising.  Returns 0, -1 on bad arguments, -3 on a
 // launch failure.
 extern "C" int probe_mfma_rate(const void* src, size_t src_bytes, void* out, void* ticks,
                                int blocks, int steps, int kind, void* stream)
 {
-    if (kind != 0 && kind != 1) return -1;
-    const size_t opb = kind == 0 ? 16 : 32;
+    if (kind < 0 || kind > 3) return -1;
+    const size_t opb = (kind == 1 || kind == 3) ? 32 : 16;
     if (!src || !out || !ticks || blocks <= 0 || steps <= 0 ||
         src_bytes < (size_t)blocks * kOperandRegs * kThreads * opb)
         return -1;
@@ -85,8 +94,14 @@ extern "C" int probe_mfma_rate(const void* src, size_t src_bytes, void* out, voi
     if (kind == 0)
         hipLaunchKernelGGL(k_mfma_rate<DT_F16>, dim3(blocks), dim3(kThreads), 0, st, s,
                            (float*)out, (unsigned long long*)ticks, steps);
-    else
+    else if (kind == 1)
         hipLaunchKernelGGL(k_mfma_rate<DT_F8E4M3>, dim3(blocks), dim3(kThreads), 0, st, s,
+                           (float*)out, (unsigned long long*)ticks, steps);
+    else if (kind == 2)
+        hipLaunchKernelGGL(k_mfma_rate<DT_MX_E2M1>, dim3(blocks), dim3(kThreads), 0, st, s,
+                           (float*)out, (unsigned long long*)ticks, steps);
+    else
+        hipLaunchKernelGGL(k_mfma_rate<DT_MX_E4M3>, dim3(blocks), dim3(kThreads), 0, st, s,
                            (float*)out, (unsigned long long*)ticks, steps);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }

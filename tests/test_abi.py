@@ -169,7 +169,7 @@ def test_mx_invalid_arguments(args):
 
 
 @pytest.mark.parametrize("M,N,K,want", [
-    (8192, 8192, 8192, "d256x256x64_s2"),
+    (8192, 8192, 8192, "d128x128x64_s2"),
     (1024, 1024, 4096, "d128x128x64_s2"),
     (64, 64, 64, "d128x128x64_s2"),
 ])
@@ -177,3 +177,18 @@ def test_mx_invalid_arguments(args):
 def test_mx_plan_selection(M, N, K, want, fmt):
     assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, M, N, K, fmt, 0) == want
     assert gr.gemm_relu_mx_plan(0, 0, 0, 0, C, 0, N, K, fmt, 0) == "none"
+
+
+@pytest.mark.parametrize("name", ["d256x256x64_s2", "d256x128x64_s2", "d128x128x64_s2"])
+def test_mx_forced_configuration(monkeypatch, name):
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", name)
+    assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 8192, 8192, 8192, 7, 0) == name
+    # a configuration not built for block-scaled inputs falls back
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x256x32_s4_i")
+    assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 8192, 8192, 8192, 7, 0) == "d128x128x64_s2"
+
+
+@pytest.mark.parametrize("in_dtype", [0, 1, 3])
+def test_mx_only_configuration_not_used_for_other_inputs(monkeypatch, in_dtype):
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x128x64_s2")
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, in_dtype, 0, 1) == "d256x256x32_s4_i"

@@ -13,7 +13,7 @@ from tests.helpers import check_close, from_device, fp32_sum_bound, out_tensor, 
 pytestmark = pytest.mark.gpu
 
 FMTS = [wl.MX_E4M3, wl.MX_E5M2, wl.MX_E2M1]
-CONFIGS = ["d256x256x64_s2", "d128x128x64_s2"]
+CONFIGS = ["d256x256x64_s2", "d256x128x64_s2", "d128x128x64_s2"]
 
 
 @pytest.fixture(autouse=True)

@@ -114,7 +114,8 @@ def test_unaligned_16_byte_loads(probe):
     assert np.array_equal(got[0], want), "direct global->LDS copy"
 
 
-@pytest.mark.parametrize("kind,opb,cycles", [(0, 16, 32), (1, 32, 64)], ids=["f16", "e4m3"])
+@pytest.mark.parametrize("kind,opb,cycles", [(0, 16, 32), (1, 32, 64), (2, 16, 32), (3, 32, 64)],
+                         ids=["f16", "e4m3", "mx_e2m1", "mx_e4m3"])
 def test_mfma_rate_probe(probe, kind, opb, cycles):
     """The MFMA-only diagnostic (random operands, no memory traffic) runs, issues
     one 32x32x16 fp16 MFMA per 32 shader cycles (one 32x32x64 E4M3 MFMA per
@@ -127,9 +128,12 @@ def test_mfma_rate_probe(probe, kind, opb, cycles):
                                     ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_void_p]
     blocks, steps = 256, 256
-    per_lane = opb // 2 if kind == 0 else opb           # elements per operand per lane
-    src = torch.empty(blocks * 8 * 256 * per_lane, dtype=torch.float32, device="cuda")
-    src = src.uniform_(-1, 1).to(torch.float16 if kind == 0 else torch.float8_e4m3fn)
+    if kind == 2:                                        # random E2M1 nibble pairs
+        src = torch.randint(0, 256, (blocks * 8 * 256 * opb,), dtype=torch.uint8, device="cuda")
+    else:
+        per_lane = opb // 2 if kind == 0 else opb       # elements per operand per lane
+        src = torch.empty(blocks * 8 * 256 * per_lane, dtype=torch.float32, device="cuda")
+        src = src.uniform_(-1, 1).to(torch.float16 if kind == 0 else torch.float8_e4m3fn)
     nbytes = src.numel() * src.element_size()
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     ticks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
@@ -137,7 +141,7 @@ def test_mfma_rate_probe(probe, kind, opb, cycles):
     assert lib.probe_mfma_rate(src.data_ptr(), nbytes - 1, out.data_ptr(),
                                ticks.data_ptr(), blocks, steps, kind, st) == -1
     assert lib.probe_mfma_rate(src.data_ptr(), nbytes, out.data_ptr(),
-                               ticks.data_ptr(), blocks, steps, 2, st) == -1
+                               ticks.data_ptr(), blocks, steps, 4, st) == -1
     assert lib.probe_mfma_rate(src.data_ptr(), nbytes, out.data_ptr(),
                                ticks.data_ptr(), blocks, steps, kind, st) == 0
     torch.cuda.synchronize()

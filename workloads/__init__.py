@@ -101,6 +101,11 @@ WORKLOADS = {
     # the FP8 GEMM of the first page's capability list at the headline shape
     "gemm_relu_f8e4m3_8192": dict(index=7, M=8192, N=8192, K=8192, in_dtype=F8E4M3,
                                   out_dtype=F16, transB=0, dist="uniform"),
+    # block-scaled (gemm_relu_mx): the MXFP4 / MXFP8 of the same list, B stored (N, K)
+    "gemm_relu_mxfp4_8192": dict(index=8, M=8192, N=8192, K=8192, in_dtype=MX_E2M1,
+                                 out_dtype=F16, transB=1, dist="uniform", mx=True),
+    "gemm_relu_mxfp8_8192": dict(index=9, M=8192, N=8192, K=8192, in_dtype=MX_E4M3,
+                                 out_dtype=F16, transB=1, dist="uniform", mx=True),
 }
 
 
