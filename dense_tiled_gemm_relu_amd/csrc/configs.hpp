@@ -252,6 +252,8 @@ inline bool fp8_config(int cfg)
     static LaunchFn FN##_out(int cfg)                                                      \
     {                                                                                      \
         switch (cfg) {                                                                     \
+        case CFG_D256x256x32_S4_I:                                                         \
+            return &launch_one<typename CfgOf<IN, OUT, true, CFG_D256x256x32_S4_I>::type>; \
         case CFG_D256x256x64_S2:                                                           \
             return &launch_one<typename CfgOf<IN, OUT, true, CFG_D256x256x64_S2>::type>;   \
         case CFG_D128x128x64_S2:                                                           \

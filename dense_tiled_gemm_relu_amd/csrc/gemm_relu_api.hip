@@ -218,20 +218,32 @@ Plan make_plan_mx(const void* A, const void* SA, const void* B, const void* SB, 
         p.status = GEMM_RELU_EINVAL;
         return p;
     }
+    // The interleaved pipeline stages scales in LDS by 16-byte row pieces (so
+    // rows of at least 16 blocks) and addresses them with 32-bit offsets.
+    const bool lds_scales_fit = K / 32 >= 16 && sa_bytes < (uint64_t(1) << 32) &&
+                                sb_bytes < (uint64_t(1) << 32);
     auto usable = [&](int id) {
-        return (id == CFG_D256x256x64_S2 || id == CFG_D256x128x64_S2 || id == CFG_D128x128x64_S2) &&
+        return (id == CFG_D256x256x64_S2 || id == CFG_D256x128x64_S2 || id == CFG_D128x128x64_S2 ||
+                (id == CFG_D256x256x32_S4_I && lds_scales_fit)) &&
                direct_fits(id, N, ks, 1);
     };
-    // The 128x128 tile: measured on MI355X at 8192^3 it matches the 256x256
-    // tile with E2M1 elements and beats it by a third with 8-bit elements (the
-    // larger tile's scale and fragment registers spill), and it gives four
-    // times as many workgroups on smaller products.  The two larger tiles stay
-    // selectable for comparison.
+    // Estimated time per K, as for the other inputs: rounds of workgroups over
+    // the CUs times the tile's area over its efficiency relative to the
+    // interleaved 256x256 tile (the two-stage 128x128 tile measured 0.59
+    // (MXFP8) and 0.74 (MXFP4) of it at 8192^3).  The two-stage 256x256 and
+    // 256x128 tiles stay selectable for comparison.
+    auto tiles = [&](int id) { return ceil_div(M, config_info(id).bm) * ceil_div(N, config_info(id).bn); };
+    auto cost = [&](int id) {
+        const ConfigInfo& ci = config_info(id);
+        return double(ceil_div(tiles(id), kNumCUs)) * ci.bm * ci.bn / (ci.bm >= 256 ? 1.0 : 0.6);
+    };
     int cfg = -1;
-    if (e.force_cfg >= 0 && usable(e.force_cfg))
+    if (e.force_cfg >= 0 && usable(e.force_cfg)) {
         cfg = e.force_cfg;
-    else if (usable(CFG_D128x128x64_S2))
-        cfg = CFG_D128x128x64_S2;
+    } else {
+        for (int id : {CFG_D256x256x32_S4_I, CFG_D128x128x64_S2})
+            if (usable(id) && (cfg < 0 || cost(id) < cost(cfg))) cfg = id;
+    }
     if (cfg < 0) {
         p.status = GEMM_RELU_EUNSUPPORTED;     // K beyond the 32-bit copy offsets
         return p;

@@ -290,7 +290,18 @@ struct Cfg {
     static constexpr int A_BYTES = BM * BK * EB;
     static constexpr int B_BYTES = BN * BK * EB;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static constexpr bool MX = In::MX;
+    // Scale blocks per row per BK step (block-scaled inputs).
+    static constexpr int BPS = MX ? BK * In::EPB / 32 : 1;
+    // Block-scaled inputs on the interleaved pipeline keep their scales in
+    // LDS: for a group of SGS steps, the 16 scale bytes of each of the tile's
+    // BM + BN rows (one 16-byte copy per row), in two regions that alternate
+    // by group.
+    static constexpr bool MX_LDS = MX && INTERLEAVE_;
+    static constexpr int SGS = MX_LDS ? 16 / BPS : 1;
+    static constexpr int SC_REGION = MX_LDS ? (BM + BN) * 16 : 0;
+    static constexpr int SC_COPIES = MX_LDS ? (BM + BN) / NTHREADS : 0;   // per thread per group
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + 2 * SC_REGION;
     static constexpr int A_CH = BM * ROW_CH;                       // 16 B chunks per stage
     static constexpr int B_CH = BN * BK * EB / 16;
     static constexpr int A_PER_THREAD = A_CH / NTHREADS;
@@ -302,13 +313,15 @@ struct Cfg {
     static_assert(BK * EB == 64 || BK * EB == 128 || BK * EB == 256, "k-contiguous rows of 64, 128 or 256 bytes");
     static_assert(KSUB >= 1 && BK % In::KMF == 0, "whole MFMA k-steps per BK step");
     static_assert(KSUB % 2 == 0 || INTERLEAVE_, "an odd k-step count needs the step-parity tags of the interleaved loop");
-    static constexpr bool MX = In::MX;
-    static_assert(!MX || (TRANS_B && DIRECT && !INTERLEAVE_ && STAGES_ == 2 && MB_ == 32),
-                  "block-scaled inputs: B stored (N,K), two-stage direct pipeline");
+    static_assert(!MX || (TRANS_B && DIRECT && MB_ == 32 && (INTERLEAVE_ ? STAGES_ == 4 : STAGES_ == 2)),
+                  "block-scaled inputs: B stored (N,K); the two-stage direct pipeline or the "
+                  "four-stage interleaved one");
+    static_assert(!MX_LDS || ((BPS == 2 || BPS == 4) && BM % NTHREADS == 0 && BN % NTHREADS == 0),
+                  "LDS-staged scales: 2 or 4 blocks per step; whole A and B row sets per copy");
     static_assert(A_CH % NTHREADS == 0 && B_CH % NTHREADS == 0, "loader tiling");
     static_assert(TRANS_B || NROW_CH >= (EB == 2 ? 4 : 2), "n-contiguous B rows of at least 64 (16-bit) or 32 (8-bit) bytes");
-        static_assert(STAGES >= 2 && STAGES <= 5, "stages");
-    static_assert((STAGES - 2) * LOADS_PER_STAGE < 64, "vmcnt range");
+    static_assert(STAGES >= 2 && STAGES <= 5, "stages");
+    static_assert((STAGES - 2) * LOADS_PER_STAGE + SC_COPIES < 64, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity of a gfx950 CU");
 
     // Interleaved direct pipeline: the LOADS_PER_STAGE copies of the stage
@@ -324,7 +337,9 @@ struct Cfg {
                   "interleave: copies and MFMAs must split evenly over the regions");
     // Copies issued after the last copy of stage t+1 when the wave waits for it
     // (start of the last k-step of step t) in the steady state: the whole of
-    // stages t+2 .. t+S-2 and the first KSUB-1 k-steps' share of stage t+S-1.
+    // stages t+2 .. t+S-2 and the first KSUB-1 k-steps' share of stage t+S-1
+    // (plus, for LDS-staged scales, a scale group's SC_COPIES when one was
+    // issued in that span; the kernel adds those at run time).
     static constexpr int STEADY_ALLOWANCE =
         (STAGES - 3) * LOADS_PER_STAGE + (KSUB - 1) * (LOADS_PER_STAGE / KSUB);
     static_assert(!INTERLEAVE || STEADY_ALLOWANCE < 64, "vmcnt range");
@@ -684,7 +699,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     // ---- block scales (block-scaled inputs only).  For one BK step the lane
     // keeps the E8M0 scales of its TM rows of A and TN rows of B: BPS blocks
     // per row, WPS words of 4.  k-step s uses block 2 s + g of the step.
-    constexpr int BPS = C::MX ? BK * In::EPB / 32 : 1;
+    constexpr int BPS = C::BPS;
     constexpr int WPS = (BPS + 3) / 4;
     constexpr int NSR = C::MX ? TM + TN : 1;
     uint32_t sc_cur[NSR][WPS], sc_nxt[NSR][WPS];
@@ -760,12 +775,91 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
             else
                 dma16(gb, b_src[l - APT], sb + ((l - APT) * C::NWAVES + wave) * 1024);
         };
-        // MFMA p of a k-step: B block p / TM against A block p % TM
-        auto mfma_op = [&](const Frags& f, int p) {
+
+        // ---- block scales (block-scaled inputs), staged in LDS by groups of
+        // SGS steps: group G holds, for each of the tile's BM + BN rows (A rows
+        // then B rows, 16 bytes apart), the row's scale bytes from block
+        // off(G) on, in region G mod 2.  off(G) is 16 G except for a last,
+        // partial group, which is moved back to end inside the row (rounded
+        // down to whole steps).  Group G+1 is copied at the first step of
+        // group G: its region was last read for step SGS G - 1, during step
+        // SGS G - 2, and every wave has passed a barrier since; it is first
+        // read during step SGS (G+1) - 1, after the wait for stage SGS (G+1),
+        // whose copies are issued later than the group's.  Each lane reads its
+        // step's scale of every A and B row it multiplies one step ahead, into
+        // one of two register sets: the byte of its own block (2 blocks per
+        // step) or the row's 4-byte word, of which k-step s takes byte 2 s + g
+        // (4 blocks per step).
+        constexpr int SGS = C::SGS, GC = C::SC_COPIES;
+        constexpr int NSC = C::MX_LDS ? TM + TN : 1;
+        uint32_t scg_src[GC > 0 ? GC : 1];
+        if constexpr (C::MX_LDS) {
+#pragma unroll
+            for (int i = 0; i < GC; ++i) {
+                const int q = i * C::NTHREADS + tid;
+                const int row = q < BM ? min(m0 + q, M - 1) : min(n0 + q - BM, N - 1);
+                scg_src[i] = (uint32_t)row * (uint32_t)args.KB;
+            }
+        }
+        auto group_off = [&](int G) { return min(16 * G, (args.KB - 16) & ~(BPS - 1)); };
+        // whether step u issues the copies of a scale group
+        auto group_step = [&](int u) {
+            return C::MX_LDS && u >= 0 && u % SGS == 0 && SGS * (u / SGS + 1) < nk;
+        };
+        auto issue_group = [&](int G) {
+            if constexpr (C::MX_LDS) {
+                const int off = group_off(G);
+                const uint32_t dst = smem_addr + S * C::STAGE_BYTES + (G & 1) * C::SC_REGION;
+#pragma unroll
+                for (int i = 0; i < GC; ++i) {
+                    const unsigned char* src = (i * C::NTHREADS < BM ? args.SA : args.SB) + off;
+                    dma16(src, scg_src[i], dst + (i * C::NWAVES + wave) * 1024);
+                }
+            }
+        };
+        const int sc_lane = (BPS == 2 ? g : 0);
+        const int sc_a = (wm0 + lr) * 16 + sc_lane, sc_b = (BM + wn0 + lr) * 16 + sc_lane;
+        uint32_t scv[2][NSC];
+        auto read_scales = [&](int t, auto set_tag) {
+            if constexpr (C::MX_LDS) {
+                constexpr int SET = decltype(set_tag)::value;
+                const int G = t / SGS;
+                const GR_LDS unsigned char* reg = smem + S * C::STAGE_BYTES + (G & 1) * C::SC_REGION +
+                                                  (BPS * t - group_off(G));
+#pragma unroll
+                for (int q = 0; q < NSC; ++q) {
+                    const GR_LDS unsigned char* p =
+                        reg + (q < TM ? sc_a + 16 * MB * q : sc_b + 16 * MB * (q - TM));
+                    if constexpr (BPS == 2)
+                        scv[SET][q] = *p;
+                    else
+                        scv[SET][q] = *reinterpret_cast<const GR_LDS uint32_t*>(p);
+                }
+            }
+        };
+        // MFMA p of k-step s: B block p / TM against A block p % TM (scales
+        // from register set SET for block-scaled inputs)
+        auto mfma_op = [&](const Frags& f, int p, int s, auto set_tag) {
             const int j = p / TM, i = p % TM;
-            acc[i][j] = In::mfma(f.b[j], f.a[i], acc[i][j]);
+            if constexpr (C::MX) {
+                constexpr int SET = decltype(set_tag)::value;
+                int sa_v, sb_v;
+                if constexpr (BPS == 2) {
+                    sa_v = (int)scv[SET][i];
+                    sb_v = (int)scv[SET][TM + j];
+                } else {
+                    const int sh = 16 * s + 8 * g;
+                    sa_v = (int)(scv[SET][i] >> sh);
+                    sb_v = (int)(scv[SET][TM + j] >> sh);
+                }
+                acc[i][j] = In::mfma_scaled(f.b[j], f.a[i], acc[i][j], sb_v, sa_v);
+            } else {
+                acc[i][j] = In::mfma(f.b[j], f.a[i], acc[i][j]);
+            }
         };
 
+        // Prologue: scale group 0, then stages 0 .. S-2.
+        if (C::MX_LDS && nk > 0) issue_group(0);
 #pragma unroll
         for (int st = 0; st < S - 1; ++st)
             if (st < nk) issue_direct(st, st);
@@ -775,13 +869,15 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
             else
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             barrier_lds();
+            read_scales(0, std::integral_constant<int, 0>{});
 #pragma unroll
             for (int q = 0; q < NR; ++q) read_op(0, 0, q, fr[0]);
         }
         // One BK step.  STEADY: the stage S-1 ahead exists, so the step needs
         // no run-time checks.  PARITY = t mod 2: with an odd number of k-steps
         // per BK step the two fragment sets swap roles from one step to the
-        // next (k-step s of step t contracts set (t KSUB + s) mod 2).
+        // next (k-step s of step t contracts set (t KSUB + s) mod 2).  SLOT =
+        // t mod S (block-scaled inputs: the scale ring).
         auto step = [&](int t, auto steady_tag, auto parity_tag) {
             constexpr bool STEADY = decltype(steady_tag)::value;
             constexpr int PARITY = decltype(parity_tag)::value;
@@ -794,19 +890,29 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
                                                  : b_tile + (size_t)ld_k0 * (size_t)N * EB;
             const uint32_t lsa = smem_addr + ld_stage * C::STAGE_BYTES;
             const uint32_t lsb = lsa + C::A_BYTES;
+            // a scale group's copies issued after stage t+1's, before this
+            // step's wait: by the previous step, or by this one when the wait
+            // is not at its top
+            const bool group_after = group_step(t - 1) || (KSUB > 1 && group_step(t));
 #pragma unroll
             for (int s = 0; s < KSUB; ++s) {
                 const bool last = s + 1 == KSUB;
                 if (last && (STEADY || t + 1 < nk)) {
-                    if (loads)
-                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::STEADY_ALLOWANCE));
-                    else
+                    if (!loads)
                         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+                    else if (C::MX_LDS && group_after)
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::STEADY_ALLOWANCE + GC));
+                    else
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::STEADY_ALLOWANCE));
                     barrier_lds();
                 }
+                if constexpr (C::MX_LDS)
+                    if (s == 0 && group_step(t)) issue_group(t / SGS + 1);
                 const bool reads = !last || STEADY || t + 1 < nk;
                 const int rd_stage = last ? (t + 1) % S : stage;
                 const int rd_s = last ? 0 : s + 1;
+                if constexpr (C::MX_LDS)
+                    if (last && reads) read_scales(t + 1, std::integral_constant<int, 1 - PARITY>{});
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     __builtin_amdgcn_sched_barrier(0);
@@ -826,7 +932,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
                     }
 #pragma unroll
                     for (int p = r * NM / R; p < (r + 1) * NM / R; ++p)
-                        mfma_op(fr[(PARITY * KSUB + s) & 1], p);
+                        mfma_op(fr[(PARITY * KSUB + s) & 1], p, s, parity_tag);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -837,12 +943,13 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
         using Checked = std::integral_constant<bool, false>;
         using P0 = std::integral_constant<int, 0>;
         using P1 = std::integral_constant<int, 1>;
-        if constexpr (KSUB % 2 == 0) {
+        if constexpr (KSUB % 2 == 0 && !C::MX_LDS) {
             for (int t = 0; t < t_steady; ++t) step(t, Steady{}, P0{});
             for (int t = t_steady; t < nk; ++t) step(t, Checked{}, P0{});
         } else {
-            // steps in pairs, so that every step's parity is known at compile
-            // time; a steady step left over before the checked ones runs checked
+            // steps in pairs, so that every step's parity (fragment sets, and
+            // the scale register sets) is known at compile time; a steady
+            // step left over before the checked ones runs checked
             int t = 0;
             for (; t + 1 < t_steady; t += 2) {
                 step(t, Steady{}, P0{});

@@ -169,8 +169,10 @@ def test_mx_invalid_arguments(args):
 
 
 @pytest.mark.parametrize("M,N,K,want", [
-    (8192, 8192, 8192, "d128x128x64_s2"),
+    (8192, 8192, 8192, "d256x256x32_s4_i"),
+    (4096, 4096, 4096, "d256x256x32_s4_i"),
     (1024, 1024, 4096, "d128x128x64_s2"),
+    (8192, 8192, 480, "d128x128x64_s2"),       # fewer than 16 scale blocks per row
     (64, 64, 64, "d128x128x64_s2"),
 ])
 @pytest.mark.parametrize("fmt", [5, 6, 7])
@@ -179,13 +181,21 @@ def test_mx_plan_selection(M, N, K, want, fmt):
     assert gr.gemm_relu_mx_plan(0, 0, 0, 0, C, 0, N, K, fmt, 0) == "none"
 
 
-@pytest.mark.parametrize("name", ["d256x256x64_s2", "d256x128x64_s2", "d128x128x64_s2"])
+@pytest.mark.parametrize("name", ["d256x256x32_s4_i", "d256x256x64_s2", "d256x128x64_s2",
+                                  "d128x128x64_s2"])
 def test_mx_forced_configuration(monkeypatch, name):
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", name)
     assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 8192, 8192, 8192, 7, 0) == name
     # a configuration not built for block-scaled inputs falls back
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d64x64x64_s4")
+    assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 8192, 8192, 8192, 7, 0) == "d256x256x32_s4_i"
+
+
+@pytest.mark.parametrize("fmt", [5, 7])
+def test_mx_interleaved_needs_16_scale_blocks_per_row(monkeypatch, fmt):
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x256x32_s4_i")
-    assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 8192, 8192, 8192, 7, 0) == "d128x128x64_s2"
+    assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 1024, 1024, 512, fmt, 0) == "d256x256x32_s4_i"
+    assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 1024, 1024, 480, fmt, 0) == "d128x128x64_s2"
 
 
 @pytest.mark.parametrize("in_dtype", [0, 1, 3])

@@ -13,7 +13,15 @@ from tests.helpers import check_close, from_device, fp32_sum_bound, out_tensor, 
 pytestmark = pytest.mark.gpu
 
 FMTS = [wl.MX_E4M3, wl.MX_E5M2, wl.MX_E2M1]
-CONFIGS = ["d256x256x64_s2", "d256x128x64_s2", "d128x128x64_s2"]
+# the interleaved four-stage tile stages scales in LDS by 16 blocks of a row,
+# so it serves K >= 512 only
+INTERLEAVED = "d256x256x32_s4_i"
+CONFIGS = [INTERLEAVED, "d256x256x64_s2", "d256x128x64_s2", "d128x128x64_s2"]
+
+
+def _needs(cfg, K):
+    if cfg == INTERLEAVED and K < 512:
+        pytest.skip("the interleaved tile needs K >= 512 (16 scale blocks per row)")
 
 
 @pytest.fixture(autouse=True)
@@ -60,13 +68,15 @@ def int_mx(M, N, K, fmt, seed, scale_choices=(127,)):
 @pytest.mark.parametrize("cfg", CONFIGS)
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("out_code", [wl.F16, wl.BF16, wl.F32])
-@pytest.mark.parametrize("shape", [(264, 520, 288), (301, 517, 224)], ids=["tail32", "ragged"])
+@pytest.mark.parametrize("shape", [(264, 520, 288), (301, 517, 224), (264, 520, 1120)],
+                         ids=["tail32", "ragged", "long"])
 def test_mx_integer_unit_scales_bitexact(cfg, fmt, out_code, shape, monkeypatch):
     M, N, K = shape
     A, SA, B, SB = int_mx(M, N, K, fmt, 900 + fmt)
     if out_code == wl.BF16:                      # keep |C| inside bf16's exact integers
         A, SA, B, SB = int_mx(M, N, 64, fmt, 901 + fmt)
         K = 64
+    _needs(cfg, K)
     ref = oracle.gemm_relu_mx_ref(A, SA, B, SB, M, N, K, fmt)
     got = run_mx(A, SA, B, SB, M, N, K, fmt, out_code, cfg, monkeypatch)
     assert np.array_equal(got, ref)
@@ -78,11 +88,26 @@ def test_mx_integer_unit_scales_bitexact(cfg, fmt, out_code, shape, monkeypatch)
 def test_mx_scaled_blocks_bitexact(cfg, fmt, monkeypatch):
     """Per-block scales 2^-1, 2^0, 2^1 on integer elements: every sum is exact
     in fp32, so an fp32 C must equal the oracle bit for bit — any block, row or
-    lane-group mix-up of the scales shows."""
-    M, N, K = 200, 330, 480
+    lane-group mix-up of the scales shows.  K spans 17 steps of 64 storage
+    bytes plus a tail, so the four-stage ring runs its steady loop."""
+    M, N, K = 200, 330, 1120
     A, SA, B, SB = int_mx(M, N, K, fmt, 910 + fmt, scale_choices=(126, 127, 128))
     ref = oracle.gemm_relu_mx_ref(A, SA, B, SB, M, N, K, fmt)
     got = run_mx(A, SA, B, SB, M, N, K, fmt, wl.F32, cfg, monkeypatch)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("K", [512, 544, 2016, 4128])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mx_interleaved_scale_groups(K, fmt, monkeypatch):
+    """The interleaved tile's LDS scale groups (16 blocks of a row per group):
+    one group exactly, a tail past it, and rows whose last group is partial
+    and moved back (K / 32 = 63, 129), with per-block scales on integer
+    elements (exact in fp32)."""
+    M, N = 300, 280
+    A, SA, B, SB = int_mx(M, N, K, fmt, 960 + K + fmt, scale_choices=(126, 127, 128))
+    ref = oracle.gemm_relu_mx_ref(A, SA, B, SB, M, N, K, fmt)
+    got = run_mx(A, SA, B, SB, M, N, K, fmt, wl.F32, INTERLEAVED, monkeypatch)
     assert np.array_equal(got, ref)
 
 
@@ -111,6 +136,7 @@ def test_mx_coded_scales(fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_mx_quantized_uniform_tolerance(cfg, fmt, monkeypatch):
     M, N, K = 331, 263, 640
+    _needs(cfg, K)
     A, SA, B, SB = wl.mx_inputs(M, N, K, fmt, 930)
     got = run_mx(A, SA, B, SB, M, N, K, fmt, wl.F16, cfg, monkeypatch)
     rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
