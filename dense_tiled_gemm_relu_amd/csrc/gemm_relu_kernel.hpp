@@ -817,23 +817,26 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
                 }
             }
         };
-        const int sc_lane = (BPS == 2 ? g : 0);
-        const int sc_a = (wm0 + lr) * 16 + sc_lane, sc_b = (BM + wn0 + lr) * 16 + sc_lane;
+        // Reads are whole aligned words; the step's first block is byte sc_sub
+        // of the word, and the lane shifts its byte down at use.  (Rows 16
+        // bytes apart put the 32 rows of a read on 16 bank positions: about 6
+        // conflict cycles per read, ~2% of the LDS's cycles.)
+        const int sc_a = (wm0 + lr) * 16, sc_b = (BM + wn0 + lr) * 16;
         uint32_t scv[2][NSC];
+        int sc_sub[2] = {0, 0};
         auto read_scales = [&](int t, auto set_tag) {
             if constexpr (C::MX_LDS) {
                 constexpr int SET = decltype(set_tag)::value;
                 const int G = t / SGS;
+                const int first = BPS * t - group_off(G);       // byte of the step's first block
                 const GR_LDS unsigned char* reg = smem + S * C::STAGE_BYTES + (G & 1) * C::SC_REGION +
-                                                  (BPS * t - group_off(G));
+                                                  (first & ~3);
+                sc_sub[SET] = first & 3;
 #pragma unroll
                 for (int q = 0; q < NSC; ++q) {
                     const GR_LDS unsigned char* p =
                         reg + (q < TM ? sc_a + 16 * MB * q : sc_b + 16 * MB * (q - TM));
-                    if constexpr (BPS == 2)
-                        scv[SET][q] = *p;
-                    else
-                        scv[SET][q] = *reinterpret_cast<const GR_LDS uint32_t*>(p);
+                    scv[SET][q] = *reinterpret_cast<const GR_LDS uint32_t*>(p);
                 }
             }
         };
@@ -843,15 +846,10 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
             const int j = p / TM, i = p % TM;
             if constexpr (C::MX) {
                 constexpr int SET = decltype(set_tag)::value;
-                int sa_v, sb_v;
-                if constexpr (BPS == 2) {
-                    sa_v = (int)scv[SET][i];
-                    sb_v = (int)scv[SET][TM + j];
-                } else {
-                    const int sh = 16 * s + 8 * g;
-                    sa_v = (int)(scv[SET][i] >> sh);
-                    sb_v = (int)(scv[SET][TM + j] >> sh);
-                }
+                // block 2 s + g of the step (the MFMA reads the low byte)
+                const int sh = 8 * (sc_sub[SET] + 2 * s + g);
+                const int sa_v = (int)(scv[SET][i] >> sh);
+                const int sb_v = (int)(scv[SET][TM + j] >> sh);
                 acc[i][j] = In::mfma_scaled(f.b[j], f.a[i], acc[i][j], sb_v, sa_v);
             } else {
                 acc[i][j] = In::mfma(f.b[j], f.a[i], acc[i][j]);
