@@ -27,7 +27,7 @@ LIB_SOURCES = ["gemm_relu_api.hip", "inst_f16_nn.hip", "inst_f16_nt.hip",
                "inst_bf16_nn.hip", "inst_bf16_nt.hip", "inst_f8e4m3_nn.hip",
                "inst_f8e4m3_nt.hip", "inst_f8e5m2_nn.hip", "inst_f8e5m2_nt.hip",
                "inst_mx_e4m3.hip", "inst_mx_e5m2.hip", "inst_mx_e2m1.hip"]
-PROBE_SOURCES = ["probe_layouts.hip", "probe_mfma_rate.hip", "probe_fp8.hip"]
+PROBE_SOURCES = ["probe_layouts.hip", "probe_mfma_rate.hip", "probe_fp8.hip", "probe_sparse.hip"]
 HEADERS = ["gemm_relu_kernel.hpp", "configs.hpp"]
 
 # gfx950 only.  Packed fp32 ALU ops are switched off: the compiler otherwise

@@ -29,6 +29,14 @@ Block-scaled (MX) products (the MXFP8 / MXFP4 of that page's §4.1 timeline)
 follow the OCP Microscaling definition: ``gemm_relu_mx_ref`` (C) and
 ``gemm_relu_mx_fraction`` (exact rationals, its own E2M1 table) take A (M, K)
 and B stored (N, K) with E8M0 scales per 32 elements along K.
+
+2:4 structured-sparse A (the T.gemm_sp of that page's §4.1 timeline; page
+"从 TVM 到 TileLang…", §四, loads the compressed A and its metadata E side by
+side): ``gemm_relu_sp_ref`` (C) and ``gemm_relu_sp_fraction`` (exact
+rationals, its own metadata reading) decode (As, E) back to the plain A — As
+(M, K/2) holds the two stored values of every group of four along K, E their
+positions as nibbles p0 | p1 << 2, blocked by 64 columns of K (M x 8 bytes per
+block) — and then take the same definition.
 """
 import ctypes
 import os
@@ -88,6 +96,9 @@ def _load():
     lib.oracle_gemm_relu_mx.argtypes = [vp, vp, vp, vp, i64p, i64p, i64, f64p, f64p,
                                         i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.oracle_gemm_relu_mx.restype = ctypes.c_int
+    lib.oracle_gemm_sp_relu.argtypes = [vp, vp, vp, i64p, i64p, i64, f64p, f64p,
+                                        i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.oracle_gemm_sp_relu.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -308,4 +319,76 @@ def gemm_relu_mx_fraction(A, SA, B, SB, M, N, K, fmt, relu=True):
                     s += xa * a[i][k] * xb * b[j][k]
             row.append(max(s, Fraction(0)) if relu else s)
         out.append(row)
+    return out
+
+
+# ------------------------------------------------------- 2:4 sparse A
+def sp_meta_bytes(M, K):
+    """Size of the metadata array E for an (M, K) sparse A: ceil(K / 64)
+    blocks of M x 8 bytes."""
+    return ((K + 63) // 64) * M * 8
+
+
+def _sp_check(As, E, B, M, N, K, dtype, transB):
+    if K % 4 != 0:
+        raise ValueError("K must be a multiple of 4 (whole groups of four)")
+    As = _bits(As, dtype).reshape(-1)
+    B = _bits(B, dtype).reshape(-1)
+    E = np.ascontiguousarray(E, dtype=np.uint8).reshape(-1)
+    if As.size != M * (K // 2) or B.size != K * N or E.size != sp_meta_bytes(M, K):
+        raise ValueError("operand sizes do not match (M, N, K)")
+    return As, E, B
+
+
+def gemm_relu_sp_ref(As, E, B, M, N, K, dtype, transB=0, relu=True, rows=None, cols=None):
+    """max(A·op(B), 0) in binary64 for a 2:4 sparse A given as (As, E): the
+    full (M, N) product, or (values, absum) at positions (rows[t], cols[t])."""
+    lib = _load()
+    As, E, B = _sp_check(As, E, B, M, N, K, dtype, transB)
+    if rows is None:
+        out = np.empty((M, N), dtype=np.float64)
+        rc = lib.oracle_gemm_sp_relu(_vptr(As), _vptr(E), _vptr(B), None, None, 0,
+                                     _ptr(out, ctypes.c_double), None, M, N, K, dtype, transB,
+                                     1 if relu else 0)
+        if rc != 0:
+            raise ValueError("oracle_gemm_sp_relu failed (%d)" % rc)
+        return out
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    out = np.empty(rows.shape, dtype=np.float64)
+    absum = np.empty(rows.shape, dtype=np.float64)
+    rc = lib.oracle_gemm_sp_relu(_vptr(As), _vptr(E), _vptr(B), _ptr(rows, ctypes.c_int64),
+                                 _ptr(cols, ctypes.c_int64), rows.size,
+                                 _ptr(out, ctypes.c_double), _ptr(absum, ctypes.c_double),
+                                 M, N, K, dtype, transB, 1 if relu else 0)
+    if rc != 0:
+        raise ValueError("oracle_gemm_sp_relu failed (%d)" % rc)
+    return out, absum
+
+
+def gemm_relu_sp_fraction(As, E, B, M, N, K, dtype, transB=0, relu=True):
+    """Exact rational sparse product (tiny shapes): the metadata read with
+    Python integer operations, the values decoded as in gemm_relu_fraction."""
+    As = _bits(As, dtype).reshape(M, K // 2)
+    E = np.ascontiguousarray(E, dtype=np.uint8).reshape(-1)
+    Bv = _exact(_bits(B, dtype).reshape(-1), dtype)
+    out = []
+    for i in range(M):
+        row = [Fraction(0)] * K
+        vals = _exact(As[i], dtype)
+        for q in range(K // 4):
+            byte = int(E[(q // 16) * M * 8 + i * 8 + (q % 16) // 2])
+            nib = (byte >> 4) if q % 2 else (byte & 15)
+            p0, p1 = nib & 3, nib >> 2
+            if p0 >= p1:
+                raise ValueError("metadata nibble with p0 >= p1")
+            row[4 * q + p0] = vals[2 * q]
+            row[4 * q + p1] = vals[2 * q + 1]
+        r = []
+        for j in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += row[k] * Bv[j * K + k if transB else k * N + j]
+            r.append(max(acc, Fraction(0)) if relu else acc)
+        out.append(r)
     return out

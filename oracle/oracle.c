@@ -39,6 +39,19 @@
  * with 4-bit E2M1 elements packed two to a byte, element k of a row in the
  * low nibble of byte k/2 when k is even and in the high nibble when odd.
  *
+ * 2:4 structured-sparse A — the "2:4 structured-sparse tensor core (T.gemm_sp)"
+ * of that page's §4.1 timeline, whose A arrives compressed together with its
+ * metadata E (page "从 TVM 到 TileLang…", §四) — is decoded back to the plain
+ * matrix first, then the same definition applies.  The pages fix no format;
+ * the one read here: every row of A is cut along K into groups of 4, each
+ * holding its (at most) two non-zeros; As (M, K/2) keeps them, As[i][2q] and
+ * As[i][2q+1] for group q, and E gives their positions p0 < p1 inside the
+ * group as the nibble p0 | p1 << 2.  E is blocked by 64 columns of K: block
+ * kb = q / 16 holds 8 bytes per row (M x 8 bytes), and group q of row i is
+ * nibble q % 2 (low nibble first) of byte (q % 16) / 2 of row i's 8 bytes.
+ * So a(i, 4q + p0) = As[i][2q], a(i, 4q + p1) = As[i][2q+1], and the other
+ * two elements of the group are zero.
+ *
  * Readings where the pages are silent (listed with the others in the design
  * notes): a negative sum maps to +0.0; K = 0 gives an empty sum, so every
  * output is +0.0; M = 0 or N = 0 is a no-op.
@@ -320,4 +333,63 @@ int oracle_gemm_relu_mx(const void* A, const void* SA, const void* B, const void
         if (absum) absum[t] = sa;
     }
     return 0;
+}
+
+/*
+ * 2:4 structured-sparse product, A given as (As, E) (format in the header
+ * comment), B dense (K, N) or stored (N, K) when transB = 1, at n positions
+ * (rows[t], cols[t]), or the full (M, N) product when rows == NULL.  K must be
+ * a multiple of 4.  Row i of A is first decoded to its K plain values, then
+ * the definition's sum is taken.  Returns 0, -1 on bad arguments, -3 when a
+ * metadata nibble used has p0 >= p1.
+ */
+int oracle_gemm_sp_relu(const void* As, const void* E, const void* B,
+                        const int64_t* rows, const int64_t* cols, int64_t n,
+                        double* out, double* absum, int64_t M, int64_t N, int64_t K,
+                        int dtype, int transB, int relu)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 4 != 0) return -1;
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    if (transB != 0 && transB != 1) return -1;
+    if (!out || (K > 0 && M > 0 && (!As || !E)) || (K > 0 && N > 0 && !B)) return -1;
+    const int64_t total = rows ? n : M * N;
+    if (rows)
+        for (int64_t t = 0; t < n; ++t)
+            if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N) return -1;
+    const uint8_t* e = (const uint8_t*)E;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* a = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+        int64_t cur = -1;             /* row decoded into a[] */
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < total; ++t) {
+            const int64_t i = rows ? rows[t] : t / N, j = rows ? cols[t] : t % N;
+            if (i != cur) {
+                for (int64_t k = 0; k < K; ++k) a[k] = 0.0;
+                for (int64_t q = 0; q < K / 4; ++q) {
+                    const uint8_t byte = e[((q / 16) * M + i) * 8 + (q % 16) / 2];
+                    const int nib = (q % 2) ? (byte >> 4) : (byte & 0xf);
+                    const int p0 = nib & 3, p1 = nib >> 2;
+                    if (p0 >= p1) {
+#pragma omp atomic write
+                        bad = 1;
+                    }
+                    a[4 * q + p0] = dec_at(As, i * (K / 2) + 2 * q, dtype);
+                    a[4 * q + p1] = dec_at(As, i * (K / 2) + 2 * q + 1, dtype);
+                }
+                cur = i;
+            }
+            double s = 0.0, sa = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double p = a[k] * dec_at(B, b_index(k, j, N, K, transB), dtype);
+                s += p;
+                sa += fabs(p);
+            }
+            out[t] = relu ? (s > 0.0 ? s : 0.0) : s;
+            if (absum) absum[t] = sa;
+        }
+        free(a);
+    }
+    return bad ? -3 : 0;
 }

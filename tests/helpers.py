@@ -11,7 +11,7 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 def read_golden(name):
     """Parse a tests/golden fixture into a dict with A, B, C as Fraction lists."""
     path = os.path.join(GOLDEN, name)
-    meta, blocks, cur = {}, {"A": [], "B": [], "C": []}, None
+    meta, blocks, cur = {}, {"A": [], "B": [], "C": [], "AS": [], "E": []}, None
     with open(path) as f:
         for raw in f:
             line = raw.strip()

@@ -472,3 +472,100 @@ def test_mx_rejects_partial_blocks():
     with pytest.raises(ValueError):
         oracle.gemm_relu_mx_ref(np.zeros(40, np.uint8), np.zeros(2, np.uint8),
                                 np.zeros(40, np.uint8), np.zeros(2, np.uint8), 1, 1, 40, MX_E4M3)
+
+
+# ------------------------------------------------------- 2:4 sparse A (NEXT)
+# The sparse product of the T.gemm_sp item (page "TileLang：GPU/NPU 通用算子
+# DSL", §4.1 timeline; page "从 TVM 到 TileLang…", §四: A compressed with its
+# metadata E): (As, E) decode to a plain A, then the same definition.
+def test_sp_golden_handworked():
+    g = read_golden("handworked_sp_f16_2x2x8.txt")
+    M, N, K = g["M"], g["N"], g["K"]
+    As = enc([float(x) for r in g["AS"] for x in r], F16)
+    E = np.array([int(x) for r in g["E"] for x in r], dtype=np.uint8)
+    B = enc([float(x) for r in g["B"] for x in r], F16)
+    C = oracle.gemm_relu_sp_ref(As, E, B, M, N, K, F16, g["transB"])
+    assert [[Fraction(float(v)) for v in row] for row in C] == g["C"]
+    assert oracle.gemm_relu_sp_fraction(As, E, B, M, N, K, F16, g["transB"]) == g["C"]
+
+
+def test_sp_metadata_blocks_by_hand():
+    """E blocked by 64 columns of K, built byte by byte: row 1's group 17 (block
+    1, byte 0, high nibble) keeps positions 2, 3; everything else keeps 0, 1."""
+    M, N, K = 2, 1, 128
+    E = np.full(2 * M * 8, 0x44, dtype=np.uint8)       # nibble 4 = positions 0, 1
+    E[1 * M * 8 + 1 * 8 + 0] = 0x4 | (0xE << 4)         # row 1, group 17 -> (2, 3)
+    As = enc(np.ones(M * K // 2), F16)
+    b = np.zeros(K)
+    b[4 * 17 + 2] = 1.0
+    b[4 * 17 + 3] = 10.0
+    B = enc(b, F16)
+    C = oracle.gemm_relu_sp_ref(As, E, B, M, N, K, F16, 0)
+    assert C.tolist() == [[0.0], [11.0]]
+    # the same byte in block 0 is row 1's groups 0 and 1
+    E2 = np.full(2 * M * 8, 0x44, dtype=np.uint8)
+    E2[1 * 8 + 0] = 0x4 | (0xE << 4)
+    b2 = np.zeros(K)
+    b2[4 + 2] = 1.0
+    B2 = enc(b2, F16)
+    assert oracle.gemm_relu_sp_ref(As, E2, B2, M, N, K, F16, 0).tolist() == [[0.0], [1.0]]
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("transB", [0, 1])
+@pytest.mark.parametrize("M,N,K", [(3, 5, 4), (7, 6, 64), (5, 9, 68), (4, 3, 200)])
+def test_sp_equals_dense_product_of_its_decompression(dtype, transB, M, N, K):
+    """A random 2:4 matrix given compressed equals the dense oracle on the plain
+    matrix it encodes (integer values: both sums exact)."""
+    rng = np.random.default_rng(1000 + M * N + K)
+    vals, positions, dense = wl.sp_random(M, K, rng, int_values=True)
+    b = rng.integers(-3, 4, size=wl.b_shape(M, N, K, transB)).astype(np.float64)
+    As, E, B = enc(vals, dtype), wl.sp_pack(positions, M, K), enc(b, dtype)
+    got = oracle.gemm_relu_sp_ref(As, E, B, M, N, K, dtype, transB)
+    want = oracle.gemm_relu_ref(enc(dense, dtype), B, M, N, K, dtype, transB)
+    assert np.array_equal(got, want)
+    # at chosen positions too, with the absolute-value sum
+    rows, cols = np.array([0, M - 1]), np.array([N - 1, 0])
+    at, absum = oracle.gemm_relu_sp_ref(As, E, B, M, N, K, dtype, transB, rows=rows, cols=cols)
+    assert np.array_equal(at, want[rows, cols])
+    bmat = b if not transB else b.T
+    assert np.array_equal(absum, np.abs(dense[rows] * bmat[:, cols].T).sum(axis=1))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 4), (2, 3, 8), (3, 2, 68)])
+@pytest.mark.parametrize("transB", [0, 1])
+def test_sp_fraction_bruteforce(M, N, K, transB):
+    rng = np.random.default_rng(2000 + M + N + K)
+    vals, positions, _ = wl.sp_random(M, K, rng)
+    b = rng.uniform(-1, 1, size=wl.b_shape(M, N, K, transB))
+    As, E, B = enc(vals, F16), wl.sp_pack(positions, M, K), enc(b, F16)
+    got = oracle.gemm_relu_sp_ref(As, E, B, M, N, K, F16, transB)
+    exact = oracle.gemm_relu_sp_fraction(As, E, B, M, N, K, F16, transB)
+    # each product of two fp16 values is exact in binary64; K / 2 terms
+    for i in range(M):
+        for j in range(N):
+            assert abs(Fraction(float(got[i][j])) - exact[i][j]) <= Fraction(K, 2 ** 40)
+
+
+def test_sp_position_sum_closed_form():
+    """All stored values 1 and b(k, 0) = k: C[i][0] = sum_q (8 q + p0 + p1)."""
+    M, K = 6, 136
+    rng = np.random.default_rng(31)
+    _, positions, _ = wl.sp_random(M, K, rng)
+    As = enc(np.ones((M, K // 2)), F16)
+    B = enc(np.arange(K, dtype=np.float64).reshape(K, 1), F16)
+    C = oracle.gemm_relu_sp_ref(As, wl.sp_pack(positions, M, K), B, M, 1, K, F16, 0)
+    q = np.arange(K // 4)
+    want = (8 * q[None, :] + positions[..., 0] + positions[..., 1]).sum(axis=1)
+    assert np.array_equal(C[:, 0], want.astype(np.float64))
+
+
+def test_sp_rejects_bad_metadata_and_partial_groups():
+    M, N, K = 1, 1, 8
+    As, B = enc(np.ones(4), F16), enc(np.ones(8), F16)
+    E = np.zeros(8, np.uint8)
+    E[0] = 0x4 | (0x5 << 4)                  # group 1: p0 = 1, p1 = 1
+    with pytest.raises(ValueError):
+        oracle.gemm_relu_sp_ref(As, E, B, M, N, K, F16, 0)
+    with pytest.raises(ValueError):
+        oracle.gemm_relu_sp_ref(As, np.zeros(8, np.uint8), B, M, N, 6, F16, 0)

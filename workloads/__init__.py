@@ -197,3 +197,57 @@ def mx_inputs(M, N, K, fmt, index, dist="uniform", int_values=False):
     qa, xa = mx_quantize(a, fmt)
     qb, xb = mx_quantize(b, fmt)
     return qa, xa, qb, xb
+
+
+# ------------------------------------------------------- 2:4 sparse A
+# The six position pairs (p0 < p1) a group of four can keep.
+SP_PAIRS = [(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)]
+
+
+def sp_meta_bytes(M, K):
+    """Bytes of the metadata E of an (M, K) sparse A: ceil(K/64) blocks of M x 8."""
+    return ((K + 63) // 64) * M * 8
+
+
+def sp_pack(positions, M, K):
+    """positions: (M, K/4, 2) int array of (p0, p1) per group -> E bytes
+    (blocked by 64 columns of K; group q of row i in nibble q % 2 of byte
+    (q % 16) / 2 of row i's 8 bytes in block q / 16; nibble = p0 | p1 << 2)."""
+    E = np.zeros(sp_meta_bytes(M, K), dtype=np.uint8)
+    pos = np.asarray(positions, dtype=np.int64)
+    nib = (pos[..., 0] | (pos[..., 1] << 2)).astype(np.uint8)        # (M, K/4)
+    for q in range(K // 4):
+        idx = (q // 16) * M * 8 + np.arange(M) * 8 + (q % 16) // 2
+        E[idx] |= (nib[:, q] << (4 * (q % 2))).astype(np.uint8)
+    return E
+
+
+def sp_random(M, K, rng, int_values=False):
+    """A random 2:4 sparse (M, K) matrix: per group of four, a uniformly chosen
+    position pair; values uniform[-1, 1] (or integers in [-3, 3]) in binary64.
+    Returns (values (M, K/2), positions (M, K/4, 2), dense (M, K))."""
+    choice = rng.integers(0, len(SP_PAIRS), size=(M, K // 4))
+    positions = np.asarray(SP_PAIRS, dtype=np.int64)[choice]
+    if int_values:
+        vals = rng.integers(-3, 4, size=(M, K // 2)).astype(np.float64)
+    else:
+        vals = rng.uniform(-1.0, 1.0, size=(M, K // 2))
+    dense = np.zeros((M, K))
+    rows = np.arange(M)[:, None]
+    groups = np.arange(K // 4)[None, :]
+    dense[rows, 4 * groups + positions[..., 0]] = vals[:, 0::2]
+    dense[rows, 4 * groups + positions[..., 1]] = vals[:, 1::2]
+    return vals, positions, dense
+
+
+def sp_inputs(M, N, K, in_dtype, transB, index, int_values=False):
+    """(As, E, B) storage for a 2:4 sparse A (values rounded to the input type
+    after the draw) and a dense B of the layout transB."""
+    sa, sb = seeds(index)
+    ra, rb = np.random.default_rng(sa), np.random.default_rng(sb)
+    vals, positions, _ = sp_random(M, K, ra, int_values)
+    if int_values:
+        b = rb.integers(-3, 4, size=b_shape(M, N, K, transB)).astype(np.float64)
+    else:
+        b = rb.uniform(-1.0, 1.0, size=b_shape(M, N, K, transB))
+    return encode(vals, in_dtype), sp_pack(positions, M, K), encode(b, in_dtype)
