@@ -160,7 +160,33 @@ def cpu_baseline_mx(w, target_s=15.0):
                       "workload, binary64), %.2f s wall" % (R - 1, R, N, K, w["name"], dt)}
 
 
-def peak_tflops(in_dtype):
+def cpu_baseline_sp(w, target_s=15.0):
+    """The 2:4 sparse oracle on the first R rows of A against all of B
+    (dense-equivalent flops, as the GPU figure)."""
+    import oracle
+    M, N, K, ic, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["transB"]
+    As, E, B = wl.sp_inputs(M, N, K, ic, tb, w["index"])
+    R = 1
+    for _ in range(6):
+        rows = np.repeat(np.arange(R), N)
+        cols = np.tile(np.arange(N), R)
+        t = time.perf_counter()
+        oracle.gemm_relu_sp_ref(As, E, B, M, N, K, ic, tb, rows=rows, cols=cols)
+        dt = time.perf_counter() - t
+        if dt >= 0.6 * target_s or R >= M:
+            break
+        R = int(min(M, max(R + 1, R * target_s / max(dt, 1e-3))))
+    flops = 2.0 * R * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count())),
+            "kind": "oracle",
+            "sample": "rows 0..%d of A (%d x %d x %d dense-equivalent multiply-adds of the %s "
+                      "workload, binary64), %.2f s wall" % (R - 1, R, N, K, w["name"], dt)}
+
+
+def peak_tflops(in_dtype, sparse=False):
+    if sparse:
+        return PEAK_TFLOPS_F16_SPARSE
     if in_dtype == wl.MX_E2M1:
         return PEAK_TFLOPS_F4
     if in_dtype in wl.FP8 or in_dtype in (wl.MX_E4M3, wl.MX_E5M2):
@@ -168,9 +194,14 @@ def peak_tflops(in_dtype):
     return PEAK_TFLOPS_F16
 
 
-def ceiling_kind(in_dtype):
+PEAK_TFLOPS_F16_SPARSE = 2 * PEAK_TFLOPS_F16   # 2:4 sparse fp16/bf16, dense-equivalent flops
+
+
+def ceiling_kind(in_dtype, sparse=False):
     """probe_mfma_rate kind matching an input type: 0 fp16, 1 E4M3, 2 E2M1
-    (scaled MFMA), 3 E4M3 on the scaled MFMA."""
+    (scaled MFMA), 3 E4M3 on the scaled MFMA, 4 the 2:4 sparse fp16 form."""
+    if sparse:
+        return 4
     if in_dtype == wl.MX_E2M1:
         return 2
     if in_dtype in (wl.MX_E4M3, wl.MX_E5M2):
@@ -195,6 +226,17 @@ def workload_call(gr, name, stream):
         plan = gr.gemm_relu_mx_plan(Ad, SAd, Bd, SBd, Cd, M, N, K, ic, oc)
         nbytes = sum(int(x.size) for x in arrs) + M * N * wl.elem_bytes(oc)
         return call, Cd, plan, nbytes, (Ad, SAd, Bd, SBd)
+    if w.get("sparse"):
+        As, E, B = wl.sp_inputs(M, N, K, ic, tb, w["index"])
+        Ad = to_device(As, ic, (M, K // 2))
+        Ed = torch.from_numpy(E).cuda()
+        Bd = to_device(B, ic, wl.b_shape(M, N, K, tb))
+
+        def call():
+            gr.gemm_relu_sp(Ad, Ed, Bd, Cd, M, N, K, ic, oc, tb, stream)
+        plan = gr.gemm_relu_sp_plan(Ad, Ed, Bd, Cd, M, N, K, ic, oc, tb)
+        nbytes = 2 * (M * K // 2 + K * N) + E.size + M * N * wl.elem_bytes(oc)
+        return call, Cd, plan, nbytes, (Ad, Ed, Bd)
     A, B = wl.workload_inputs(name)
     Ad = to_device(A, ic, (M, K))
     Bd = to_device(B, ic, wl.b_shape(M, N, K, tb))
@@ -225,7 +267,8 @@ def mfma_ceiling(gr, stream, blocks=1024, steps=2048, kind=0):
     library's probe_mfma_rate: 4 waves per CU, each streaming the 32 MFMAs of
     one step of a 128x128 wave tile; kind 0: fp16 32x32x16, 1: E4M3 32x32x64,
     2: E2M1 32x32x64 on the scaled MFMA with unit scales, 3: E4M3 on the scaled
-    MFMA).  The chip is
+    MFMA, 4: the 2:4 sparse fp16 32x32x32 form, counted at its dense-equivalent
+    flops).  The chip is
     power-limited, so this, not 2.4 GHz x the instruction rate, is what the
     contraction step alone can reach on this machine now.  None if the probe
     library is not built."""
@@ -240,7 +283,7 @@ def mfma_ceiling(gr, stream, blocks=1024, steps=2048, kind=0):
     if kind == 2:                               # random E2M1 nibbles, 16 bytes per lane
         src = torch.randint(0, 256, (blocks * 8 * 256 * 16,), dtype=torch.uint8, device="cuda")
     else:
-        per_lane = 32 if kind in (1, 3) else 8  # operand elements per lane (32 bytes / 16 bytes)
+        per_lane = {1: 32, 3: 32, 4: 16}.get(kind, 8)   # operand elements per lane
         src = torch.empty(blocks * 8 * 256 * per_lane, dtype=torch.float32, device="cuda")
         src = src.uniform_(-1, 1).to(torch.float8_e4m3fn if kind in (1, 3) else torch.float16)
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
@@ -264,11 +307,12 @@ def mfma_ceiling(gr, stream, blocks=1024, steps=2048, kind=0):
     t = ticks.view(blocks, 2).double()
     cycles = t[:, 0].mean().item()
     clock_mhz = (t[:, 0] / t[:, 1]).mean().item() * 100.0
-    flops = blocks * 4 * steps * 32 * (32 * 32 * (16 if kind == 0 else 64) * 2)
+    flops = blocks * 4 * steps * 32 * (32 * 32 * {0: 16, 4: 32}.get(kind, 64) * 2)
     return {"tflops": round(flops / sec / 1e12, 1), "clock_mhz": round(clock_mhz),
             "cycles_per_mfma": round(cycles / (steps * 32), 2),
             "kind": "MFMA-only, random %s operands, no memory traffic (probe_mfma_rate)"
-                    % ("fp16", "E4M3", "E2M1 (unit block scales)", "E4M3 (unit block scales)")[kind]}
+                    % ("fp16", "E4M3", "E2M1 (unit block scales)", "E4M3 (unit block scales)",
+                       "fp16, 2:4 sparse (dense-equivalent flops)")[kind]}
 
 
 def table(gr):
@@ -280,16 +324,17 @@ def table(gr):
     import torch
     stream = torch.cuda.current_stream()
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
-    ceilings = {k: mfma_ceiling(gr, stream, kind=k) for k in (0, 1, 2, 3)}
+    ceilings = {k: mfma_ceiling(gr, stream, kind=k) for k in (0, 1, 2, 3, 4)}
     print(json.dumps({"mfma_ceiling": ceilings[0], "mfma_ceiling_fp8": ceilings[1],
-                      "mfma_ceiling_mxfp4": ceilings[2], "mfma_ceiling_mxfp8": ceilings[3]}),
+                      "mfma_ceiling_mxfp4": ceilings[2], "mfma_ceiling_mxfp8": ceilings[3],
+                      "mfma_ceiling_sparse_f16": ceilings[4]}),
           flush=True)
     for name in sorted(wl.WORKLOADS, key=lambda n: wl.WORKLOADS[n]["index"]):
         w = wl.WORKLOADS[name]
         M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
         call, Cd, plan, nbytes, keep = workload_call(gr, name, stream)
-        ceiling = ceilings[ceiling_kind(ic)]
-        peak = peak_tflops(ic)
+        ceiling = ceilings[ceiling_kind(ic, w.get("sparse", False))]
+        peak = peak_tflops(ic, w.get("sparse", False))
 
         for _ in range(10):
             call()
@@ -376,7 +421,8 @@ def main():
     M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
     stream = torch.cuda.current_stream()
     step, Cd, plan, nbytes, keep = workload_call(gr, args.workload, stream)
-    peak = peak_tflops(ic)
+    sparse = w.get("sparse", False)
+    peak = peak_tflops(ic, sparse)
 
     for _ in range(args.warmup):
         step()
@@ -402,7 +448,8 @@ def main():
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     metric = METRIC if args.workload == "gemm_relu_f16_8192" else (
         "TFLOP/s and %% of MI355X %s MFMA peak, %s" %
-        ({PEAK_TFLOPS_F4: "fp4", PEAK_TFLOPS_F8: "fp8"}.get(peak_tflops(ic), "fp16/bf16"),
+        ({PEAK_TFLOPS_F4: "fp4", PEAK_TFLOPS_F8: "fp8",
+          PEAK_TFLOPS_F16_SPARSE: "2:4 sparse fp16/bf16 (dense-equivalent)"}.get(peak, "fp16/bf16"),
          args.workload))
     out = {
         "metric": metric,
@@ -427,12 +474,14 @@ def main():
                      "algorithmic_bytes": int(nbytes),
                      "kernel_ms": round(kernel_ms, 5)},
     }
-    ceiling = mfma_ceiling(gr, stream, kind=ceiling_kind(ic))
+    ceiling = mfma_ceiling(gr, stream, kind=ceiling_kind(ic, sparse))
     if ceiling is not None:
         out["mfma_ceiling"] = dict(ceiling, frac=round(achieved / ceiling["tflops"], 4))
     if not args.no_cpu_baseline:
         if w.get("mx"):
             out["cpu_baseline"] = cpu_baseline_mx(w)
+        elif w.get("sparse"):
+            out["cpu_baseline"] = cpu_baseline_sp(w)
         else:
             A, B = wl.workload_inputs(args.workload)
             out["cpu_baseline"] = cpu_baseline(w, A, B)

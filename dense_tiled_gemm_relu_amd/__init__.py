@@ -31,7 +31,7 @@ LIB_PATH = os.path.join(_PKG, "libgemm_relu.so")
 PROBE_LIB_PATH = os.path.join(_PKG, "libgemm_relu_probe.so")
 
 EXPORTS = ("gemm_relu", "gemm_relu_strerror", "gemm_relu_plan", "gemm_relu_mx",
-           "gemm_relu_mx_plan")
+           "gemm_relu_mx_plan", "gemm_relu_sp", "gemm_relu_sp_plan")
 
 _lib = None
 
@@ -65,6 +65,12 @@ def library():
     lib.gemm_relu_mx_plan.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int,
                                       ctypes.c_int]
     lib.gemm_relu_mx_plan.restype = ctypes.c_char_p
+    lib.gemm_relu_sp.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, vp]
+    lib.gemm_relu_sp.restype = ctypes.c_int
+    lib.gemm_relu_sp_plan.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int]
+    lib.gemm_relu_sp_plan.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -133,6 +139,28 @@ def gemm_relu_mx(A, SA, B, SB, C, M, N, K, fmt, out_dtype, stream=None):
 def gemm_relu_mx_plan(A, SA, B, SB, C, M, N, K, fmt, out_dtype):
     r = library().gemm_relu_mx_plan(_addr(A), _addr(SA), _addr(B), _addr(SB), _addr(C), int(M),
                                     int(N), int(K), int(fmt), int(out_dtype))
+    return None if r is None else r.decode()
+
+
+def gemm_relu_sp_status(As, E, B, C, M, N, K, in_dtype, out_dtype, transB, stream=None):
+    """Call the 2:4 sparse C-ABI entry and return its status code."""
+    return library().gemm_relu_sp(_addr(As), _addr(E), _addr(B), _addr(C), int(M), int(N),
+                                  int(K), int(in_dtype), int(out_dtype), int(transB),
+                                  _stream_handle(stream))
+
+
+def gemm_relu_sp(As, E, B, C, M, N, K, in_dtype, out_dtype, transB, stream=None):
+    """C = max(A·op(B), 0) for a 2:4 sparse A given compressed: As (M, K/2)
+    stored values and E metadata (blocked by 64 columns of K); raises
+    GemmReluError."""
+    rc = gemm_relu_sp_status(As, E, B, C, M, N, K, in_dtype, out_dtype, transB, stream)
+    if rc != OK:
+        raise GemmReluError(rc, gemm_relu_strerror(rc))
+
+
+def gemm_relu_sp_plan(As, E, B, C, M, N, K, in_dtype, out_dtype, transB):
+    r = library().gemm_relu_sp_plan(_addr(As), _addr(E), _addr(B), _addr(C), int(M), int(N),
+                                    int(K), int(in_dtype), int(out_dtype), int(transB))
     return None if r is None else r.decode()
 
 

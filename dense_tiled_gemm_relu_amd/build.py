@@ -26,15 +26,22 @@ PROBE_LIB = os.path.join(PKG, "libgemm_relu_probe.so")
 LIB_SOURCES = ["gemm_relu_api.hip", "inst_f16_nn.hip", "inst_f16_nt.hip",
                "inst_bf16_nn.hip", "inst_bf16_nt.hip", "inst_f8e4m3_nn.hip",
                "inst_f8e4m3_nt.hip", "inst_f8e5m2_nn.hip", "inst_f8e5m2_nt.hip",
-               "inst_mx_e4m3.hip", "inst_mx_e5m2.hip", "inst_mx_e2m1.hip"]
+               "inst_mx_e4m3.hip", "inst_mx_e5m2.hip", "inst_mx_e2m1.hip", "inst_sp.hip"]
 PROBE_SOURCES = ["probe_layouts.hip", "probe_mfma_rate.hip", "probe_fp8.hip", "probe_sparse.hip"]
-HEADERS = ["gemm_relu_kernel.hpp", "configs.hpp"]
+HEADERS = ["gemm_relu_kernel.hpp", "configs.hpp", "gemm_sp_relu_kernel.hpp"]
 
 # gfx950 only.  Packed fp32 ALU ops are switched off: the compiler otherwise
 # forms v_pk_* fp32 instructions from ordinary float code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
+
+
+# Per-source extra flags.  The sparse kernel's accumulators: by default the
+# compiler splits them between VGPRs and AGPRs for v_smfmac and spills the
+# copy offsets, whose reloads drain the copy pipeline every step; the VGPR
+# form of the matrix instructions leaves the main loop spill-free.
+EXTRA_FLAGS = {"inst_sp.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _newer(target, deps):
@@ -49,7 +56,7 @@ def _compile(src, force, verbose):
     deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, h) for h in HEADERS] + \
         [os.path.join(INCLUDE, "gemm_relu.h")]
     if force or _newer(obj, deps):
-        cmd = [HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + HIP_FLAGS + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -15,8 +15,14 @@
 
 #include "configs.hpp"
 #include "gemm_relu.h"
+#include "gemm_sp_relu_kernel.hpp"
 
 using namespace gemm_relu_hip;
+
+namespace gemm_relu_hip {
+typedef hipError_t (*SpLaunchFn)(const SpArgs& args, int grid, hipStream_t stream);
+SpLaunchFn launcher_sp(int in_dt, int out_dt, int transB);   // inst_sp.hip
+}
 
 namespace {
 
@@ -259,6 +265,59 @@ Plan make_plan_mx(const void* A, const void* SA, const void* B, const void* SB, 
     return p;
 }
 
+// ---- 2:4 sparse A
+constexpr const char* kSpConfigName = "sp256x256x64_s3";
+constexpr int kSpTile = 256;
+
+Plan make_plan_sp(const void* As, const void* E, const void* B, const void* C, int64_t M,
+                  int64_t N, int64_t K, int in_dt, int out_dt, int transB)
+{
+    Plan p;
+    const int64_t lim = INT32_MAX;
+    if (M < 0 || N < 0 || K < 0 || M > lim || N > lim || K > lim || K % 4 != 0 ||
+        (in_dt != GEMM_RELU_F16 && in_dt != GEMM_RELU_BF16) ||
+        (out_dt != GEMM_RELU_F16 && out_dt != GEMM_RELU_BF16 && out_dt != GEMM_RELU_F32) ||
+        (transB != 0 && transB != 1)) {
+        p.status = GEMM_RELU_EINVAL;
+        return p;
+    }
+    if (M == 0 || N == 0) {
+        p.empty = true;
+        return p;
+    }
+    const uint64_t as_bytes = uint64_t(M) * uint64_t(K / 2) * 2;
+    const uint64_t e_bytes = uint64_t((K + 63) / 64) * uint64_t(M) * 8;
+    const uint64_t b_bytes = uint64_t(K) * uint64_t(N) * 2;
+    const uint64_t c_bytes = uint64_t(M) * uint64_t(N) * uint64_t(elem_bytes(out_dt));
+    const uintptr_t ua = reinterpret_cast<uintptr_t>(As), ub = reinterpret_cast<uintptr_t>(B);
+    const uintptr_t uc = reinterpret_cast<uintptr_t>(C), ue = reinterpret_cast<uintptr_t>(E);
+    if ((as_bytes && (!As || !E)) || (b_bytes && !B) || !C || (ua & 1) || (ub & 1) ||
+        (uc & uintptr_t(elem_bytes(out_dt) - 1))) {
+        p.status = GEMM_RELU_EINVAL;
+        return p;
+    }
+    if (overlaps(uc, c_bytes, ua, as_bytes) || overlaps(uc, c_bytes, ue, e_bytes) ||
+        overlaps(uc, c_bytes, ub, b_bytes)) {
+        p.status = GEMM_RELU_EINVAL;
+        return p;
+    }
+    // 32-bit copy offsets (a tile's rows span 256 * K * 2 bytes, a (K,N) B step
+    // 64 * N * 2), and a (K,N) B needs one full tile of columns
+    if (K > (int64_t(1) << 22) || N > (int64_t(1) << 24) || (!transB && N < kSpTile)) {
+        p.status = GEMM_RELU_EUNSUPPORTED;
+        return p;
+    }
+    const int64_t tm = ceil_div(M, kSpTile), tn = ceil_div(N, kSpTile);
+    if (tm * tn > lim) {
+        p.status = GEMM_RELU_EUNSUPPORTED;
+        return p;
+    }
+    p.cfg = 0;
+    p.tiles_m = int(tm);
+    p.tiles_n = int(tn);
+    return p;
+}
+
 LaunchFn pick_launcher_mx(int fmt, int out_dt, int cfg)
 {
     switch (fmt) {
@@ -389,4 +448,51 @@ extern "C" const char* gemm_relu_mx_plan(const void* A, const void* SA, const vo
     if (p.status != GEMM_RELU_OK) return "unsupported";
     if (p.empty) return "none";
     return config_info(p.cfg).name;
+}
+
+extern "C" int gemm_relu_sp(const void* As, const void* E, const void* B, void* C, int64_t M,
+                            int64_t N, int64_t K, int in_dtype, int out_dtype, int transB,
+                            void* stream)
+{
+    const Env e = env();
+    const Plan p = make_plan_sp(As, E, B, C, M, N, K, in_dtype, out_dtype, transB);
+    if (p.status != GEMM_RELU_OK) return p.status;
+    if (p.empty) return GEMM_RELU_OK;
+    const int dev = check_device();
+    if (dev != GEMM_RELU_OK) return dev;
+
+    SpArgs args;
+    args.As = static_cast<const unsigned char*>(As);
+    args.E = static_cast<const unsigned char*>(E);
+    args.B = static_cast<const unsigned char*>(B);
+    args.C = static_cast<unsigned char*>(C);
+    args.M = int(M);
+    args.N = int(N);
+    args.K = int(K);
+    args.tiles_m = p.tiles_m;
+    args.tiles_n = p.tiles_n;
+    const int panel = e.panel > 0 ? e.panel : 8;
+    args.panel = panel < p.tiles_m ? panel : p.tiles_m;
+    args.nxcd = e.nxcd;
+
+    SpLaunchFn fn = launcher_sp(in_dtype, out_dtype, transB);
+    if (!fn) return GEMM_RELU_EUNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (fn(args, p.tiles_m * p.tiles_n, st) != hipSuccess) return GEMM_RELU_EHIP;
+    if (e.sync) {
+        if (hipStreamSynchronize(st) != hipSuccess) return GEMM_RELU_EHIP;
+        if (hipGetLastError() != hipSuccess) return GEMM_RELU_EHIP;
+    }
+    return GEMM_RELU_OK;
+}
+
+extern "C" const char* gemm_relu_sp_plan(const void* As, const void* E, const void* B,
+                                         const void* C, int64_t M, int64_t N, int64_t K,
+                                         int in_dtype, int out_dtype, int transB)
+{
+    const Plan p = make_plan_sp(As, E, B, C, M, N, K, in_dtype, out_dtype, transB);
+    if (p.status == GEMM_RELU_EINVAL) return nullptr;
+    if (p.status != GEMM_RELU_OK) return "unsupported";
+    if (p.empty) return "none";
+    return kSpConfigName;
 }

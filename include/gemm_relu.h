@@ -136,6 +136,45 @@ const char* gemm_relu_mx_plan(const void* A, const void* SA, const void* B, cons
                               const void* C, int64_t M, int64_t N, int64_t K, int fmt,
                               int out_dtype);
 
+/*
+ * gemm_relu_sp — the 2:4 structured-sparse product: the "2:4 structured-sparse
+ * tensor core (T.gemm_sp)" item of the first page's §4.1 timeline, whose A
+ * arrives compressed together with its metadata (page "从 TVM 到 TileLang…",
+ * §四).  Every row of A is cut along K into groups of 4 consecutive elements
+ * with at most two non-zeros; the caller passes them compressed:
+ *
+ *   As   device pointer, M x (K / 2) row-major, in_dtype: As[i][2q] and
+ *        As[i][2q + 1] are the two stored values of group q of row i (zeros
+ *        where the group has fewer non-zeros).
+ *   E    device pointer, metadata bytes, blocked by 64 columns of K:
+ *        ceil(K / 64) blocks, each M x 8 bytes row-major.  Group q of row i is
+ *        nibble q % 2 (the low nibble for even q) of byte (q % 16) / 2 of row
+ *        i's 8 bytes in block q / 16; the nibble is p0 | p1 << 2, the positions
+ *        (0..3, p0 < p1) inside the group of As[i][2q] and As[i][2q + 1].
+ *        Nibbles of groups past K are ignored.  A nibble with p0 >= p1 gives an
+ *        unspecified result (the library does not read E on the host).
+ *   B, C, transB, stream   as for gemm_relu (B dense (K, N) or stored (N, K)).
+ *   M, N, K    >= 0, <= INT32_MAX; K a multiple of 4 (whole groups).
+ *   in_dtype   GEMM_RELU_F16 or GEMM_RELU_BF16 (As and B share it).
+ *   out_dtype  GEMM_RELU_F16, GEMM_RELU_BF16 or GEMM_RELU_F32.
+ *
+ *   C[i][j] = max( sum_q As[i][2q] opB[4q + p0][j] + As[i][2q + 1] opB[4q + p1][j], 0 )
+ *
+ * Numerics: products summed in fp32 on the sparse matrix units (order
+ * unspecified); ReLU and rounding as for gemm_relu.  Ownership and execution as
+ * for gemm_relu.  Errors: EINVAL for bad sizes, K not a multiple of 4, an
+ * unknown code, a NULL or misaligned pointer (As, B 2-byte aligned; C to its
+ * element), or C overlapping As, E or B; EUNSUPPORTED when K > 2^22, N > 2^24,
+ * or B is stored (K, N) with N < 256; EHIP as for gemm_relu.
+ */
+int gemm_relu_sp(const void* As, const void* E, const void* B, void* C, int64_t M, int64_t N,
+                 int64_t K, int in_dtype, int out_dtype, int transB, void* stream);
+
+/* Configuration name gemm_relu_sp would launch (as gemm_relu_plan). */
+const char* gemm_relu_sp_plan(const void* As, const void* E, const void* B, const void* C,
+                              int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
+                              int transB);
+
 #ifdef __cplusplus
 }
 #endif

@@ -202,3 +202,32 @@ def test_mx_interleaved_needs_16_scale_blocks_per_row(monkeypatch, fmt):
 def test_mx_only_configuration_not_used_for_other_inputs(monkeypatch, in_dtype):
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x128x64_s2")
     assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, in_dtype, 0, 1) == "d256x256x32_s4_i"
+
+
+# ------------------------------------------------ 2:4 sparse entry point
+E_ = 6 << 32
+
+
+@pytest.mark.parametrize("args", [
+    (A, E_, B, C, 4, 4, 6, 0, 0, 0),          # K not a multiple of 4
+    (A, E_, B, C, 4, 4, 8, 3, 0, 0),          # FP8 inputs are not a sparse format here
+    (A, E_, B, C, 4, 4, 8, 0, 3, 0),          # unknown output
+    (A, E_, B, C, 4, 4, 8, 0, 0, 2),          # transB not in {0, 1}
+    (A, 0, B, C, 4, 4, 8, 0, 0, 1),           # NULL metadata with elements
+    (A + 1, E_, B, C, 4, 4, 8, 0, 0, 1),      # misaligned As
+    (A, E_, B, E_, 4, 4, 8, 0, 0, 1),         # C overlaps E
+    (A, E_, B, C, 4, -1, 8, 0, 0, 1),         # negative N
+])
+def test_sp_invalid_arguments(args):
+    assert gr.gemm_relu_sp_status(*args, stream=0) == gr.EINVAL
+    assert gr.gemm_relu_sp_plan(*args) is None
+
+
+def test_sp_plan():
+    assert gr.gemm_relu_sp_plan(A, E_, B, C, 8192, 8192, 8192, 0, 0, 0) == "sp256x256x64_s3"
+    assert gr.gemm_relu_sp_plan(A, E_, B, C, 1, 1, 4, 1, 2, 1) == "sp256x256x64_s3"
+    assert gr.gemm_relu_sp_plan(A, E_, B, C, 0, 8, 8, 0, 0, 0) == "none"
+    # B stored (K, N) needs a full tile of columns
+    assert gr.gemm_relu_sp_plan(A, E_, B, C, 64, 255, 64, 0, 0, 0) == "unsupported"
+    assert gr.gemm_relu_sp_status(A, E_, B, C, 64, 255, 64, 0, 0, 0, stream=0) == gr.EUNSUPPORTED
+    assert gr.gemm_relu_sp_plan(A, E_, B, C, 64, 8, (1 << 22) + 4, 0, 0, 1) == "unsupported"

@@ -360,7 +360,7 @@ def _sample_positions(M, N, rng, n=2048):
     return np.concatenate([r, edge_r]), np.concatenate([c, edge_c])
 
 
-@pytest.mark.parametrize("name", [n for n, w in wl.WORKLOADS.items() if not w.get("mx")])
+@pytest.mark.parametrize("name", [n for n, w in wl.WORKLOADS.items() if not w.get("mx") and not w.get("sparse")])
 def test_workload_full_size(name):
     """Each workload at its full size, with the configuration the bench times:
     random inputs checked on sampled outputs (oracle dot products one by one),

@@ -114,8 +114,9 @@ def test_unaligned_16_byte_loads(probe):
     assert np.array_equal(got[0], want), "direct global->LDS copy"
 
 
-@pytest.mark.parametrize("kind,opb,cycles", [(0, 16, 32), (1, 32, 64), (2, 16, 32), (3, 32, 64)],
-                         ids=["f16", "e4m3", "mx_e2m1", "mx_e4m3"])
+@pytest.mark.parametrize("kind,opb,cycles", [(0, 16, 32), (1, 32, 64), (2, 16, 32), (3, 32, 64),
+                                              (4, 32, 32)],
+                         ids=["f16", "e4m3", "mx_e2m1", "mx_e4m3", "sparse_f16"])
 def test_mfma_rate_probe(probe, kind, opb, cycles):
     """The MFMA-only diagnostic (random operands, no memory traffic) runs, issues
     one 32x32x16 fp16 MFMA per 32 shader cycles (one 32x32x64 E4M3 MFMA per
@@ -131,9 +132,9 @@ def test_mfma_rate_probe(probe, kind, opb, cycles):
     if kind == 2:                                        # random E2M1 nibble pairs
         src = torch.randint(0, 256, (blocks * 8 * 256 * opb,), dtype=torch.uint8, device="cuda")
     else:
-        per_lane = opb // 2 if kind == 0 else opb       # elements per operand per lane
+        per_lane = opb // 2 if kind in (0, 4) else opb  # elements per operand per lane
         src = torch.empty(blocks * 8 * 256 * per_lane, dtype=torch.float32, device="cuda")
-        src = src.uniform_(-1, 1).to(torch.float16 if kind == 0 else torch.float8_e4m3fn)
+        src = src.uniform_(-1, 1).to(torch.float16 if kind in (0, 4) else torch.float8_e4m3fn)
     nbytes = src.numel() * src.element_size()
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     ticks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
@@ -141,7 +142,7 @@ def test_mfma_rate_probe(probe, kind, opb, cycles):
     assert lib.probe_mfma_rate(src.data_ptr(), nbytes - 1, out.data_ptr(),
                                ticks.data_ptr(), blocks, steps, kind, st) == -1
     assert lib.probe_mfma_rate(src.data_ptr(), nbytes, out.data_ptr(),
-                               ticks.data_ptr(), blocks, steps, 4, st) == -1
+                               ticks.data_ptr(), blocks, steps, 5, st) == -1
     assert lib.probe_mfma_rate(src.data_ptr(), nbytes, out.data_ptr(),
                                ticks.data_ptr(), blocks, steps, kind, st) == 0
     torch.cuda.synchronize()
@@ -227,3 +228,50 @@ def test_byte_unaligned_16_byte_loads():
     want = np.stack([src[o:o + 16] for o in off])
     assert np.array_equal(got[1], want), "plain vector load"
     assert np.array_equal(got[0], want), "direct global->LDS copy"
+
+
+# ------------------------------------------------------- 2:4 sparse MFMA
+@pytest.mark.parametrize("bf16", [False, True], ids=["f16", "bf16"])
+@pytest.mark.parametrize("abid", [0, 1])
+def test_smfmac_32x32x32_layout(bf16, abid):
+    """v_smfmac_f32_32x32x32: lane 32 g + i of the sparse operand holds the 8
+    stored values of groups 4 g .. 4 g + 3 of row i (2 per group, in order);
+    its index word holds their positions as nibbles p0 | p1 << 2 in group order
+    (bits 0..15, or 16..31 when ABID = 1); lane 32 g + j of the dense operand
+    holds k = 8 g .. 8 g + 7 then 16 + 8 g .. 16 + 8 g + 7 of column j; result
+    register r of lane l is D[8 (r/4) + 4 (l/32) + r%4][l%32], rows from the
+    sparse operand — the layout gemm_sp_relu_kernel.hpp assumes."""
+    import torch
+    lib = ctypes.CDLL(gr.PROBE_LIB_PATH)
+    lib.probe_smfmac_raw.restype = ctypes.c_int
+    lib.probe_smfmac_raw.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int, ctypes.c_int]
+    rng = np.random.default_rng(40 + abid + 2 * bf16)
+    av = rng.integers(-3, 4, size=(64, 8)).astype(np.float64)
+    bv = rng.integers(-3, 4, size=(64, 16)).astype(np.float64)
+    pairs = np.asarray(wl.SP_PAIRS)
+    pick = rng.integers(0, 6, size=(64, 8))               # 8 groups: both halves of the word
+    idx = np.zeros(64, np.uint32)
+    for grp in range(8):
+        idx |= ((pairs[pick[:, grp], 0] | (pairs[pick[:, grp], 1] << 2)) << (4 * grp)).astype(np.uint32)
+    dt = wl.BF16 if bf16 else wl.F16
+    a_d = torch.from_numpy(wl.encode(av, dt).view(np.int16)).cuda()
+    b_d = torch.from_numpy(wl.encode(bv, dt).view(np.int16)).cuda()
+    i_d = torch.from_numpy(idx.view(np.int32)).cuda()
+    d = torch.zeros(64 * 16, dtype=torch.float32, device="cuda")
+    assert lib.probe_smfmac_raw(a_d.data_ptr(), b_d.data_ptr(), i_d.data_ptr(), d.data_ptr(),
+                                1 if bf16 else 0, abid) == 0
+    torch.cuda.synchronize()
+    A = np.zeros((32, 32))
+    Bm = np.zeros((32, 32))
+    for lane in range(64):
+        i, g = lane % 32, lane // 32
+        w = int(idx[lane]) >> (16 * abid)
+        for v in range(8):
+            pos = (w >> (2 * v)) & 3
+            A[i, 16 * g + 4 * (v // 2) + pos] += av[lane, v]
+        for e in range(16):
+            Bm[8 * g + e if e < 8 else 16 + 8 * g + e - 8, i] = bv[lane, e]
+    D = A @ Bm
+    want = np.array([[D[8 * (r // 4) + 4 * (lane // 32) + r % 4, lane % 32] for r in range(16)]
+                     for lane in range(64)])
+    assert np.array_equal(d.cpu().numpy().reshape(64, 16), want)

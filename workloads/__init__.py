@@ -106,6 +106,9 @@ WORKLOADS = {
                                  out_dtype=F16, transB=1, dist="uniform", mx=True),
     "gemm_relu_mxfp8_8192": dict(index=9, M=8192, N=8192, K=8192, in_dtype=MX_E4M3,
                                  out_dtype=F16, transB=1, dist="uniform", mx=True),
+    # 2:4 sparse A (gemm_relu_sp): the T.gemm_sp of the same list, B (K, N)
+    "gemm_relu_sp_f16_8192": dict(index=10, M=8192, N=8192, K=8192, in_dtype=F16,
+                                  out_dtype=F16, transB=0, dist="uniform", sparse=True),
 }
 
 
