@@ -18,6 +18,7 @@ enum ConfigId : int {
     CFG_D256x256x32_S5,
     CFG_D256x256x32_S4_I,
     CFG_D256x256x64_S2_16,
+    CFG_D256x256x32_S4_I16,
     CFG_D256x256x32_S4_W8I,
     CFG_D256x256x32_S5_W8I,
     CFG_D256x256x64_S2_W8,
@@ -45,6 +46,7 @@ inline const ConfigInfo& config_info(int id)
         {"d256x256x32_s5", 256, 256, true},
         {"d256x256x32_s4_i", 256, 256, true},
         {"d256x256x64_s2_16", 256, 256, true},
+        {"d256x256x32_s4_i16", 256, 256, true},
         {"d256x256x32_s4_w8i", 256, 256, true},
         {"d256x256x32_s5_w8i", 256, 256, true},
         {"d256x256x64_s2_w8", 256, 256, true},
@@ -87,6 +89,12 @@ template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4
 // tuples every step.
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_16> {
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 64>, 2, 2, 2, true, false, 16>;
+};
+// The interleaved four-stage tile with 16x16x32 MFMA blocks (16-bit inputs):
+// one MFMA k step per 32-k step.  Built in its own units (inst_i16.hip), with
+// the matrix instructions in their VGPR form.
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I16> {
+    using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 4, true, true, 16>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_W8I> {
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 4, 4, true, true>;
@@ -146,6 +154,8 @@ LaunchFn launcher_f8e5m2_nt(int out_dt, int cfg);
 LaunchFn launcher_mx_e4m3(int out_dt, int cfg);
 LaunchFn launcher_mx_e5m2(int out_dt, int cfg);
 LaunchFn launcher_mx_e2m1(int out_dt, int cfg);
+// the 16x16-block interleaved tile for a 16-bit input type (inst_i16.hip)
+LaunchFn launcher_i16(int in_dt, int out_dt, bool transB);
 
 // Configurations built for 8-bit inputs: the ones plan selection can choose
 // (the 16-bit comparison variants are not instantiated for them).
@@ -175,6 +185,8 @@ inline bool fp8_config(int cfg)
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I>::type>;   \
         case CFG_D256x256x64_S2_16:                                                        \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_16>::type>;  \
+        case CFG_D256x256x32_S4_I16:                                                       \
+            return launcher_i16(IN, OUT, TB);                                              \
         case CFG_D256x256x32_S4_W8I:                                                       \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_W8I>::type>; \
         case CFG_D256x256x32_S5_W8I:                                                       \

@@ -949,6 +949,16 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
             // the scale register sets) is known at compile time; a steady
             // step left over before the checked ones runs checked
             int t = 0;
+            if constexpr (C::MB == 16 && !C::MX) {
+                // 16x16 blocks: single steady steps, the fragment set read for
+                // the next step copied into the contracted one (64 register
+                // moves a step); the two-step form makes the register
+                // allocator shuffle the 64 small accumulators instead
+                for (; t < t_steady; ++t) {
+                    step(t, Steady{}, P0{});
+                    fr[0] = fr[1];
+                }
+            }
             for (; t + 1 < t_steady; t += 2) {
                 step(t, Steady{}, P0{});
                 step(t + 1, Steady{}, P1{});
