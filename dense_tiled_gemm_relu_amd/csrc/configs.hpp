@@ -19,6 +19,7 @@ enum ConfigId : int {
     CFG_D256x256x32_S4_I,
     CFG_D256x256x64_S2_16,
     CFG_D256x256x32_S4_I16,
+    CFG_D256x256x32_S4_IP,
     CFG_D256x256x32_S4_W8I,
     CFG_D256x256x32_S5_W8I,
     CFG_D256x256x64_S2_W8,
@@ -36,6 +37,7 @@ struct ConfigInfo {
     const char* name;
     int bm, bn;
     bool direct;
+    bool persistent = false;   // grid of min(tiles, CUs) workgroups looping over tiles
 };
 
 inline const ConfigInfo& config_info(int id)
@@ -47,6 +49,7 @@ inline const ConfigInfo& config_info(int id)
         {"d256x256x32_s4_i", 256, 256, true},
         {"d256x256x64_s2_16", 256, 256, true},
         {"d256x256x32_s4_i16", 256, 256, true},
+        {"d256x256x32_s4_ip", 256, 256, true, true},
         {"d256x256x32_s4_w8i", 256, 256, true},
         {"d256x256x32_s5_w8i", 256, 256, true},
         {"d256x256x64_s2_w8", 256, 256, true},
@@ -95,6 +98,11 @@ template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x64_S2
 // the matrix instructions in their VGPR form.
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I16> {
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 4, true, true, 16>;
+};
+// The default interleaved tile as a persistent kernel: at most one workgroup
+// per CU, each looping over its tiles (the Ascend version's T.Persistent).
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_IP> {
+    using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 4, true, true, 32, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_W8I> {
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 4, 4, true, true>;
@@ -187,6 +195,8 @@ inline bool fp8_config(int cfg)
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_16>::type>;  \
         case CFG_D256x256x32_S4_I16:                                                       \
             return launcher_i16(IN, OUT, TB);                                              \
+        case CFG_D256x256x32_S4_IP:                                                        \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_IP>::type>;  \
         case CFG_D256x256x32_S4_W8I:                                                       \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_W8I>::type>; \
         case CFG_D256x256x32_S5_W8I:                                                       \

@@ -372,7 +372,9 @@ extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64
     LaunchFn fn = pick_launcher(in_dtype, out_dtype, transB, p.cfg);
     if (!fn) return GEMM_RELU_EUNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (fn(args, p.tiles_m * p.tiles_n, st) != hipSuccess) return GEMM_RELU_EHIP;
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int grid = config_info(p.cfg).persistent ? std::min(tiles, kNumCUs) : tiles;
+    if (fn(args, grid, st) != hipSuccess) return GEMM_RELU_EHIP;
     if (e.sync) {
         if (hipStreamSynchronize(st) != hipSuccess) return GEMM_RELU_EHIP;
         if (hipGetLastError() != hipSuccess) return GEMM_RELU_EHIP;

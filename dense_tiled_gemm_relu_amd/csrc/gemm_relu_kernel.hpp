@@ -267,8 +267,10 @@ template <> struct OutTraits<DT_F32> {
 
 // ---------------------------------------------------------- configuration
 template <int IN_DT_, int OUT_DT_, bool TRANS_B_, int BM_, int BN_, int BK_, int WAVES_M_,
-          int WAVES_N_, int STAGES_, bool DIRECT_, bool INTERLEAVE_ = false, int MB_ = 32>
+          int WAVES_N_, int STAGES_, bool DIRECT_, bool INTERLEAVE_ = false, int MB_ = 32,
+          bool PERSISTENT_ = false>
 struct Cfg {
+    static constexpr bool PERSISTENT = PERSISTENT_;   // tile loop over a grid of <= 1 per CU
     static constexpr int IN_DT = IN_DT_, OUT_DT = OUT_DT_;
     static constexpr bool TRANS_B = TRANS_B_, DIRECT = DIRECT_, INTERLEAVE = INTERLEAVE_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
@@ -411,8 +413,11 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
 }
 
 // ------------------------------------------------------------- the kernel
+// One output tile: the tile with launch-order index wg (see tile_coords), its
+// accumulator cleared, its whole K range contracted, the ReLU epilogue stored.
 template <class C>
-__global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs args)
+__device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
+                                               GR_LDS unsigned char* smem)
 {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::STAGES;
     constexpr int TM = C::TM, TN = C::TN, KSUB = C::KSUB;
@@ -422,16 +427,13 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
     using In = typename C::In;
     using Op = typename In::Op;
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[C::LDS_BYTES];
-    GR_LDS unsigned char* smem = (GR_LDS unsigned char*)(smem_raw);
-
     const int M = args.M, N = args.N, K = args.K;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     int tm, tn;
-    tile_coords(blockIdx.x, args.tiles_m, args.tiles_n, args.panel, args.nxcd, tm, tn);
+    tile_coords(wg, args.tiles_m, args.tiles_n, args.panel, args.nxcd, tm, tn);
     const int m0 = tm * BM;
     // (K,N) B on the direct path: the last tile column is moved back to end at N,
     // so every B chunk it copies lies inside its row (the columns it shares with
@@ -1155,6 +1157,29 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
                 }
             }
         }
+    }
+}
+
+// One workgroup per tile, or (persistent configurations, the T.Persistent form
+// of page "TileLang：GPU/NPU 通用算子 DSL", §3.3) a grid of at most one
+// workgroup per CU whose workgroups walk the tiles wg, wg + grid, ...: the
+// accumulator is cleared per tile, and a barrier after each tile keeps the
+// next tile's copies off the LDS the epilogue may still be reading.  A grid
+// that is a multiple of 8 keeps every tile of a workgroup on its XCD.
+template <class C>
+__global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs args)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[C::LDS_BYTES];
+    GR_LDS unsigned char* smem = (GR_LDS unsigned char*)(smem_raw);
+    if constexpr (C::PERSISTENT) {
+        const int total = args.tiles_m * args.tiles_n;
+        for (int wg = blockIdx.x; wg < total; wg += gridDim.x) {
+            gemm_relu_tile<C>(args, wg, smem);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            barrier_lds();
+        }
+    } else {
+        gemm_relu_tile<C>(args, blockIdx.x, smem);
     }
 }
 

@@ -231,3 +231,14 @@ def test_sp_plan():
     assert gr.gemm_relu_sp_plan(A, E_, B, C, 64, 255, 64, 0, 0, 0) == "unsupported"
     assert gr.gemm_relu_sp_status(A, E_, B, C, 64, 255, 64, 0, 0, 0, stream=0) == gr.EUNSUPPORTED
     assert gr.gemm_relu_sp_plan(A, E_, B, C, 64, 8, (1 << 22) + 4, 0, 0, 1) == "unsupported"
+
+
+@pytest.mark.parametrize("name", ["d256x256x32_s4_ip", "d256x256x32_s4_i16"])
+def test_comparison_configurations_are_selectable(monkeypatch, name):
+    """The persistent tile loop and the 16x16-block tile: forced by name for
+    16-bit inputs, never chosen automatically, not built for 8-bit inputs."""
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0) == "d256x256x32_s4_i"
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", name)
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0) == name
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 1, 2, 1) == name
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 3, 0, 0) == "d256x256x32_s4_i"

@@ -21,7 +21,7 @@ from tests.helpers import (check_close, from_device, fp32_sum_bound, out_tensor,
 pytestmark = pytest.mark.gpu
 
 DIRECT = ["d256x256x64_s2", "d256x256x32_s4", "d256x256x32_s5", "d256x256x32_s4_i",
-          "d256x256x64_s2_16", "d256x256x32_s4_i16", "d256x256x32_s4_w8i",
+          "d256x256x64_s2_16", "d256x256x32_s4_i16", "d256x256x32_s4_ip", "d256x256x32_s4_w8i",
           "d256x256x32_s5_w8i", "d256x256x64_s2_w8", "d128x128x64_s3", "d64x64x64_s4",
           "d64x32x128_s4"]
 STAGED = ["g128x128x64", "g64x64x64"]
@@ -36,7 +36,7 @@ def _gpu():
 
 
 BN_OF = {"d256x256x64_s2": 256, "d256x256x32_s4": 256, "d256x256x32_s5": 256,
-         "d256x256x32_s4_i": 256, "d256x256x64_s2_16": 256, "d256x256x32_s4_i16": 256,
+         "d256x256x32_s4_i": 256, "d256x256x64_s2_16": 256, "d256x256x32_s4_i16": 256, "d256x256x32_s4_ip": 256,
          "d256x256x32_s4_w8i": 256, "d256x256x32_s5_w8i": 256,
          "d256x256x64_s2_w8": 256, "d128x128x64_s3": 128, "d64x64x64_s4": 64,
          "d64x32x128_s4": 32}
