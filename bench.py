@@ -448,8 +448,8 @@ def main():
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     metric = METRIC if args.workload == "gemm_relu_f16_8192" else (
         "TFLOP/s and %% of MI355X %s MFMA peak, %s" %
-        ({PEAK_TFLOPS_F4: "fp4", PEAK_TFLOPS_F8: "fp8",
-          PEAK_TFLOPS_F16_SPARSE: "2:4 sparse fp16/bf16 (dense-equivalent)"}.get(peak, "fp16/bf16"),
+        ("2:4 sparse fp16/bf16 (dense-equivalent)" if sparse else
+         {PEAK_TFLOPS_F4: "fp4", PEAK_TFLOPS_F8: "fp8"}.get(peak, "fp16/bf16"),
          args.workload))
     out = {
         "metric": metric,
