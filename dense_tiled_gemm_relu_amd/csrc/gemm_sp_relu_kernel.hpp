@@ -186,6 +186,22 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_sp_relu_kernel(SpArgs arg
 #pragma unroll
         for (int i = 0; i < EPT; ++i) dma4(ge, e_src[i], se + (i * C::NWAVES + wave) * 256);
     };
+    // copy l (< LOADS_PER_STAGE: A chunks, B chunks, metadata pieces) of stage t
+    auto issue_one = [&](int t, int stage, int l) {
+        const uint32_t sa = smem_addr + stage * C::STAGE_BYTES;
+        const uint32_t sb = sa + C::A_BYTES;
+        const uint32_t se = sb + C::B_BYTES;
+        if (l < APT) {
+            dma16(a_tile + (size_t)t * (BK / 2) * 2, a_src[l], sa + (l * C::NWAVES + wave) * 1024);
+        } else if (l < APT + BPT) {
+            const unsigned char* gb = C::TRANS_B ? b_tile + (size_t)t * BK * 2
+                                                 : b_tile + (size_t)t * BK * (size_t)N * 2;
+            dma16(gb, b_src[l - APT], sb + ((l - APT) * C::NWAVES + wave) * 1024);
+        } else {
+            const unsigned char* ge = args.E + ((size_t)t * (size_t)M + (size_t)m0) * 8;
+            dma4(ge, e_src[l - APT - BPT], se + ((l - APT - BPT) * C::NWAVES + wave) * 256);
+        }
+    };
 
     // ---- K tail (K % 64): one register-staged step, zero-filled past K; the
     // metadata block of the tail exists whole, so it takes the direct copy.
@@ -334,17 +350,25 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_sp_relu_kernel(SpArgs arg
         }
     };
 
-    // ---- pipeline: S-1 stages in flight ahead of the one contracted; at the
-    // last k step of stage t the wave waits for stage t+1, meets the others at
-    // a barrier (which also retires every read of stage t, so its buffer may be
-    // refilled) and reads stage t+1's first fragments.
+    // ---- pipeline: S-1 stages in flight ahead of the one contracted.  The
+    // copies of stage t+S-1 are spread over step t: each k step is TN
+    // scheduling regions (block column j: its copies, its MFMAs, then the
+    // read of its next B block), with LK copies per k step.  At the last k
+    // step of stage t the wave waits for stage t+1 (the copies issued after
+    // it: stages t+2 .. t+S-2 whole and the first k steps' share of stage
+    // t+S-1), meets the others at a barrier (which also retires every read of
+    // stage t, so its buffer may be refilled) and reads stage t+1's first
+    // fragments.
+    constexpr int L = C::LOADS_PER_STAGE, LK = (L + KSUB - 1) / KSUB;
+    constexpr int ALLOW = (S - 3) * L + (KSUB - 1) * LK;
+    static_assert(ALLOW < 64, "vmcnt range");
     AFrags fa[2];
 #pragma unroll
     for (int st = 0; st < S - 1; ++st)
         if (st < nk) issue_stage(st, st);
     if (nk > 0) {
         if (nk - 1 >= S - 2)
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 2) * C::LOADS_PER_STAGE));
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 2) * L));
         else
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         barrier_lds();
@@ -354,7 +378,8 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_sp_relu_kernel(SpArgs arg
     }
     for (int t = 0; t < nk; ++t) {
         const int stage = t % S;
-        if (t + S - 1 < nk) issue_stage(t + S - 1, (t + S - 1) % S);
+        const bool loads = t + S - 1 < nk;
+        const int ld_stage = (t + S - 1) % S;
 #pragma unroll
         for (int s = 0; s < KSUB; ++s) {
             int next_stage = -1, next_s = 0;
@@ -362,16 +387,29 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_sp_relu_kernel(SpArgs arg
                 next_stage = stage;
                 next_s = s + 1;
             } else if (t + 1 < nk) {
-                // stages issued after t+1: t+2 .. min(t+S-1, nk-1)
-                if (nk - 2 - t >= S - 2)
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 2) * C::LOADS_PER_STAGE));
+                if (loads)
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALLOW));
                 else
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
                 barrier_lds();
                 next_stage = (t + 1) % S;
             }
-            if (next_stage >= 0) read_a(next_stage, next_s, fa[(s + 1) & 1]);
-            contract(fa[s & 1], next_stage, next_s);
+            const AFrags& f = fa[s & 1];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (loads) {
+#pragma unroll
+                    for (int l = s * LK + (j * LK + TN - 1) / TN; l < s * LK + ((j + 1) * LK + TN - 1) / TN; ++l)
+                        if (l < L) issue_one(t + S - 1, ld_stage, l);
+                }
+                if (j == 0 && next_stage >= 0) read_a(next_stage, next_s, fa[(s + 1) & 1]);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    acc[i][j] = SpIn<C::IN_DT>::smfmac(f.a[i], b[j], acc[i][j], f.idx[i]);
+                if (next_stage >= 0) read_b(next_stage, next_s, j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     if (K % BK != 0) {
