@@ -126,6 +126,15 @@ __device__ __forceinline__ i32x2_t lds_read_tr8(const GR_LDS unsigned char* p)
         reinterpret_cast<GR_LDS i32x2_t*>(const_cast<GR_LDS unsigned char*>(p)));
 }
 
+// f(integral_constant<int, I>) for I = B .. E-1, each I a compile-time constant.
+template <int B, int E, class F> __device__ __forceinline__ void static_for(F&& f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // Input element types and MFMA shapes.  MB is the MFMA block (32: 32x32 C
 // block; 16: 16x16), NG = 64 / MB lane groups along k.  A lane's operand holds
 // the OPB bytes of KMF / NG consecutive k of one row (or column): OPB / 16
@@ -303,7 +312,10 @@ struct Cfg {
     static constexpr int SGS = MX_LDS ? 16 / BPS : 1;
     static constexpr int SC_REGION = MX_LDS ? (BM + BN) * 16 : 0;
     static constexpr int SC_COPIES = MX_LDS ? (BM + BN) / NTHREADS : 0;   // per thread per group
-    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + 2 * SC_REGION;
+    // ... and a word-major copy of each group (word k of every row, rows 4
+    // bytes apart), in two more regions, which the per-step reads use
+    static constexpr int SC_T_REGION = SC_REGION;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + 2 * SC_REGION + 2 * SC_T_REGION;
     static constexpr int A_CH = BM * ROW_CH;                       // 16 B chunks per stage
     static constexpr int B_CH = BN * BK * EB / 16;
     static constexpr int A_PER_THREAD = A_CH / NTHREADS;
@@ -320,6 +332,8 @@ struct Cfg {
                   "four-stage interleaved one");
     static_assert(!MX_LDS || ((BPS == 2 || BPS == 4) && BM % NTHREADS == 0 && BN % NTHREADS == 0),
                   "LDS-staged scales: 2 or 4 blocks per step; whole A and B row sets per copy");
+    static_assert(!MX_LDS || SGS >= 4, "a scale group is rearranged two steps after its copies, "
+                                        "before its first read");
     static_assert(A_CH % NTHREADS == 0 && B_CH % NTHREADS == 0, "loader tiling");
     static_assert(TRANS_B || NROW_CH >= (EB == 2 ? 4 : 2), "n-contiguous B rows of at least 64 (16-bit) or 32 (8-bit) bytes");
     static_assert(STAGES >= 2 && STAGES <= 5, "stages");
@@ -792,7 +806,15 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
         // one of two register sets: the byte of its own block (2 blocks per
         // step) or the row's 4-byte word, of which k-step s takes byte 2 s + g
         // (4 blocks per step).
+        // The reads go to a word-major copy of the group: two steps after a
+        // group's copies (the step whose wait covers them), each thread moves
+        // its rows' 16 bytes into word planes (word k of row q at plane k, q * 4),
+        // so a read of 32 consecutive rows is 32 consecutive words.  (Read
+        // straight from the 16-byte rows, 32 rows fall on 16 bank positions:
+        // measured at 8192^3, about 6 conflict cycles per read.)  The plane
+        // region of group G+1 was last read for step SGS G - 1.
         constexpr int SGS = C::SGS, GC = C::SC_COPIES;
+        constexpr int SC_ROWS = BM + BN;
         constexpr int NSC = C::MX_LDS ? TM + TN : 1;
         uint32_t scg_src[GC > 0 ? GC : 1];
         if constexpr (C::MX_LDS) {
@@ -819,11 +841,25 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
                 }
             }
         };
-        // Reads are whole aligned words; the step's first block is byte sc_sub
-        // of the word, and the lane shifts its byte down at use.  (Rows 16
-        // bytes apart put the 32 rows of a read on 16 bank positions: measured
-        // at 8192^3, about 6 conflict cycles per read, ~11% of LDS cycles.)
-        const int sc_a = (wm0 + lr) * 16, sc_b = (BM + wn0 + lr) * 16;
+        GR_LDS unsigned char* const sc_raw = smem + S * C::STAGE_BYTES;
+        GR_LDS unsigned char* const sc_planes = sc_raw + 2 * C::SC_REGION;
+        auto rearrange_group = [&](int G) {
+            if constexpr (C::MX_LDS) {
+                const GR_LDS unsigned char* raw = sc_raw + (G & 1) * C::SC_REGION;
+                GR_LDS unsigned char* pl = sc_planes + (G & 1) * C::SC_T_REGION;
+#pragma unroll
+                for (int i = 0; i < GC; ++i) {
+                    const int q = i * C::NTHREADS + tid;
+                    const u32x4_t v = lds_read_b128(raw + q * 16);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        *reinterpret_cast<GR_LDS uint32_t*>(pl + k * SC_ROWS * 4 + q * 4) = v[k];
+                }
+            }
+        };
+        // Reads are whole words; the step's first block is byte sc_sub of the
+        // word, and the lane shifts its byte down at use.
+        const int sc_a = (wm0 + lr) * 4, sc_b = (BM + wn0 + lr) * 4;
         uint32_t scv[2][NSC];
         int sc_sub[2] = {0, 0};
         auto read_scales = [&](int t, auto set_tag) {
@@ -831,13 +867,13 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
                 constexpr int SET = decltype(set_tag)::value;
                 const int G = t / SGS;
                 const int first = BPS * t - group_off(G);       // byte of the step's first block
-                const GR_LDS unsigned char* reg = smem + S * C::STAGE_BYTES + (G & 1) * C::SC_REGION +
-                                                  (first & ~3);
+                const GR_LDS unsigned char* pl = sc_planes + (G & 1) * C::SC_T_REGION +
+                                                 (first >> 2) * SC_ROWS * 4;
                 sc_sub[SET] = first & 3;
 #pragma unroll
                 for (int q = 0; q < NSC; ++q) {
                     const GR_LDS unsigned char* p =
-                        reg + (q < TM ? sc_a + 16 * MB * q : sc_b + 16 * MB * (q - TM));
+                        pl + (q < TM ? sc_a + 4 * MB * q : sc_b + 4 * MB * (q - TM));
                     scv[SET][q] = *reinterpret_cast<const GR_LDS uint32_t*>(p);
                 }
             }
@@ -869,6 +905,10 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
             else
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             barrier_lds();
+            if constexpr (C::MX_LDS) {
+                rearrange_group(0);
+                barrier_lds();
+            }
             read_scales(0, std::integral_constant<int, 0>{});
 #pragma unroll
             for (int q = 0; q < NR; ++q) read_op(0, 0, q, fr[0]);
@@ -878,9 +918,16 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
         // per BK step the two fragment sets swap roles from one step to the
         // next (k-step s of step t contracts set (t KSUB + s) mod 2).  SLOT =
         // t mod S (block-scaled inputs: the scale ring).
-        auto step = [&](int t, auto steady_tag, auto parity_tag) {
+        // RUN (block-scaled inputs): the step's position in an unrolled run of
+        // SGS steady steps that starts a scale group, or -1 for a step whose
+        // group duties are decided at run time.  In a run they are fixed at
+        // compile time and taken unconditionally (a group past the last one
+        // copies and rearranges clamped, in-bounds bytes nobody reads), so the
+        // run has no branches for the compiler to move MFMAs across.
+        auto step = [&](int t, auto steady_tag, auto parity_tag, auto run_tag) {
             constexpr bool STEADY = decltype(steady_tag)::value;
             constexpr int PARITY = decltype(parity_tag)::value;
+            constexpr int RUN = decltype(run_tag)::value;
             const int stage = t % S;
             const bool loads = STEADY || t + S - 1 < nk;
             const int ld_stage = (t + S - 1) % S;
@@ -893,7 +940,10 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
             // a scale group's copies issued after stage t+1's, before this
             // step's wait: by the previous step, or by this one when the wait
             // is not at its top
-            const bool group_after = group_step(t - 1) || (KSUB > 1 && group_step(t));
+            const bool group_after = RUN >= 0 ? (RUN == 1 || (KSUB > 1 && RUN == 0))
+                                              : (group_step(t - 1) || (KSUB > 1 && group_step(t)));
+            const bool group_now = RUN >= 0 ? RUN == 0 : group_step(t);
+            const bool rearrange_now = RUN >= 0 ? RUN == 2 : (t % SGS == 2 && group_step(t - 2));
 #pragma unroll
             for (int s = 0; s < KSUB; ++s) {
                 const bool last = s + 1 == KSUB;
@@ -907,12 +957,17 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
                     barrier_lds();
                 }
                 if constexpr (C::MX_LDS)
-                    if (s == 0 && group_step(t)) issue_group(t / SGS + 1);
+                    if (s == 0 && group_now) issue_group(t / SGS + 1);
                 const bool reads = !last || STEADY || t + 1 < nk;
                 const int rd_stage = last ? (t + 1) % S : stage;
                 const int rd_s = last ? 0 : s + 1;
-                if constexpr (C::MX_LDS)
+                if constexpr (C::MX_LDS) {
+                    // the group copied two steps ago has landed (this step's
+                    // wait covers it): rearrange it before its first read,
+                    // which comes at least one barrier later
+                    if (last && rearrange_now) rearrange_group(t / SGS + 1);
                     if (last && reads) read_scales(t + 1, std::integral_constant<int, 1 - PARITY>{});
+                }
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     __builtin_amdgcn_sched_barrier(0);
@@ -943,33 +998,43 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
         using Checked = std::integral_constant<bool, false>;
         using P0 = std::integral_constant<int, 0>;
         using P1 = std::integral_constant<int, 1>;
+        using NoRun = std::integral_constant<int, -1>;
         if constexpr (KSUB % 2 == 0 && !C::MX_LDS) {
-            for (int t = 0; t < t_steady; ++t) step(t, Steady{}, P0{});
-            for (int t = t_steady; t < nk; ++t) step(t, Checked{}, P0{});
+            for (int t = 0; t < t_steady; ++t) step(t, Steady{}, P0{}, NoRun{});
+            for (int t = t_steady; t < nk; ++t) step(t, Checked{}, P0{}, NoRun{});
         } else {
             // steps in pairs, so that every step's parity (fragment sets, and
             // the scale register sets) is known at compile time; a steady
             // step left over before the checked ones runs checked
             int t = 0;
+            if constexpr (C::MX_LDS) {
+                // whole scale groups of steady steps, unrolled (SGS is even,
+                // so parities alternate within a run)
+                for (; t + SGS - 1 < t_steady; t += SGS)
+                    static_for<0, SGS>([&](auto k_tag) {
+                        constexpr int k = decltype(k_tag)::value;
+                        step(t + k, Steady{}, std::integral_constant<int, k % 2>{}, k_tag);
+                    });
+            }
             if constexpr (C::MB == 16 && !C::MX) {
                 // 16x16 blocks: single steady steps, the fragment set read for
                 // the next step copied into the contracted one (64 register
                 // moves a step); the two-step form makes the register
                 // allocator shuffle the 64 small accumulators instead
                 for (; t < t_steady; ++t) {
-                    step(t, Steady{}, P0{});
+                    step(t, Steady{}, P0{}, NoRun{});
                     fr[0] = fr[1];
                 }
             }
             for (; t + 1 < t_steady; t += 2) {
-                step(t, Steady{}, P0{});
-                step(t + 1, Steady{}, P1{});
+                step(t, Steady{}, P0{}, NoRun{});
+                step(t + 1, Steady{}, P1{}, NoRun{});
             }
             for (; t + 1 < nk; t += 2) {
-                step(t, Checked{}, P0{});
-                step(t + 1, Checked{}, P1{});
+                step(t, Checked{}, P0{}, NoRun{});
+                step(t + 1, Checked{}, P1{}, NoRun{});
             }
-            if (t < nk) step(t, Checked{}, P0{});
+            if (t < nk) step(t, Checked{}, P0{}, NoRun{});
         }
     } else if constexpr (C::DIRECT) {
         // Pipeline: S-1 stages in flight ahead of the one being contracted.
