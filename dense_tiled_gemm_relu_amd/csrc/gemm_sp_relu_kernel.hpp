@@ -376,9 +376,11 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_sp_relu_kernel(SpArgs arg
 #pragma unroll
         for (int j = 0; j < TN; ++j) read_b(0, 0, j);
     }
-    for (int t = 0; t < nk; ++t) {
+    // one step; STEADY: the stage S-1 ahead exists (no run-time checks)
+    auto step = [&](int t, auto steady_tag) {
+        constexpr bool STEADY = decltype(steady_tag)::value;
         const int stage = t % S;
-        const bool loads = t + S - 1 < nk;
+        const bool loads = STEADY || t + S - 1 < nk;
         const int ld_stage = (t + S - 1) % S;
 #pragma unroll
         for (int s = 0; s < KSUB; ++s) {
@@ -386,7 +388,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_sp_relu_kernel(SpArgs arg
             if (s + 1 < KSUB) {
                 next_stage = stage;
                 next_s = s + 1;
-            } else if (t + 1 < nk) {
+            } else if (STEADY || t + 1 < nk) {
                 if (loads)
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm(ALLOW));
                 else
@@ -411,7 +413,10 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_sp_relu_kernel(SpArgs arg
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-    }
+    };
+    const int t_steady = nk - (S - 1) > 0 ? nk - (S - 1) : 0;
+    for (int t = 0; t < t_steady; ++t) step(t, std::integral_constant<bool, true>{});
+    for (int t = t_steady; t < nk; ++t) step(t, std::integral_constant<bool, false>{});
     if (K % BK != 0) {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         barrier_lds();
