@@ -377,6 +377,22 @@ def table(gr):
         del keep, Cd
 
 
+def profile_workloads(gr, calls):
+    """`calls` synchronised calls of each workload in index order, nothing else
+    on the GPU in between: the dispatch list a counter run attributes to
+    workloads (printed as JSON, one line per workload)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for name in sorted(wl.WORKLOADS, key=lambda n: wl.WORKLOADS[n]["index"]):
+        call, Cd, plan, nbytes, keep = workload_call(gr, name, stream)
+        torch.cuda.synchronize()
+        for _ in range(calls):
+            call()
+            torch.cuda.synchronize()
+        print(json.dumps({"workload": name, "tile_config": plan, "calls": calls}), flush=True)
+        del keep, Cd
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -386,6 +402,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--table", action="store_true",
                     help="time every workload (warm and cold caches), one JSON line each")
+    ap.add_argument("--profile-workloads", type=int, default=0, metavar="CALLS",
+                    help="run CALLS synchronised calls of every workload (for counter runs under "
+                         "rocprofv3); prints the dispatch order")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only the plain copy used to scale HBM byte counters")
     ap.add_argument("--ingest-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"),
@@ -415,6 +434,9 @@ def main():
         __graft_entry__.build()
     if args.table:
         table(gr)
+        return
+    if args.profile_workloads:
+        profile_workloads(gr, args.profile_workloads)
         return
 
     w = dict(wl.WORKLOADS[args.workload], name=args.workload)
