@@ -20,6 +20,7 @@ enum ConfigId : int {
     CFG_D256x256x64_S2_16,
     CFG_D256x256x32_S4_I16,
     CFG_D256x256x32_S4_IP,
+    CFG_D256x256x32_S4_ISK,
     CFG_D256x256x32_S4_W8I,
     CFG_D256x256x32_S5_W8I,
     CFG_D256x256x64_S2_W8,
@@ -38,6 +39,7 @@ struct ConfigInfo {
     int bm, bn;
     bool direct;
     bool persistent = false;   // grid of min(tiles, CUs) workgroups looping over tiles
+    bool streamk = false;      // whole-tile workgroups, then stream-K units (workspace)
 };
 
 inline const ConfigInfo& config_info(int id)
@@ -50,6 +52,7 @@ inline const ConfigInfo& config_info(int id)
         {"d256x256x64_s2_16", 256, 256, true},
         {"d256x256x32_s4_i16", 256, 256, true},
         {"d256x256x32_s4_ip", 256, 256, true, true},
+        {"d256x256x32_s4_isk", 256, 256, true, false, true},
         {"d256x256x32_s4_w8i", 256, 256, true},
         {"d256x256x32_s5_w8i", 256, 256, true},
         {"d256x256x64_s2_w8", 256, 256, true},
@@ -103,6 +106,12 @@ template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4
 // per CU, each looping over its tiles (the Ascend version's T.Persistent).
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_IP> {
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 4, true, true, 32, true>;
+};
+// The default interleaved tile with its last round split along K (stream-K):
+// the tiles that do not fill a whole round of CUs share their K steps out
+// over all of them.
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_ISK> {
+    using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 4, true, true, 32, false, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_W8I> {
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 4, 4, true, true>;
@@ -169,7 +178,8 @@ LaunchFn launcher_i16(int in_dt, int out_dt, bool transB);
 // (the 16-bit comparison variants are not instantiated for them).
 inline bool fp8_config(int cfg)
 {
-    return cfg == CFG_D256x256x32_S4_I || cfg == CFG_D128x128x64_S3 || cfg == CFG_D64x64x64_S4 ||
+    return cfg == CFG_D256x256x32_S4_I || cfg == CFG_D256x256x32_S4_ISK ||
+           cfg == CFG_D128x128x64_S3 || cfg == CFG_D64x64x64_S4 ||
            cfg == CFG_D64x32x128_S4 || cfg == CFG_G128x128x64 || cfg == CFG_G64x64x64;
 }
 
@@ -197,6 +207,8 @@ inline bool fp8_config(int cfg)
             return launcher_i16(IN, OUT, TB);                                              \
         case CFG_D256x256x32_S4_IP:                                                        \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_IP>::type>;  \
+        case CFG_D256x256x32_S4_ISK:                                                       \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_ISK>::type>; \
         case CFG_D256x256x32_S4_W8I:                                                       \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_W8I>::type>; \
         case CFG_D256x256x32_S5_W8I:                                                       \
@@ -239,6 +251,8 @@ inline bool fp8_config(int cfg)
         switch (cfg) {                                                                     \
         case CFG_D256x256x32_S4_I:                                                         \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I>::type>;   \
+        case CFG_D256x256x32_S4_ISK:                                                       \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_ISK>::type>; \
         case CFG_D128x128x64_S3:                                                           \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D128x128x64_S3>::type>;     \
         case CFG_D128x128x64_S2:                                                           \

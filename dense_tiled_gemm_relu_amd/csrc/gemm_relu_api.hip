@@ -12,6 +12,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "configs.hpp"
 #include "gemm_relu.h"
@@ -34,6 +35,7 @@ struct Env {
     int force_cfg = -1;   // GEMM_RELU_FORCE_CONFIG=<name>
     int panel = 0;        // GEMM_RELU_PANEL=<tile rows>, 0 = default
     int nxcd = 8;         // GEMM_RELU_XCDS=<n>: 1 disables the XCD-aware tile remap
+    int sk_units = 0;     // GEMM_RELU_SK_UNITS=<n>: stream-K units, 0 = one per CU
 };
 
 // Debug and tuning switches, read on every call so a process can change them
@@ -52,6 +54,8 @@ Env env()
     if (p && p[0]) e.panel = std::atoi(p);
     const char* x = std::getenv("GEMM_RELU_XCDS");
     if (x && x[0]) e.nxcd = std::atoi(x) > 0 ? std::atoi(x) : 1;
+    const char* u = std::getenv("GEMM_RELU_SK_UNITS");
+    if (u && u[0]) e.sk_units = std::max(0, std::atoi(u));
     return e;
 }
 
@@ -96,7 +100,80 @@ struct Plan {
     bool empty = false;   // nothing to launch
     int cfg = -1;
     int tiles_m = 0, tiles_n = 0;
+    int dp_tiles = 0, sk_units = 0;   // stream-K configurations
 };
+
+// ---- stream-K split (the 256x256 interleaved tile, selected by name only):
+// whole rounds of tiles over the CUs keep one workgroup per tile; the
+// remaining tiles' K steps go to `units` workgroups, one per CU unless
+// GEMM_RELU_SK_UNITS sets the count.  Measured on MI355X it loses to one
+// workgroup per tile on every shape tried (the fp32 partials and the
+// cross-XCD cache write-back and invalidation cost more than the partly empty
+// last round), so plan selection never chooses it.
+constexpr int kSkMaxUnits = kNumCUs;    // the workspace holds 2 partials per unit
+
+struct SkSplit {
+    int dp_tiles = 0, units = 0;
+};
+
+SkSplit sk_split(int64_t tiles, int64_t iters, int forced_units)
+{
+    SkSplit sp;
+    int64_t dp = tiles / kNumCUs * kNumCUs, rest = tiles - dp;
+    if (rest == 0) {       // whole rounds: the last one as units of one tile each
+        dp -= kNumCUs;
+        rest = kNumCUs;
+    }
+    const int64_t total = rest * iters;
+    const int64_t want = forced_units > 0 ? forced_units : kSkMaxUnits;
+    sp.dp_tiles = int(dp);
+    sp.units = int(std::min<int64_t>({want, kSkMaxUnits, total}));
+    return sp;
+}
+
+// Stream-K workspace per (device, stream): two fp32 partial tiles per unit and
+// one arrival counter per split tile, counters zeroed once at allocation (the
+// kernel returns each to zero).  Calls on one stream are ordered, so they can
+// share it; calls on different streams get different ones.  Allocated on a
+// stream's first stream-K call, never while the stream is being captured into
+// a graph (the call then uses whole tiles), and kept until the process ends.
+constexpr size_t kSkFlagBytes = 4 * kNumCUs;
+constexpr size_t kSkSlotBytes = size_t(256) * 256 * 4;
+constexpr size_t kSkWsBytes = kSkFlagBytes + 2 * size_t(kSkMaxUnits) * kSkSlotBytes;
+constexpr int kSkMaxPerDevice = 16;
+
+struct SkWorkspace {
+    int dev;
+    hipStream_t stream;
+    unsigned char* base;
+};
+std::mutex g_ws_mu;
+std::vector<SkWorkspace> g_ws;
+
+unsigned char* sk_workspace(int dev, hipStream_t st)
+{
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    int on_dev = 0;
+    for (const SkWorkspace& w : g_ws) {
+        if (w.dev == dev && w.stream == st) return w.base;
+        on_dev += w.dev == dev;
+    }
+    if (on_dev >= kSkMaxPerDevice) return nullptr;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return nullptr;
+    void* p = nullptr;
+    if (hipMalloc(&p, kSkWsBytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (hipMemsetAsync(p, 0, kSkFlagBytes, st) != hipSuccess) {
+        (void)hipFree(p);
+        return nullptr;
+    }
+    g_ws.push_back({dev, st, static_cast<unsigned char*>(p)});
+    return static_cast<unsigned char*>(p);
+}
 
 // A direct-copy configuration needs its 32-bit copy offsets to fit (a tile's
 // rows of A or transposed B span BM * K * 2 bytes; a (K,N) B step spans
@@ -113,7 +190,7 @@ bool direct_fits(int id, int64_t N, int64_t K, int transB)
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
-               int in_dt, int out_dt, int transB, const Env& e)
+               int in_dt, int out_dt, int transB, const Env& e, bool sk_ok = true)
 {
     Plan p;
     const int64_t lim = INT32_MAX;
@@ -153,8 +230,13 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     }
 
     auto tiles = [&](int id) { return ceil_div(M, config_info(id).bm) * ceil_div(N, config_info(id).bn); };
+    // K steps of the 256x256x32 tile (64 elements a step for 8-bit inputs);
+    // a stream-K split needs at least two
+    const int64_t sk_iters = ceil_div(K, fp8_input(in_dt) ? 64 : 32);
+    const bool sk_possible = sk_ok && sk_iters >= 2;
     auto usable = [&](int id) {
         return id != CFG_D256x128x64_S2 &&             // built for block-scaled inputs only
+               (id != CFG_D256x256x32_S4_ISK || sk_possible) &&
                direct_fits(id, N, K, transB) && (!fp8_input(in_dt) || fp8_config(id));
     };
     // Estimated time of a direct configuration, per K: rounds of workgroups
@@ -186,6 +268,11 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     p.cfg = cfg;
     p.tiles_m = int(tm);
     p.tiles_n = int(tn);
+    if (config_info(cfg).streamk) {
+        const SkSplit sp = sk_split(tm * tn, sk_iters, e.sk_units);
+        p.dp_tiles = sp.dp_tiles;
+        p.sk_units = sp.units;
+    }
     return p;
 }
 
@@ -347,13 +434,21 @@ extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64
                          int in_dtype, int out_dtype, int transB, void* stream)
 {
     const Env e = env();
-    const Plan p = make_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB, e);
+    Plan p = make_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB, e);
     if (p.status != GEMM_RELU_OK) return p.status;
     if (p.empty) return GEMM_RELU_OK;
     const int dev = check_device();
     if (dev != GEMM_RELU_OK) return dev;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    unsigned char* ws = nullptr;
+    if (config_info(p.cfg).streamk) {
+        int d = 0;
+        if (hipGetDevice(&d) != hipSuccess) return GEMM_RELU_EHIP;
+        ws = sk_workspace(d, st);
+        if (!ws) p = make_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB, e, false);
+    }
 
-    KernelArgs args;
+    KernelArgs args{};
     args.A = static_cast<const unsigned char*>(A);
     args.B = static_cast<const unsigned char*>(B);
     args.C = static_cast<unsigned char*>(C);
@@ -368,12 +463,19 @@ extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64
     args.SA = nullptr;
     args.SB = nullptr;
     args.KB = 0;
+    if (config_info(p.cfg).streamk) {
+        args.flags = reinterpret_cast<unsigned*>(ws);
+        args.ws = reinterpret_cast<float*>(ws + kSkFlagBytes);
+        args.dp_tiles = p.dp_tiles;
+        args.sk_units = p.sk_units;
+    }
 
     LaunchFn fn = pick_launcher(in_dtype, out_dtype, transB, p.cfg);
     if (!fn) return GEMM_RELU_EUNSUPPORTED;
-    hipStream_t st = static_cast<hipStream_t>(stream);
     const int tiles = p.tiles_m * p.tiles_n;
-    const int grid = config_info(p.cfg).persistent ? std::min(tiles, kNumCUs) : tiles;
+    const int grid = config_info(p.cfg).persistent ? std::min(tiles, kNumCUs)
+                     : config_info(p.cfg).streamk  ? p.dp_tiles + p.sk_units
+                                                   : tiles;
     if (fn(args, grid, st) != hipSuccess) return GEMM_RELU_EHIP;
     if (e.sync) {
         if (hipStreamSynchronize(st) != hipSuccess) return GEMM_RELU_EHIP;
@@ -414,7 +516,7 @@ extern "C" int gemm_relu_mx(const void* A, const void* SA, const void* B, const 
     const int dev = check_device();
     if (dev != GEMM_RELU_OK) return dev;
 
-    KernelArgs args;
+    KernelArgs args{};
     args.A = static_cast<const unsigned char*>(A);
     args.B = static_cast<const unsigned char*>(B);
     args.C = static_cast<unsigned char*>(C);

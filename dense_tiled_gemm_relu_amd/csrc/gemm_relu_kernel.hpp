@@ -71,6 +71,13 @@ struct KernelArgs {
     const unsigned char* SB;  // (N, KB) E8M0 scales of B (stored (N, K))
     int KB;                   // scale blocks per row (K elements / 32)
     int nxcd;                 // XCDs the dispatcher round-robins over (1 = no remap)
+    // Stream-K configurations: workgroups [0, dp_tiles) take whole tiles; the
+    // next sk_units split the K steps of the remaining tiles evenly.  ws holds
+    // 2 sk_units fp32 partial tiles (BM x BN each), flags one arrival counter
+    // per split tile, zero between launches.
+    float* ws;
+    unsigned* flags;
+    int dp_tiles, sk_units;
 };
 
 // ------------------------------------------------------------------ helpers
@@ -277,9 +284,10 @@ template <> struct OutTraits<DT_F32> {
 // ---------------------------------------------------------- configuration
 template <int IN_DT_, int OUT_DT_, bool TRANS_B_, int BM_, int BN_, int BK_, int WAVES_M_,
           int WAVES_N_, int STAGES_, bool DIRECT_, bool INTERLEAVE_ = false, int MB_ = 32,
-          bool PERSISTENT_ = false>
+          bool PERSISTENT_ = false, bool STREAMK_ = false>
 struct Cfg {
     static constexpr bool PERSISTENT = PERSISTENT_;   // tile loop over a grid of <= 1 per CU
+    static constexpr bool STREAMK = STREAMK_;         // last round split along K
     static constexpr int IN_DT = IN_DT_, OUT_DT = OUT_DT_;
     static constexpr bool TRANS_B = TRANS_B_, DIRECT = DIRECT_, INTERLEAVE = INTERLEAVE_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
@@ -339,6 +347,8 @@ struct Cfg {
     static_assert(STAGES >= 2 && STAGES <= 5, "stages");
     static_assert((STAGES - 2) * LOADS_PER_STAGE + SC_COPIES < 64, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity of a gfx950 CU");
+    static_assert(!STREAMK_ || (INTERLEAVE_ && !MX && !PERSISTENT_),
+                  "stream-K: the interleaved pipeline, unscaled inputs");
 
     // Interleaved direct pipeline: the LOADS_PER_STAGE copies of the stage
     // STAGES-1 ahead are spread over the KSUB k-steps of a BK step, one per
@@ -426,12 +436,38 @@ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, in
     tn = within / rows;
 }
 
+// One stream-K piece: the K steps [kt0, kt1) (of ceil(K / BK)) of a tile that
+// count pieces share.  Pieces are numbered in K order; piece p > 0 is the first
+// piece of unit first + p and keeps its partial in that unit's slot 2 (first +
+// p); piece 0 keeps it in slot0 (its unit's second slot when the unit began in
+// an earlier tile).
+struct SkPiece {
+    int kt0, kt1;
+    int tile;      // split-tile index (its arrival counter)
+    int count;     // pieces of the tile; 1: the piece is the whole tile
+    int pos;       // this piece's number
+    int first;     // unit of piece 0
+    int slot0;     // partial slot of piece 0
+};
+// A workgroup's stream-K state, kept in LDS so that none of it occupies
+// registers across the main loop (which needs all of them): the current
+// piece, its tile's launch-order index, and the unit's remaining steps.
+struct SkState {
+    SkPiece pc;
+    int wg;
+    int lo, hi;
+    int arrived;   // the piece's arrival count, for the whole workgroup
+};
+
 // ------------------------------------------------------------- the kernel
 // One output tile: the tile with launch-order index wg (see tile_coords), its
 // accumulator cleared, its whole K range contracted, the ReLU epilogue stored.
+// Stream-K configurations contract the piece pc of it instead; see
+// gemm_relu_kernel for how a tile's pieces are combined.
 template <class C>
 __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
-                                               GR_LDS unsigned char* smem)
+                                               GR_LDS unsigned char* smem,
+                                               GR_LDS SkState* sk = nullptr)
 {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::STAGES;
     constexpr int TM = C::TM, TN = C::TN, KSUB = C::KSUB;
@@ -450,12 +486,19 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
     tile_coords(wg, args.tiles_m, args.tiles_n, args.panel, args.nxcd, tm, tn);
     const int m0 = tm * BM;
     // (K,N) B on the direct path: the last tile column is moved back to end at N,
-    // so every B chunk it copies lies inside its row (the columns it shares with
-    // its neighbour are recomputed bit for bit and stored twice).
+    // so every B chunk it copies lies inside its row.  The columns it shares with
+    // its neighbour are recomputed but stored by the neighbour only (n_own is the
+    // tile's first stored column): each element of C has one writer, so results
+    // do not depend on which tile finishes last, even when the two tiles sum
+    // their K range in different pieces.
     const int n0 = (C::DIRECT && !C::TRANS_B) ? min(tn * BN, N - BN) : tn * BN;
+    const int n_own = tn * BN;
     // Direct path: K / BK full steps through the copy pipeline plus, if K % BK,
     // one register-staged tail step.  Register-staged path: ceil(K / BK) steps.
-    const int nk = C::DIRECT ? K / BK : (K + BK - 1) / BK;
+    // A stream-K piece: its full steps from kt0 on, and the tail step if it
+    // ends the K range.
+    const int kt0 = C::STREAMK ? sk->pc.kt0 : 0;
+    const int nk = C::STREAMK ? min(sk->pc.kt1, K / BK) - kt0 : C::DIRECT ? K / BK : (K + BK - 1) / BK;
 
     // ---- loader geometry: this thread owns LDS slots q = i*NTHREADS + tid of
     // each stage region; a wave's 64 slots are contiguous (one 1 KiB DMA write).
@@ -494,9 +537,11 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
         }
     }
 
-    const unsigned char* a_tile = args.A + (size_t)m0 * (size_t)K * EB;
-    const unsigned char* b_tile = C::TRANS_B ? args.B + (size_t)n0 * (size_t)K * EB
-                                             : args.B + (size_t)n0 * EB;
+    // origins of the tile's A rows and B columns at the first K step
+    const unsigned char* a_tile = args.A + (size_t)m0 * (size_t)K * EB + (size_t)kt0 * BK * EB;
+    const unsigned char* b_tile = C::TRANS_B
+                                      ? args.B + (size_t)n0 * (size_t)K * EB + (size_t)kt0 * BK * EB
+                                      : args.B + (size_t)n0 * EB + (size_t)kt0 * BK * (size_t)N * EB;
 
     // ---- direct loader: global -> LDS without registers.
     const uint32_t smem_addr = lds_addr(smem);
@@ -1089,11 +1134,11 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
     if constexpr (C::DIRECT) {
         // K tail (K % BK != 0): one register-staged step with element-wise zero
         // fill past K, after every wave has left the copy ring.
-        if (K % BK != 0) {
+        if (C::STREAMK ? (K % BK != 0 && sk->pc.kt1 > K / BK) : K % BK != 0) {
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             barrier_lds();
             if constexpr (C::MX) load_scales_tail(nk, sc_cur);
-            fill_staged(nk, 0);
+            fill_staged(kt0 + nk, 0);
             barrier_lds();
             read_frags(0, 0, fr[0]);
 #pragma unroll
@@ -1123,37 +1168,161 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
         }
     }
 
+    // ---- stream-K: a piece that is not the whole tile publishes its fp32
+    // partial; the piece that arrives last at the tile's counter stores the
+    // tile from the sum of all of them, read back in piece order.  (Summing
+    // from memory leaves the accumulators to the matrix instructions alone:
+    // vector adds into them make the compiler split them over both register
+    // files and shuffle them every main-loop step.)
+    constexpr int NQ = NACC / 4;                 // 4-float groups per block
+    bool from_partials = false;
+    // partial layout: group v = (i TN + j) NQ + q of thread tid at float4 index
+    // v NTHREADS + tid (each wave writes and reads whole 1 KiB lines)
+    auto slot_of = [&](int p) {
+        const GR_LDS SkPiece* pc = &sk->pc;
+        const int s = p == 0 ? pc->slot0 : 2 * (pc->first + p);
+        return reinterpret_cast<f32x4_t*>(args.ws + (size_t)s * (BM * BN)) + tid;
+    };
+    if constexpr (C::STREAMK) {
+        const GR_LDS SkPiece* pc = &sk->pc;
+        if (pc->count > 1) {
+            f32x4_t* own = slot_of(pc->pos);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                           acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                        own[((i * TN + j) * NQ + q) * C::NTHREADS] = v;
+                    }
+            // every wave's stores reach device scope before the count is taken
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __builtin_amdgcn_s_barrier();
+            if (tid == 0)
+                sk->arrived = (int)__hip_atomic_fetch_add(args.flags + pc->tile, 1u, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+            barrier_lds();
+            if (sk->arrived + 1 != pc->count) return;     // a later piece completes the tile
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            if (tid == 0)
+                __hip_atomic_store(args.flags + pc->tile, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            from_partials = true;
+        }
+    }
+
     // ---- epilogue: ReLU on the fp32 accumulators, convert, store.
     // Lane owns C[m][n .. n+3] with m = m0 + wm0 + MB i + lr and
     // n = n0 + wn0 + MB j + 4 NG q + 4 g, for q < NACC / 4 (registers 4q .. 4q+3).
+    // 16-bit C: the tile goes through the (now idle) LDS ring so that the
+    // global stores are whole rows, 16 bytes per lane, instead of 8-byte
+    // pieces of 32 different rows.  Row r of the staged tile keeps its 16-byte
+    // chunk c at c ^ (r mod 16) (mod the row's chunk count when shorter):
+    // conflict-free row reads, 2-way writes.  Otherwise (fp32 C, or a tile
+    // larger than the ring): four values inside the row go out as one 8- or
+    // 16-byte store (any element alignment: unaligned-access mode); a row's
+    // last partial group element-wise.
     constexpr int OB = OutTraits<C::OUT_DT>::bytes;
-    if constexpr (OB == 2 && BM * BN * 2 <= C::LDS_BYTES) {
-        // 16-bit C: the tile goes through the (now idle) LDS ring so that the
-        // global stores are whole rows, 16 bytes per lane, instead of 8-byte
-        // pieces of 32 different rows.  Row r of the staged tile keeps its
-        // 16-byte chunk c at c ^ (r mod 16) (mod the row's chunk count when
-        // shorter): conflict-free row reads, 2-way writes.
-        constexpr int RB = BN * 2, RCH = BN / 8;          // bytes and chunks per tile row
-        constexpr int XM = (RCH < 16 ? RCH : 16) - 1;
+    constexpr bool STAGED = OB == 2 && BM * BN * 2 <= C::LDS_BYTES;
+    constexpr int RB = BN * 2, RCH = BN / 8;          // staged: bytes and chunks per tile row
+    constexpr int XM = (RCH < 16 ? RCH : 16) - 1;
+    auto put_group = [&](int i, int j, int q, const f32x4_t& x) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = relu(x[e]);
+        if constexpr (STAGED) {
+            const int r = wm0 + MB * i + lr;
+            const int c = wn0 + MB * j + 4 * NG * q + 4 * g;
+            unsigned short h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = OutTraits<C::OUT_DT>::cvt(v[e]);
+            const u32x2_t w = {h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16)};
+            *reinterpret_cast<GR_LDS u32x2_t*>(smem + r * RB + (((c >> 3) ^ (r & XM)) << 4) +
+                                               (c & 7) * 2) = w;
+        } else {
+            const int m = m0 + wm0 + MB * i + lr;
+            const int n = n0 + wn0 + MB * j + 4 * NG * q + 4 * g;
+            if (m >= M || n >= N || n + 4 <= n_own) return;
+            unsigned char* crow = args.C + (size_t)m * (size_t)N * OB;
+            const bool whole = n >= n_own && n + 4 <= N;
+            if constexpr (C::OUT_DT == DT_F32) {
+                float* dst = reinterpret_cast<float*>(crow) + n;
+                if (whole) {
+                    const u32x4_t w = {__builtin_bit_cast(unsigned, v[0]), __builtin_bit_cast(unsigned, v[1]),
+                                       __builtin_bit_cast(unsigned, v[2]), __builtin_bit_cast(unsigned, v[3])};
+                    __builtin_memcpy(dst, &w, 16);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e >= n_own && n + e < N) dst[e] = v[e];
+                }
+            } else {
+                unsigned short h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = OutTraits<C::OUT_DT>::cvt(v[e]);
+                unsigned short* dst = reinterpret_cast<unsigned short*>(crow) + n;
+                if (whole) {
+                    const u32x2_t w = {h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16)};
+                    __builtin_memcpy(dst, &w, 8);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e >= n_own && n + e < N) dst[e] = h[e];
+                }
+            }
+        }
+    };
+    if constexpr (STAGED) {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         barrier_lds();
+    }
+    auto put_acc = [&] {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = wm0 + MB * i + lr;
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int q = 0; q < NACC / 4; ++q) {
-                    const int c = wn0 + MB * j + 4 * NG * q + 4 * g;
-                    unsigned short h[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        h[e] = OutTraits<C::OUT_DT>::cvt(relu(acc[i][j][4 * q + e]));
-                    const u32x2_t w = {h[0] | ((unsigned)h[1] << 16), h[2] | ((unsigned)h[3] << 16)};
-                    *reinterpret_cast<GR_LDS u32x2_t*>(
-                        smem + r * RB + (((c >> 3) ^ (r & XM)) << 4) + (c & 7) * 2) = w;
+                for (int q = 0; q < NQ; ++q) {
+                    const f32x4_t x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                       acc[i][j][4 * q + 3]};
+                    put_group(i, j, q, x);
                 }
+    };
+    if constexpr (C::STREAMK) {
+        if (from_partials) {
+            // groups of VB: the sum p_0 + p_1 + ... of each, then its stores
+            constexpr int NV = TM * TN * NQ, VB = 16;
+            static_assert(NV % VB == 0, "partial load batches");
+            const int count = sk->pc.count;
+#pragma unroll
+            for (int c = 0; c < NV; c += VB) {
+                const f32x4_t* s0 = slot_of(0);
+                f32x4_t sum[VB];
+#pragma unroll
+                for (int k = 0; k < VB; ++k) sum[k] = s0[(c + k) * C::NTHREADS];
+                for (int p = 1; p < count; ++p) {
+                    const f32x4_t* sp = slot_of(p);
+                    f32x4_t x[VB];
+#pragma unroll
+                    for (int k = 0; k < VB; ++k) x[k] = sp[(c + k) * C::NTHREADS];
+#pragma unroll
+                    for (int k = 0; k < VB; ++k) sum[k] += x[k];
+                }
+#pragma unroll
+                for (int k = 0; k < VB; ++k) {
+                    const int v = c + k, b = v / NQ;
+                    put_group(b / TN, b % TN, v % NQ, sum[k]);
+                }
+            }
+        } else {
+            put_acc();
         }
+    } else {
+        put_acc();
+    }
+    if constexpr (STAGED) {
         barrier_lds();
         constexpr int ROWS_PER_PASS = C::NTHREADS / RCH;
         static_assert(C::NTHREADS % RCH == 0 && BM % ROWS_PER_PASS == 0, "epilogue row passes");
@@ -1161,65 +1330,17 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
 #pragma unroll 4
         for (int r = tid / RCH; r < BM; r += ROWS_PER_PASS) {
             const int m = m0 + r, n = n0 + 8 * cc;
-            if (m >= M || n >= N) continue;
+            if (m >= M || n >= N || n + 8 <= n_own) continue;
             const u32x4_t v = *reinterpret_cast<const GR_LDS u32x4_t*>(
                 smem + r * RB + ((cc ^ (r & XM)) << 4));
             unsigned short* dst = reinterpret_cast<unsigned short*>(args.C) + (size_t)m * N + n;
-            if (n + 8 <= N) {
+            if (n >= n_own && n + 8 <= N) {
                 __builtin_memcpy(dst, &v, 16);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    if (n + e < N) dst[e] = (unsigned short)(v[e >> 1] >> (16 * (e & 1)));
-            }
-        }
-        return;
-    }
-    // Otherwise (fp32 C, or a tile larger than the ring): four values inside the
-    // row go out as one 8- or 16-byte store (any element alignment:
-    // unaligned-access mode); a row's last partial group element-wise.
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int m = m0 + wm0 + MB * i + lr;
-        if (m >= M) continue;
-        unsigned char* crow = args.C + (size_t)m * (size_t)N * OB;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-#pragma unroll
-            for (int q = 0; q < NACC / 4; ++q) {
-                const int n = n0 + wn0 + MB * j + 4 * NG * q + 4 * g;
-                if (n >= N) continue;
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = relu(acc[i][j][4 * q + e]);
-                if constexpr (C::OUT_DT == DT_F32) {
-                    float* dst = reinterpret_cast<float*>(crow) + n;
-                    if (n + 4 <= N) {
-                        const u32x4_t w = {__builtin_bit_cast(unsigned, v[0]),
-                                           __builtin_bit_cast(unsigned, v[1]),
-                                           __builtin_bit_cast(unsigned, v[2]),
-                                           __builtin_bit_cast(unsigned, v[3])};
-                        __builtin_memcpy(dst, &w, 16);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < N) dst[e] = v[e];
-                    }
-                } else {
-                    unsigned short h[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) h[e] = OutTraits<C::OUT_DT>::cvt(v[e]);
-                    unsigned short* dst = reinterpret_cast<unsigned short*>(crow) + n;
-                    if (n + 4 <= N) {
-                        const u32x2_t w = {h[0] | ((unsigned)h[1] << 16),
-                                           h[2] | ((unsigned)h[3] << 16)};
-                        __builtin_memcpy(dst, &w, 8);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < N) dst[e] = h[e];
-                    }
-                }
+                    if (n + e >= n_own && n + e < N)
+                        dst[e] = (unsigned short)(v[e >> 1] >> (16 * (e & 1)));
             }
         }
     }
@@ -1231,12 +1352,80 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
 // accumulator is cleared per tile, and a barrier after each tile keeps the
 // next tile's copies off the LDS the epilogue may still be reading.  A grid
 // that is a multiple of 8 keeps every tile of a workgroup on its XCD.
+//
+// Stream-K configurations (the published Stream-K decomposition, Osama et al.,
+// 2023, in its data-parallel + stream-K hybrid): the first dp_tiles workgroups
+// take whole tiles; the remaining tiles' K steps, ceil(K / BK) per tile, are
+// laid end to end and split into sk_units near-equal ranges, one per further
+// workgroup.  A range crosses at most a few tile boundaries; each part of it in
+// one tile is a piece.  Pieces never wait for one another: each publishes its
+// partial and counts itself in at the tile's counter, and the last to arrive
+// finishes the tile, so no workgroup depends on another being resident.
 template <class C>
 __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs args)
 {
     __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[C::LDS_BYTES];
     GR_LDS unsigned char* smem = (GR_LDS unsigned char*)(smem_raw);
-    if constexpr (C::PERSISTENT) {
+    if constexpr (C::STREAMK) {
+        __shared__ SkState sk_raw;
+        GR_LDS SkState* sk = (GR_LDS SkState*)(&sk_raw);
+        const int iters = (args.K + C::BK - 1) / C::BK;
+        const int u = (int)blockIdx.x - args.dp_tiles;
+        // unit w takes steps [lo(w), lo(w + 1)) of the split tiles' sequence;
+        // a whole-tile workgroup (u < 0) runs the loop once over its tile
+        auto split = [&](int& q, int& r) {
+            const int total = (args.tiles_m * args.tiles_n - args.dp_tiles) * iters;
+            q = total / args.sk_units;
+            r = total % args.sk_units;
+        };
+        if (threadIdx.x == 0) {
+            int q, r;
+            split(q, r);
+            sk->lo = u < 0 ? 0 : u * q + min(u, r);
+            sk->hi = u < 0 ? iters : (u + 1) * q + min(u + 1, r);
+        }
+        for (;;) {
+            barrier_lds();      // the state is written; the last tile's epilogue is done with LDS
+            const int lo = sk->lo, hi = sk->hi;
+            if (lo >= hi) break;
+            barrier_lds();      // every wave has read lo before thread 0 advances it
+            if (threadIdx.x == 0) {
+                SkPiece pc;
+                if (u < 0) {
+                    pc = SkPiece{0, iters, 0, 1, 0, 0, 0};
+                    sk->wg = blockIdx.x;
+                } else {
+                    int q, r;
+                    split(q, r);
+                    auto lo_of = [&](int w) { return w * q + min(w, r); };
+                    auto unit_of = [&](int x) {
+                        return x < r * (q + 1) ? x / (q + 1) : r + (x - r * (q + 1)) / q;
+                    };
+                    const int t = lo / iters, t0 = t * iters;
+                    pc.kt0 = lo - t0;
+                    pc.kt1 = min(iters, pc.kt0 + hi - lo);
+                    pc.tile = t;
+                    pc.first = unit_of(t0);
+                    pc.count = unit_of(t0 + iters - 1) - pc.first + 1;
+                    pc.pos = u - pc.first;
+                    pc.slot0 = 2 * pc.first + (lo_of(pc.first) < t0 ? 1 : 0);
+                    sk->wg = args.dp_tiles + t;
+                }
+                // field by field: no assignment operator into an LDS object
+                sk->pc.kt0 = pc.kt0;
+                sk->pc.kt1 = pc.kt1;
+                sk->pc.tile = pc.tile;
+                sk->pc.count = pc.count;
+                sk->pc.pos = pc.pos;
+                sk->pc.first = pc.first;
+                sk->pc.slot0 = pc.slot0;
+                sk->lo = lo + pc.kt1 - pc.kt0;
+            }
+            barrier_lds();
+            gemm_relu_tile<C>(args, sk->wg, smem, sk);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        }
+    } else if constexpr (C::PERSISTENT) {
         const int total = args.tiles_m * args.tiles_n;
         for (int wg = blockIdx.x; wg < total; wg += gridDim.x) {
             gemm_relu_tile<C>(args, wg, smem);

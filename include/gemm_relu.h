@@ -72,7 +72,13 @@ extern "C" {
  * nearest-even into out_dtype.
  *
  * Ownership: the caller owns A, B and C; the library keeps no pointer after the
- * call returns and allocates no device memory.
+ * call returns and allocates no device memory, except with the stream-K
+ * comparison configuration (chosen only by name, GEMM_RELU_FORCE_CONFIG=
+ * d256x256x32_s4_isk): its first call on a stream allocates and zeroes a
+ * 128 MiB workspace for that stream (fp32 partial tiles and arrival counters),
+ * kept until the process ends.  Calls on one stream share it in stream order;
+ * a call on a stream that is being captured into a graph and has no workspace
+ * yet takes whole tiles instead.
  *
  * Execution: asynchronous on `stream`; the call returns after the launch.  A
  * device-side fault surfaces at the caller's next synchronisation.  With the

@@ -242,3 +242,19 @@ def test_comparison_configurations_are_selectable(monkeypatch, name):
     assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0) == name
     assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 1, 2, 1) == name
     assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 3, 0, 0) == "d256x256x32_s4_i"
+
+
+def test_streamk_selection(monkeypatch):
+    """Stream-K (the 256x256 tile with its last round split along K) is
+    selected by name only, for 16-bit and 8-bit inputs with at least two K
+    steps a tile; never chosen automatically; not built for block-scaled inputs."""
+    for shape in [(4096, 7168, 4096), (4097, 3001, 5003), (3000, 3000, 3000)]:
+        assert gr.gemm_relu_plan(A, B, C, *shape, 0, 0, 0) != "d256x256x32_s4_isk"
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x256x32_s4_isk")
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0) == "d256x256x32_s4_isk"
+    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == "d256x256x32_s4_isk"
+    assert gr.gemm_relu_plan(A, B, C, 512, 512, 64, 0, 0, 0) == "d256x256x32_s4_isk"
+    assert gr.gemm_relu_plan(A, B, C, 512, 512, 32, 0, 0, 0) != "d256x256x32_s4_isk"
+    assert gr.gemm_relu_plan(A, B, C, 512, 512, 128, 3, 0, 0) == "d256x256x32_s4_isk"
+    assert gr.gemm_relu_plan(A, B, C, 512, 512, 64, 3, 0, 0) != "d256x256x32_s4_isk"
+    assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 8192, 8192, 8192, 7, 0) == "d256x256x32_s4_i"

@@ -21,7 +21,8 @@ from tests.helpers import (check_close, from_device, fp32_sum_bound, out_tensor,
 pytestmark = pytest.mark.gpu
 
 DIRECT = ["d256x256x64_s2", "d256x256x32_s4", "d256x256x32_s5", "d256x256x32_s4_i",
-          "d256x256x64_s2_16", "d256x256x32_s4_i16", "d256x256x32_s4_ip", "d256x256x32_s4_w8i",
+          "d256x256x64_s2_16", "d256x256x32_s4_i16", "d256x256x32_s4_ip", "d256x256x32_s4_isk",
+          "d256x256x32_s4_w8i",
           "d256x256x32_s5_w8i", "d256x256x64_s2_w8", "d128x128x64_s3", "d64x64x64_s4",
           "d64x32x128_s4"]
 STAGED = ["g128x128x64", "g64x64x64"]
@@ -37,13 +38,19 @@ def _gpu():
 
 BN_OF = {"d256x256x64_s2": 256, "d256x256x32_s4": 256, "d256x256x32_s5": 256,
          "d256x256x32_s4_i": 256, "d256x256x64_s2_16": 256, "d256x256x32_s4_i16": 256, "d256x256x32_s4_ip": 256,
+         "d256x256x32_s4_isk": 256,
          "d256x256x32_s4_w8i": 256, "d256x256x32_s5_w8i": 256,
          "d256x256x64_s2_w8": 256, "d128x128x64_s3": 128, "d64x64x64_s4": 64,
          "d64x32x128_s4": 32}
 
 
-def usable(cfg, N, transB):
-    """Direct-copy configurations need a full tile of columns of a (K,N) B."""
+def usable(cfg, N, transB, K=None, in_code=wl.F16):
+    """Direct-copy configurations need a full tile of columns of a (K,N) B; the
+    stream-K one at least two K steps (32 elements, 64 for 8-bit inputs)."""
+    if cfg == "d256x256x32_s4_isk" and K is not None:
+        step = 64 if in_code in (wl.F8E4M3, wl.F8E5M2) else 32
+        if -(-K // step) < 2:
+            return False
     return cfg not in BN_OF or transB or N >= BN_OF[cfg]
 
 
@@ -129,7 +136,8 @@ def test_coded_mapping(cfg, transB, monkeypatch):
 
 
 # ----------------------------------------------------------- 8-bit inputs
-FP8_CONFIGS = ["d256x256x32_s4_i", "d128x128x64_s3", "d64x64x64_s4", "d64x32x128_s4",
+FP8_CONFIGS = ["d256x256x32_s4_i", "d256x256x32_s4_isk", "d128x128x64_s3", "d64x64x64_s4",
+               "d64x32x128_s4",
                "g128x128x64", "g64x64x64"]
 FP8 = [wl.F8E4M3, wl.F8E5M2]
 
@@ -243,8 +251,8 @@ def test_tail_sweep_integer(M, N, K, transB):
 @pytest.mark.parametrize("M,N,K", [(1, 8, 8), (65, 72, 136), (33, 200, 520), (300, 16, 64),
                                    (70, 300, 24), (257, 263, 1), (5, 259, 37)])
 def test_tail_shapes_every_config(cfg, M, N, K, monkeypatch):
-    if not usable(cfg, N, 0):
-        pytest.skip("needs a full tile of B columns")
+    if not usable(cfg, N, 0, K, wl.BF16):
+        pytest.skip("needs a full tile of B columns (stream-K: two K steps)")
     A, B = int_inputs(M, N, K, wl.BF16, 0, 400 + M, wl.F32)
     ref = oracle.gemm_relu_ref(A, B, M, N, K, wl.BF16, 0)
     got = run(A, B, M, N, K, wl.BF16, wl.F32, 0, cfg, monkeypatch)
