@@ -45,6 +45,28 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+
+
+def roofline(flops, nbytes, kernel_ms, peak_tflops, traffic):
+    """The roofline record of one launch: MFMA-bound when the algorithmic
+    intensity (flops per algorithmic byte) is above the ridge point of the input
+    type's peak and 8 TB/s, HBM-bound below it (achieved = algorithmic bytes per
+    launch over the launch's duration)."""
+    ridge = peak_tflops * 1e12 / (HBM_PEAK_GBS * 1e9)
+    rec = {"intensity": round(flops / nbytes, 1), "ridge": round(ridge, 1)}
+    if flops / nbytes >= ridge:
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
+        rec.update(bound="mfma", achieved=round(achieved, 2), peak=peak_tflops, unit="TFLOP/s",
+                   frac=round(achieved / peak_tflops, 4))
+    else:
+        achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+        rec.update(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                   frac=round(achieved / HBM_PEAK_GBS, 4))
+    rec.update(traffic=traffic, algorithmic_bytes=int(nbytes), kernel_ms=round(kernel_ms, 5))
+    return rec
+
+
 def measured_traffic(workload, launches_per_record=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
@@ -490,11 +512,7 @@ def main():
         "config": {"workload": args.workload, "M": M, "N": N, "K": K,
                    "in": wl.DTYPE_NAMES[ic], "out": wl.DTYPE_NAMES[oc], "transB": tb,
                    "accumulate": "f32", "inputs": w["dist"], "tile_config": plan},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(args.workload),
-                     "algorithmic_bytes": int(nbytes),
-                     "kernel_ms": round(kernel_ms, 5)},
+        "roofline": roofline(flops, nbytes, kernel_ms, peak, measured_traffic(args.workload)),
     }
     ceiling = mfma_ceiling(gr, stream, kind=ceiling_kind(ic, sparse))
     if ceiling is not None:

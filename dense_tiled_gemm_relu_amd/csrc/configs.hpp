@@ -29,6 +29,7 @@ enum ConfigId : int {
     CFG_D256x128x64_S2,
     CFG_D64x64x64_S4,
     CFG_D64x32x128_S4,
+    CFG_D32x64x128_S4,
     CFG_G128x128x64,
     CFG_G64x64x64,
     CFG_COUNT
@@ -61,6 +62,7 @@ inline const ConfigInfo& config_info(int id)
         {"d256x128x64_s2", 256, 128, true},
         {"d64x64x64_s4", 64, 64, true},
         {"d64x32x128_s4", 64, 32, true},
+        {"d32x64x128_s4", 32, 64, true},
         {"g128x128x64", 128, 128, false},
         {"g64x64x64", 64, 64, false},
     };
@@ -142,6 +144,11 @@ template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D64x64x64_S4> 
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D64x32x128_S4> {
     using type = Cfg<IN, OUT, TB, 64, 32, bk_of<IN, 128>, 2, 1, 4, true>;
 };
+// Skinny problems, the other way round: 32 rows by 64 columns, so each k row
+// of a (K,N) B tile is one whole 128-byte line; two waves side by side in N.
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D32x64x128_S4> {
+    using type = Cfg<IN, OUT, TB, 32, 64, bk_of<IN, 128>, 1, 2, 4, true>;
+};
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_G128x128x64> {
     using type = Cfg<IN, OUT, TB, 128, 128, bk_of<IN, 64>, 2, 2, 2, false>;
 };
@@ -179,7 +186,7 @@ LaunchFn launcher_i16(int in_dt, int out_dt, bool transB);
 inline bool fp8_config(int cfg)
 {
     return cfg == CFG_D256x256x32_S4_I || cfg == CFG_D256x256x32_S4_ISK ||
-           cfg == CFG_D128x128x64_S3 || cfg == CFG_D64x64x64_S4 ||
+           cfg == CFG_D128x128x64_S3 || cfg == CFG_D64x64x64_S4 || cfg == CFG_D32x64x128_S4 ||
            cfg == CFG_D64x32x128_S4 || cfg == CFG_G128x128x64 || cfg == CFG_G64x64x64;
 }
 
@@ -223,6 +230,8 @@ inline bool fp8_config(int cfg)
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x64x64_S4>::type>;       \
         case CFG_D64x32x128_S4:                                                            \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x32x128_S4>::type>;      \
+        case CFG_D32x64x128_S4:                                                            \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D32x64x128_S4>::type>;      \
         case CFG_G128x128x64:                                                              \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_G128x128x64>::type>;        \
         case CFG_G64x64x64:                                                                \
@@ -261,6 +270,8 @@ inline bool fp8_config(int cfg)
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x64x64_S4>::type>;       \
         case CFG_D64x32x128_S4:                                                            \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x32x128_S4>::type>;      \
+        case CFG_D32x64x128_S4:                                                            \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D32x64x128_S4>::type>;      \
         case CFG_G128x128x64:                                                              \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_G128x128x64>::type>;        \
         case CFG_G64x64x64:                                                                \

@@ -256,8 +256,17 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     if (forced >= 0 && usable(forced)) {
         cfg = forced;
     } else {
-        for (int id : {CFG_D256x256x32_S4_I, CFG_D128x128x64_S3, CFG_D64x64x64_S4, CFG_D64x32x128_S4})
-            if (usable(id) && (cfg < 0 || cost(id) < cost(cfg))) cfg = id;
+        // The 32x64 tile costs what the 64x32 one does under this model; measured
+        // on MI355X it streams (K,N) B faster (whole 128-byte lines per k row) and
+        // wins where M <= 64 and 64x64 tiles would leave half the CUs idle
+        // (64x8192x8192: 28.0 vs 30.1 us; 64x4096x16384: 45.1 vs 50.1 us).  Where
+        // 64x64 tiles fill the CUs they stream faster still (32x16384x8192: 41.7
+        // vs 45.9 us), so it is not a candidate there.
+        const bool skinny = M <= 64 && tiles(CFG_D64x64x64_S4) * 2 <= kNumCUs;
+        for (int id : {CFG_D256x256x32_S4_I, CFG_D128x128x64_S3, CFG_D64x64x64_S4, CFG_D32x64x128_S4,
+                       CFG_D64x32x128_S4})
+            if (usable(id) && (id != CFG_D32x64x128_S4 || skinny) && (cfg < 0 || cost(id) < cost(cfg)))
+                cfg = id;
         if (cfg < 0) cfg = tiles(CFG_G128x128x64) >= kNumCUs ? CFG_G128x128x64 : CFG_G64x64x64;
     }
     const int64_t tm = ceil_div(M, config_info(cfg).bm), tn = ceil_div(N, config_info(cfg).bn);

@@ -84,7 +84,8 @@ def test_null_operands_allowed_when_K_is_zero():
     (4096, 4096, 4096, 0, True, "d256x256x32_s4_i"),
     (4096, 7168, 4096, 1, True, "d256x256x32_s4_i"),
     (256, 256, 256, 0, True, "d64x32x128_s4"),
-    (64, 8192, 8192, 0, True, "d64x32x128_s4"),        # skinny: twice the workgroups of 64x64
+    (64, 8192, 8192, 0, True, "d32x64x128_s4"),        # skinny: whole-line B rows, twice the workgroups of 64x64
+    (32, 16384, 8192, 0, True, "d64x64x64_s4"),        # skinny, but 64x64 tiles fill the CUs
     (2048, 2048, 512, 0, True, "d128x128x64_s3"),
     (4096, 7168, 4096, 0, True, "d256x256x32_s4_i"),
     (4097, 3001, 5003, 0, True, "d256x256x32_s4_i"),  # ragged and 2-byte aligned rows
@@ -102,7 +103,7 @@ def test_plan_selection(M, N, K, transB, aligned, want):
 @pytest.mark.parametrize("M,N,K,transB,want", [
     (8192, 8192, 8192, 0, "d256x256x32_s4_i"),
     (4096, 7168, 4096, 1, "d256x256x32_s4_i"),
-    (64, 8192, 8192, 0, "d64x32x128_s4"),
+    (64, 8192, 8192, 0, "d32x64x128_s4"),
     (100, 16, 100, 0, "g64x64x64"),                   # fewer than 16 columns of (K,N) B
     (100, 16, 100, 1, "d64x32x128_s4"),
 ])

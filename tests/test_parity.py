@@ -24,7 +24,7 @@ DIRECT = ["d256x256x64_s2", "d256x256x32_s4", "d256x256x32_s5", "d256x256x32_s4_
           "d256x256x64_s2_16", "d256x256x32_s4_i16", "d256x256x32_s4_ip", "d256x256x32_s4_isk",
           "d256x256x32_s4_w8i",
           "d256x256x32_s5_w8i", "d256x256x64_s2_w8", "d128x128x64_s3", "d64x64x64_s4",
-          "d64x32x128_s4"]
+          "d64x32x128_s4", "d32x64x128_s4"]
 STAGED = ["g128x128x64", "g64x64x64"]
 COMBOS = [(i, o) for i in (wl.F16, wl.BF16) for o in (wl.F16, wl.BF16, wl.F32)]
 
@@ -41,7 +41,7 @@ BN_OF = {"d256x256x64_s2": 256, "d256x256x32_s4": 256, "d256x256x32_s5": 256,
          "d256x256x32_s4_isk": 256,
          "d256x256x32_s4_w8i": 256, "d256x256x32_s5_w8i": 256,
          "d256x256x64_s2_w8": 256, "d128x128x64_s3": 128, "d64x64x64_s4": 64,
-         "d64x32x128_s4": 32}
+         "d64x32x128_s4": 32, "d32x64x128_s4": 64}
 
 
 def usable(cfg, N, transB, K=None, in_code=wl.F16):
@@ -137,7 +137,7 @@ def test_coded_mapping(cfg, transB, monkeypatch):
 
 # ----------------------------------------------------------- 8-bit inputs
 FP8_CONFIGS = ["d256x256x32_s4_i", "d256x256x32_s4_isk", "d128x128x64_s3", "d64x64x64_s4",
-               "d64x32x128_s4",
+               "d64x32x128_s4", "d32x64x128_s4",
                "g128x128x64", "g64x64x64"]
 FP8 = [wl.F8E4M3, wl.F8E5M2]
 
