@@ -7,6 +7,7 @@ already resident in HBM.  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline]
     python bench.py --table      # one JSON line per workload (warm and cold L2/MALL)
+    python bench.py --vendor     # the vendor GEMM (+ a separate ReLU) beside it, per workload
 
 Default workload: fp16 GEMM+ReLU at M = N = K = 8192 (row-major A and B,
 uniform[-1, 1] inputs from a fixed seed, fp32 accumulation, fp16 output) — the
@@ -17,6 +18,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -415,6 +417,73 @@ def profile_workloads(gr, calls):
         del keep, Cd
 
 
+def vendor(gr):
+    """Context for the fused kernel: each plain (not block-scaled, not sparse)
+    workload timed through the vendor GEMM (torch.mm / torch._scaled_mm, which
+    dispatch to hipBLASLt on this image) without and with a separate ReLU, and
+    through gemm_relu, on the same resident inputs in the same process; one JSON
+    line per workload.  Median of 5 trials of 20 back-to-back calls, after 10
+    warm-up calls."""
+    import torch
+    stream = torch.cuda.current_stream()
+
+    def median_us(fn):
+        for _ in range(10):
+            fn()
+        trials = []
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            trials.append(e0.elapsed_time(e1) * 1e3 / 20)
+        return statistics.median(trials)
+
+    for name in sorted(wl.WORKLOADS, key=lambda n: wl.WORKLOADS[n]["index"]):
+        w = wl.WORKLOADS[name]
+        if w.get("mx") or w.get("sparse"):
+            continue
+        M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
+        call, Cd, plan, nbytes, keep = workload_call(gr, name, stream)
+        Ad, Bd = keep
+        Bkn = Bd.t() if tb else Bd             # (K, N) operand of the product, a view
+        rec = {"workload": name, "tile_config": plan, "ours_us": round(median_us(call), 2)}
+        try:
+            if ic in wl.FP8:
+                one = torch.ones((), device="cuda")
+                Bcm = Bkn.t().contiguous().t()   # column-major (K, N), as the fp8 GEMM takes it
+                vfn = lambda: torch._scaled_mm(Ad, Bcm, scale_a=one, scale_b=one,
+                                               out_dtype=torch_dtype(oc))
+                rec["vendor"] = "torch._scaled_mm (unit scales)"
+            elif oc == wl.F32 and ic != wl.F32:
+                vfn = lambda: torch.mm(Ad, Bkn, out_dtype=torch.float32)
+                rec["vendor"] = "torch.mm, fp32 out_dtype"
+            else:
+                vfn = lambda: torch.mm(Ad, Bkn)
+                rec["vendor"] = "torch.mm"
+            out = vfn()
+            torch.cuda.synchronize()
+            rec["vendor_us"] = round(median_us(vfn), 2)
+            rec["vendor_relu_us"] = round(median_us(lambda: torch.relu_(vfn())), 2)
+            # same result up to the summation order: the largest difference
+            # after ReLU, relative to the largest output
+            call()
+            torch.cuda.synchronize()
+            ref = torch.relu(out.float())
+            rec["max_rel_diff"] = float((Cd.float() - ref).abs().max() / ref.abs().max().clamp_min(1e-30))
+        except Exception as exc:               # a vendor path this image does not offer
+            rec["vendor_error"] = repr(exc)[:160]
+        flops = 2.0 * M * N * K
+        for k in ("ours_us", "vendor_us", "vendor_relu_us"):
+            if k in rec:
+                rec[k.replace("_us", "_tflops")] = round(flops / rec[k] / 1e6, 1)
+        print(json.dumps(rec), flush=True)
+        del keep, Cd
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -427,6 +496,9 @@ def main():
     ap.add_argument("--profile-workloads", type=int, default=0, metavar="CALLS",
                     help="run CALLS synchronised calls of every workload (for counter runs under "
                          "rocprofv3); prints the dispatch order")
+    ap.add_argument("--vendor", action="store_true",
+                    help="time the vendor GEMM (with and without a separate ReLU) beside "
+                         "gemm_relu on every plain workload, one JSON line each")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only the plain copy used to scale HBM byte counters")
     ap.add_argument("--ingest-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"),
@@ -459,6 +531,9 @@ def main():
         return
     if args.profile_workloads:
         profile_workloads(gr, args.profile_workloads)
+        return
+    if args.vendor:
+        vendor(gr)
         return
 
     w = dict(wl.WORKLOADS[args.workload], name=args.workload)

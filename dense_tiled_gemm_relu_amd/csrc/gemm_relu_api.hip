@@ -162,8 +162,14 @@ unsigned char* sk_workspace(int dev, hipStream_t st)
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
         return nullptr;
+    // Relaxed capture mode for this thread around the allocation, so that a
+    // graph capture in global mode on another thread is not invalidated by it.
     void* p = nullptr;
-    if (hipMalloc(&p, kSkWsBytes) != hipSuccess) {
+    hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+    const bool swapped = hipThreadExchangeStreamCaptureMode(&mode) == hipSuccess;
+    const hipError_t merr = hipMalloc(&p, kSkWsBytes);
+    if (swapped) (void)hipThreadExchangeStreamCaptureMode(&mode);
+    if (merr != hipSuccess) {
         (void)hipGetLastError();
         return nullptr;
     }
