@@ -208,6 +208,49 @@ def cpu_baseline_sp(w, target_s=15.0):
                       "workload, binary64), %.2f s wall" % (R - 1, R, N, K, w["name"], dt)}
 
 
+def host_cpu():
+    """(model name, logical CPUs this process may run on) of the host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def cpu_table(names=None):
+    """The oracle, untuned, over the whole of each plain workload (every output
+    element), once on all host threads (OMP_NUM_THREADS if set) and, for the two smallest
+    square workloads, once on one thread: one JSON line per run.  A CPU
+    baseline for the GPU figures, not a target."""
+    import oracle
+    model, ncpu = host_cpu()
+    # explicit counts: a one-thread run leaves OpenMP's default at one thread
+    all_threads = int(os.environ.get("OMP_NUM_THREADS") or ncpu)
+    order = sorted(wl.WORKLOADS, key=lambda n: wl.WORKLOADS[n]["index"])
+    names = names or [n for n in order if not (wl.WORKLOADS[n].get("mx") or
+                                                wl.WORKLOADS[n].get("sparse") or
+                                                wl.WORKLOADS[n]["in_dtype"] in wl.FP8)]
+    for name in names:
+        w = wl.WORKLOADS[name]
+        M, N, K, ic, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["transB"]
+        A, B = wl.workload_inputs(name)
+        runs = [all_threads] + ([1] if name in ("gemm_relu_f16_256", "gemm_relu_f16_4096") else [])
+        for threads in runs:
+            t = time.perf_counter()
+            _, used = oracle.gemm_relu_ref(A, B, M, N, K, ic, tb, threads=threads,
+                                           return_threads=True)
+            dt = time.perf_counter() - t
+            rec = {"workload": name, "M": M, "N": N, "K": K, "threads": int(used),
+                   "oracle_s": round(dt, 3), "oracle_gflops": round(2.0 * M * N * K / dt / 1e9, 2),
+                   "host_cpu": model, "host_cpus": ncpu}
+            print(json.dumps(rec), flush=True)
+
+
 def peak_tflops(in_dtype, sparse=False):
     if sparse:
         return PEAK_TFLOPS_F16_SPARSE
@@ -499,6 +542,9 @@ def main():
     ap.add_argument("--vendor", action="store_true",
                     help="time the vendor GEMM (with and without a separate ReLU) beside "
                          "gemm_relu on every plain workload, one JSON line each")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="time the oracle over every plain workload on the host cores "
+                         "(no GPU), one JSON line per run")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only the plain copy used to scale HBM byte counters")
     ap.add_argument("--ingest-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"),
@@ -509,6 +555,9 @@ def main():
         return
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.cpu_table:
+        cpu_table()
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
