@@ -246,7 +246,7 @@ def cpu_table(names=None):
                                            return_threads=True)
             dt = time.perf_counter() - t
             rec = {"workload": name, "M": M, "N": N, "K": K, "threads": int(used),
-                   "oracle_s": round(dt, 3), "oracle_gflops": round(2.0 * M * N * K / dt / 1e9, 2),
+                   "oracle_s": round(dt, 6), "oracle_gflops": round(2.0 * M * N * K / dt / 1e9, 3),
                    "host_cpu": model, "host_cpus": ncpu}
             print(json.dumps(rec), flush=True)
 

@@ -33,3 +33,16 @@ def test_more_than_one_gpu_is_refused():
                        cwd=bench.ROOT, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr) or "1 GPU" in (r.stdout + r.stderr)
+
+
+def test_cpu_table_times_the_oracle_over_a_whole_workload(capsys):
+    import json
+    import bench
+    bench.cpu_table(["gemm_relu_f16_256"])
+    recs = [json.loads(line) for line in capsys.readouterr().out.splitlines() if line.startswith("{")]
+    # one run on all host threads, one on a single thread for the smallest square workload
+    assert [r["workload"] for r in recs] == ["gemm_relu_f16_256"] * 2
+    assert recs[1]["threads"] == 1
+    for r in recs:
+        assert r["oracle_s"] > 0
+        assert abs(r["oracle_gflops"] - 2 * 256 ** 3 / r["oracle_s"] / 1e9) <= 0.01 * r["oracle_gflops"] + 0.01
