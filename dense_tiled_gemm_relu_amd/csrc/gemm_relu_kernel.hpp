@@ -746,14 +746,18 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
         for (int q = 0; q < C::NR; ++q) read_op(stage, s, q, f);
     };
     // Operands swapped (B block as the MFMA's first source) so that each lane
-    // ends up owning 4 consecutive n of one output row.
+    // ends up owning 4 consecutive n of one output row.  B blocks in snake
+    // order (backwards for odd i), so one operand is unchanged from each MFMA
+    // to the next.
     auto mma = [&](const Frags& f) {
         if constexpr (!C::MX) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
+                for (int jj = 0; jj < TN; ++jj) {
+                    const int j = (i & 1) ? TN - 1 - jj : jj;
                     acc[i][j] = In::mfma(f.b[j], f.a[i], acc[i][j]);
+                }
         }
     };
 

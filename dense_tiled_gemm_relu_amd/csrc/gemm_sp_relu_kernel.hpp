@@ -343,9 +343,13 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_sp_relu_kernel(SpArgs arg
     auto contract = [&](const AFrags& f, int next_stage, int next_s) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
+            // A blocks in snake order (down the column for odd j), so the
+            // compressed operand is unchanged where j steps
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int ii = 0; ii < TM; ++ii) {
+                const int i = (j & 1) ? TM - 1 - ii : ii;
                 acc[i][j] = SpIn<C::IN_DT>::smfmac(f.a[i], b[j], acc[i][j], f.idx[i]);
+            }
             if (next_stage >= 0) read_b(next_stage, next_s, j);
         }
     };
@@ -407,8 +411,10 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_sp_relu_kernel(SpArgs arg
                 }
                 if (j == 0 && next_stage >= 0) read_a(next_stage, next_s, fa[(s + 1) & 1]);
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+                for (int ii = 0; ii < TM; ++ii) {
+                    const int i = (j & 1) ? TM - 1 - ii : ii;     // snake order, as above
                     acc[i][j] = SpIn<C::IN_DT>::smfmac(f.a[i], b[j], acc[i][j], f.idx[i]);
+                }
                 if (next_stage >= 0) read_b(next_stage, next_s, j);
                 __builtin_amdgcn_sched_barrier(0);
             }
