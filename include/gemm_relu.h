@@ -41,7 +41,7 @@ extern "C" {
 /* Status codes.  The library never aborts, throws or prints. */
 #define GEMM_RELU_OK            0
 #define GEMM_RELU_EINVAL       -1 /* bad argument: size, pointer, code, overlap */
-#define GEMM_RELU_EUNSUPPORTED -2 /* valid request this build cannot run (device, size limits) */
+#define GEMM_RELU_EUNSUPPORTED -2 /* valid request the library cannot run (device, size limits) */
 #define GEMM_RELU_EHIP         -3 /* a HIP runtime call or kernel launch failed */
 
 /*
