@@ -382,9 +382,13 @@ def mfma_ceiling(gr, stream, blocks=1024, steps=2048, kind=0):
                        "fp16, 2:4 sparse (dense-equivalent flops)")[kind]}
 
 
+TABLE_WARMUP_S = 0.5
+
+
 def table(gr):
     """One JSON line per workload: median per-call kernel time over 5 trials of
-    20 back-to-back calls (HIP events on the launch stream, 10 warm-up calls),
+    20 back-to-back calls (HIP events on the launch stream, after at least 10
+    and at least TABLE_WARMUP_S seconds of warm-up calls),
     and a cold-cache time (median of 20 calls, each after a 512 MiB write
     that evicts the 256 MiB MALL and the L2s)."""
     import statistics
@@ -403,8 +407,14 @@ def table(gr):
         ceiling = ceilings[ceiling_kind(ic, w.get("sparse", False))]
         peak = peak_tflops(ic, w.get("sparse", False))
 
-        for _ in range(10):
+        # warm-up by time, not by count: the power-limited clock takes tens of
+        # milliseconds to settle, far longer than 10 calls of a small workload
+        n, t_end = 0, time.perf_counter() + TABLE_WARMUP_S
+        while n < 10 or time.perf_counter() < t_end:
             call()
+            n += 1
+            if n % 10 == 0:
+                torch.cuda.synchronize()
         trials = []
         for _ in range(5):
             e0 = torch.cuda.Event(enable_timing=True)
