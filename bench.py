@@ -541,7 +541,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
+    # 200 calls: the power-limited clock settles within about 60-150 calls of
+    # the 8192^3 kernel (tens of milliseconds) and then holds steady
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="gemm_relu_f16_8192", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--table", action="store_true",
