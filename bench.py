@@ -475,25 +475,38 @@ def vendor(gr):
     workload timed through the vendor GEMM (torch.mm / torch._scaled_mm, which
     dispatch to hipBLASLt on this image) without and with a separate ReLU, and
     through gemm_relu, on the same resident inputs in the same process; one JSON
-    line per workload.  Median of 5 trials of 20 back-to-back calls, after 10
-    warm-up calls."""
+    line per workload.  The three are warmed up together for at least
+    TABLE_WARMUP_S seconds (the clock is shared, and it takes tens of
+    milliseconds to settle), then timed in 5 rounds of one trial each, in an
+    order that rotates from round to round; a trial is 20 back-to-back calls.
+    Each figure is the median of its 5 trials."""
     import torch
     stream = torch.cuda.current_stream()
 
-    def median_us(fn):
-        for _ in range(10):
+    def trial_us(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
             fn()
-        trials = []
-        for _ in range(5):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(20):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            trials.append(e0.elapsed_time(e1) * 1e3 / 20)
-        return statistics.median(trials)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / 20
+
+    def median_us(fns):
+        names = list(fns)
+        n, t_end = 0, time.perf_counter() + TABLE_WARMUP_S
+        while n < 10 or time.perf_counter() < t_end:
+            for k in names:
+                fns[k]()
+            n += 1
+            if n % 10 == 0:
+                torch.cuda.synchronize()
+        trials = {k: [] for k in names}
+        for r in range(5):
+            for k in names[r % len(names):] + names[:r % len(names)]:
+                trials[k].append(trial_us(fns[k]))
+        return {k: statistics.median(v) for k, v in trials.items()}
 
     for name in sorted(wl.WORKLOADS, key=lambda n: wl.WORKLOADS[n]["index"]):
         w = wl.WORKLOADS[name]
@@ -503,7 +516,7 @@ def vendor(gr):
         call, Cd, plan, nbytes, keep = workload_call(gr, name, stream)
         Ad, Bd = keep
         Bkn = Bd.t() if tb else Bd             # (K, N) operand of the product, a view
-        rec = {"workload": name, "tile_config": plan, "ours_us": round(median_us(call), 2)}
+        rec = {"workload": name, "tile_config": plan}
         try:
             if ic in wl.FP8:
                 one = torch.ones((), device="cuda")
@@ -519,8 +532,9 @@ def vendor(gr):
                 rec["vendor"] = "torch.mm"
             out = vfn()
             torch.cuda.synchronize()
-            rec["vendor_us"] = round(median_us(vfn), 2)
-            rec["vendor_relu_us"] = round(median_us(lambda: torch.relu_(vfn())), 2)
+            med = median_us({"ours": call, "vendor": vfn, "vendor_relu": lambda: torch.relu_(vfn())})
+            rec.update(ours_us=round(med["ours"], 2), vendor_us=round(med["vendor"], 2),
+                       vendor_relu_us=round(med["vendor_relu"], 2))
             # same result up to the summation order: the largest difference
             # after ReLU, relative to the largest output
             call()
@@ -529,6 +543,7 @@ def vendor(gr):
             rec["max_rel_diff"] = float((Cd.float() - ref).abs().max() / ref.abs().max().clamp_min(1e-30))
         except Exception as exc:               # a vendor path this image does not offer
             rec["vendor_error"] = repr(exc)[:160]
+            rec["ours_us"] = round(median_us({"ours": call})["ours"], 2)
         flops = 2.0 * M * N * K
         for k in ("ours_us", "vendor_us", "vendor_relu_us"):
             if k in rec:
