@@ -99,17 +99,18 @@ template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x64_S2
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 64>, 2, 2, 2, true, false, 16>;
 };
 // The interleaved four-stage tile with 16x16x32 MFMA blocks (16-bit inputs):
-// one MFMA k step per 32-k step.  Built in its own units (inst_i16.hip), with
-// the matrix instructions in their VGPR form.
+// one MFMA k step per 32-k step, one fragment set reloaded in place.  The
+// large-shape tile that plan selection takes for 16-bit inputs.  Built in its
+// own units (inst_i16.hip), with the matrix instructions in their VGPR form.
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I16> {
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 4, true, true, 16>;
 };
-// The default interleaved tile as a persistent kernel: at most one workgroup
+// The 32x32-block interleaved tile as a persistent kernel: at most one workgroup
 // per CU, each looping over its tiles (the Ascend version's T.Persistent).
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_IP> {
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 4, true, true, 32, true>;
 };
-// The default interleaved tile with its last round split along K (stream-K):
+// The 32x32-block interleaved tile with its last round split along K (stream-K):
 // the tiles that do not fill a whole round of CUs share their K steps out
 // over all of them.
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_ISK> {

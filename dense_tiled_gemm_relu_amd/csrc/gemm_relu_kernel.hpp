@@ -1070,13 +1070,65 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
                     });
             }
             if constexpr (C::MB == 16 && !C::MX) {
-                // 16x16 blocks: single steady steps, the fragment set read for
-                // the next step copied into the contracted one (64 register
-                // moves a step); the two-step form makes the register
-                // allocator shuffle the 64 small accumulators instead
+                // 16x16 blocks (one MFMA k step per BK step, 8 x 8 blocks a
+                // wave): steady steps with one fragment set, reloaded in place.
+                // Fragment sets alternating by step parity need the loop
+                // unrolled by two steps, and the register allocator then moves
+                // the 64 small accumulators around the loop; a second set
+                // copied into the first costs 64 moves a step.  Instead the
+                // step's 64 MFMAs run as two halves, all A blocks against B
+                // blocks 0..3 and then against B blocks 4..7 (rows of A in
+                // pairs, snake order inside a pair), and each fragment is
+                // read for the next step right after its last use in this
+                // one: B 0..3 after the first half, A blocks 2k, 2k+1 after
+                // region 4 + k, B 4..7 at the end.  Every read then has at
+                // least four regions (32 MFMAs) before its first use.
+                static_assert(TM == 8 && TN == 8 && KSUB == 1 && R == 8 && NM == 64 &&
+                                  C::LOADS_PER_STAGE == 8,
+                              "in-place 16x16 steps: 8 x 8 blocks, one copy per region");
+                constexpr int QA = TM * FRAG_CH;
+                constexpr int QB = C::TRANS_B ? FRAG_CH : TR_READS;     // reads per B block
                 for (; t < t_steady; ++t) {
-                    step(t, Steady{}, P0{}, NoRun{});
-                    fr[0] = fr[1];
+                    const int ld_stage = (t + S - 1) % S;
+                    const int ld_k0 = (t + S - 1) * BK;
+                    const unsigned char* ga = a_tile + (size_t)ld_k0 * EB;
+                    const unsigned char* gb = C::TRANS_B ? b_tile + (size_t)ld_k0 * EB
+                                                         : b_tile + (size_t)ld_k0 * (size_t)N * EB;
+                    const uint32_t lsa = smem_addr + ld_stage * C::STAGE_BYTES;
+                    const uint32_t lsb = lsa + C::A_BYTES;
+                    const int rd_stage = (t + 1) % S;
+                    // stage t+1 has landed, and every wave is past its reads of
+                    // the buffer the copies below refill
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::STEADY_ALLOWANCE));
+                    barrier_lds();
+                    static_for<0, 8>([&](auto r_tag) {
+                        constexpr int r = decltype(r_tag)::value;
+                        __builtin_amdgcn_sched_barrier(0);
+                        if constexpr (r < APT)
+                            dma16(ga, a_src[r], lsa + (r * C::NWAVES + wave) * 1024);
+                        else
+                            dma16(gb, b_src[r - APT], lsb + ((r - APT) * C::NWAVES + wave) * 1024);
+                        constexpr int half = r / 4, i0 = 2 * (r % 4);
+#pragma unroll
+                        for (int di = 0; di < 2; ++di)
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj) {
+                                const int i = i0 + di;
+                                const int j = 4 * half + (di ? 3 - jj : jj);
+                                acc[i][j] = In::mfma(fr[0].b[j], fr[0].a[i], acc[i][j]);
+                            }
+                        if constexpr (r == 3 || r == 7) {
+#pragma unroll
+                            for (int q = QA + 4 * half * QB; q < QA + (4 * half + 4) * QB; ++q)
+                                read_op(rd_stage, 0, q, fr[0]);
+                        }
+                        if constexpr (r >= 4) {
+#pragma unroll
+                            for (int q = i0 * FRAG_CH; q < (i0 + 2) * FRAG_CH; ++q)
+                                read_op(rd_stage, 0, q, fr[0]);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
                 }
             }
             for (; t + 1 < t_steady; t += 2) {

@@ -80,16 +80,16 @@ def test_null_operands_allowed_when_K_is_zero():
 
 
 @pytest.mark.parametrize("M,N,K,transB,aligned,want", [
-    (8192, 8192, 8192, 0, True, "d256x256x32_s4_i"),
-    (4096, 4096, 4096, 0, True, "d256x256x32_s4_i"),
-    (4096, 7168, 4096, 1, True, "d256x256x32_s4_i"),
+    (8192, 8192, 8192, 0, True, "d256x256x32_s4_i16"),
+    (4096, 4096, 4096, 0, True, "d256x256x32_s4_i16"),
+    (4096, 7168, 4096, 1, True, "d256x256x32_s4_i16"),
     (256, 256, 256, 0, True, "d64x32x128_s4"),
     (64, 8192, 8192, 0, True, "d32x64x128_s4"),        # skinny: whole-line B rows, twice the workgroups of 64x64
     (32, 16384, 8192, 0, True, "d64x64x64_s4"),        # skinny, but 64x64 tiles fill the CUs
     (2048, 2048, 512, 0, True, "d128x128x64_s3"),
-    (4096, 7168, 4096, 0, True, "d256x256x32_s4_i"),
-    (4097, 3001, 5003, 0, True, "d256x256x32_s4_i"),  # ragged and 2-byte aligned rows
-    (4096, 4096, 4096, 0, False, "d256x256x32_s4_i"), # 2-byte aligned base pointer
+    (4096, 7168, 4096, 0, True, "d256x256x32_s4_i16"),
+    (4097, 3001, 5003, 0, True, "d256x256x32_s4_i16"),  # ragged and 2-byte aligned rows
+    (4096, 4096, 4096, 0, False, "d256x256x32_s4_i16"), # 2-byte aligned base pointer
     (100, 100, 100, 0, True, "d64x32x128_s4"),
     (100, 24, 100, 0, True, "g64x64x64"),              # fewer than 32 columns of (K,N) B
     (100, 24, 100, 1, True, "d64x32x128_s4"),          # transposed B rows are clamped
@@ -199,10 +199,11 @@ def test_mx_interleaved_needs_16_scale_blocks_per_row(monkeypatch, fmt):
     assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 1024, 1024, 480, fmt, 0) == "d128x128x64_s2"
 
 
-@pytest.mark.parametrize("in_dtype", [0, 1, 3])
-def test_mx_only_configuration_not_used_for_other_inputs(monkeypatch, in_dtype):
+@pytest.mark.parametrize("in_dtype,want", [(0, "d256x256x32_s4_i16"), (1, "d256x256x32_s4_i16"),
+                                           (3, "d256x256x32_s4_i")])
+def test_mx_only_configuration_not_used_for_other_inputs(monkeypatch, in_dtype, want):
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x128x64_s2")
-    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, in_dtype, 0, 1) == "d256x256x32_s4_i"
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, in_dtype, 0, 1) == want
 
 
 # ------------------------------------------------ 2:4 sparse entry point
@@ -234,15 +235,22 @@ def test_sp_plan():
     assert gr.gemm_relu_sp_plan(A, E_, B, C, 64, 8, (1 << 22) + 4, 0, 0, 1) == "unsupported"
 
 
-@pytest.mark.parametrize("name", ["d256x256x32_s4_ip", "d256x256x32_s4_i16"])
+@pytest.mark.parametrize("name", ["d256x256x32_s4_ip", "d256x256x32_s4_i"])
 def test_comparison_configurations_are_selectable(monkeypatch, name):
-    """The persistent tile loop and the 16x16-block tile: forced by name for
-    16-bit inputs, never chosen automatically, not built for 8-bit inputs."""
-    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0) == "d256x256x32_s4_i"
+    """The persistent tile loop and the 32x32-block tile: forced by name for
+    16-bit inputs, never chosen automatically for them (the 16x16-block tile
+    is); 8-bit inputs have no persistent build and take the 32x32 tile."""
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0) == "d256x256x32_s4_i16"
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", name)
     assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0) == name
     assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 1, 2, 1) == name
     assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 3, 0, 0) == "d256x256x32_s4_i"
+
+
+def test_16x16_tile_not_built_for_8bit_inputs(monkeypatch):
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x256x32_s4_i16")
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 3, 0, 0) == "d256x256x32_s4_i"
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 4, 0, 1) == "d256x256x32_s4_i"
 
 
 def test_streamk_selection(monkeypatch):
