@@ -264,11 +264,14 @@ def peak_tflops(in_dtype, sparse=False):
 PEAK_TFLOPS_F16_SPARSE = 2 * PEAK_TFLOPS_F16   # 2:4 sparse fp16/bf16, dense-equivalent flops
 
 
-def ceiling_kind(in_dtype, sparse=False):
-    """probe_mfma_rate kind matching an input type: 0 fp16, 1 E4M3, 2 E2M1
-    (scaled MFMA), 3 E4M3 on the scaled MFMA, 4 the 2:4 sparse fp16 form."""
+def ceiling_kind(in_dtype, sparse=False, plan=None):
+    """probe_mfma_rate kind matching an input type and tile configuration: 0
+    fp16 32x32x16, 1 E4M3, 2 E2M1 (scaled MFMA), 3 E4M3 on the scaled MFMA, 4
+    the 2:4 sparse fp16 form, 5 fp16 16x16x32 (the 16x16-block tiles)."""
     if sparse:
         return 4
+    if plan is not None and (plan.endswith("_i16") or plan.endswith("_16")):
+        return 5
     if in_dtype == wl.MX_E2M1:
         return 2
     if in_dtype in (wl.MX_E4M3, wl.MX_E5M2):
@@ -335,7 +338,7 @@ def mfma_ceiling(gr, stream, blocks=1024, steps=2048, kind=0):
     one step of a 128x128 wave tile; kind 0: fp16 32x32x16, 1: E4M3 32x32x64,
     2: E2M1 32x32x64 on the scaled MFMA with unit scales, 3: E4M3 on the scaled
     MFMA, 4: the 2:4 sparse fp16 32x32x32 form, counted at its dense-equivalent
-    flops).  The chip is
+    flops; 5: fp16 16x16x32, the same step as 64 MFMAs).  The chip is
     power-limited, so this, not 2.4 GHz x the instruction rate, is what the
     contraction step alone can reach on this machine now.  None if the probe
     library is not built."""
@@ -374,12 +377,14 @@ def mfma_ceiling(gr, stream, blocks=1024, steps=2048, kind=0):
     t = ticks.view(blocks, 2).double()
     cycles = t[:, 0].mean().item()
     clock_mhz = (t[:, 0] / t[:, 1]).mean().item() * 100.0
-    flops = blocks * 4 * steps * 32 * (32 * 32 * {0: 16, 4: 32}.get(kind, 64) * 2)
+    # flops of one 128x128x32 (fp16) or 128x128x128 (8-bit) wave step, per wave and step
+    flops = blocks * 4 * steps * 32 * (32 * 32 * {0: 16, 4: 32, 5: 16}.get(kind, 64) * 2)
+    mfmas = steps * 32 * (2 if kind == 5 else 1)    # kind 5: 16x16x32, half the MACs each
     return {"tflops": round(flops / sec / 1e12, 1), "clock_mhz": round(clock_mhz),
-            "cycles_per_mfma": round(cycles / (steps * 32), 2),
+            "cycles_per_mfma": round(cycles / mfmas, 2),
             "kind": "MFMA-only, random %s operands, no memory traffic (probe_mfma_rate)"
                     % ("fp16", "E4M3", "E2M1 (unit block scales)", "E4M3 (unit block scales)",
-                       "fp16, 2:4 sparse (dense-equivalent flops)")[kind]}
+                       "fp16, 2:4 sparse (dense-equivalent flops)", "fp16, 16x16x32 form")[kind]}
 
 
 TABLE_WARMUP_S = 0.5
@@ -395,16 +400,16 @@ def table(gr):
     import torch
     stream = torch.cuda.current_stream()
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
-    ceilings = {k: mfma_ceiling(gr, stream, kind=k) for k in (0, 1, 2, 3, 4)}
+    ceilings = {k: mfma_ceiling(gr, stream, kind=k) for k in (0, 1, 2, 3, 4, 5)}
     print(json.dumps({"mfma_ceiling": ceilings[0], "mfma_ceiling_fp8": ceilings[1],
                       "mfma_ceiling_mxfp4": ceilings[2], "mfma_ceiling_mxfp8": ceilings[3],
-                      "mfma_ceiling_sparse_f16": ceilings[4]}),
+                      "mfma_ceiling_sparse_f16": ceilings[4], "mfma_ceiling_f16_16x16": ceilings[5]}),
           flush=True)
     for name in sorted(wl.WORKLOADS, key=lambda n: wl.WORKLOADS[n]["index"]):
         w = wl.WORKLOADS[name]
         M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
         call, Cd, plan, nbytes, keep = workload_call(gr, name, stream)
-        ceiling = ceilings[ceiling_kind(ic, w.get("sparse", False))]
+        ceiling = ceilings[ceiling_kind(ic, w.get("sparse", False), plan)]
         peak = peak_tflops(ic, w.get("sparse", False))
 
         # warm-up by time, not by count: the power-limited clock takes tens of
@@ -665,7 +670,7 @@ def main():
                    "accumulate": "f32", "inputs": w["dist"], "tile_config": plan},
         "roofline": roofline(flops, nbytes, kernel_ms, peak, measured_traffic(args.workload)),
     }
-    ceiling = mfma_ceiling(gr, stream, kind=ceiling_kind(ic, sparse))
+    ceiling = mfma_ceiling(gr, stream, kind=ceiling_kind(ic, sparse, plan))
     if ceiling is not None:
         out["mfma_ceiling"] = dict(ceiling, frac=round(achieved / ceiling["tflops"], 4))
     if not args.no_cpu_baseline:

@@ -28,7 +28,8 @@ LIB_SOURCES = ["gemm_relu_api.hip", "inst_f16_nn.hip", "inst_f16_nt.hip",
                "inst_f8e4m3_nt.hip", "inst_f8e5m2_nn.hip", "inst_f8e5m2_nt.hip",
                "inst_mx_e4m3.hip", "inst_mx_e5m2.hip", "inst_mx_e2m1.hip", "inst_sp.hip",
                "inst_i16.hip"]
-PROBE_SOURCES = ["probe_layouts.hip", "probe_mfma_rate.hip", "probe_fp8.hip", "probe_sparse.hip"]
+PROBE_SOURCES = ["probe_layouts.hip", "probe_mfma_rate.hip", "probe_mfma16.hip", "probe_fp8.hip",
+                 "probe_sparse.hip"]
 HEADERS = ["gemm_relu_kernel.hpp", "configs.hpp", "gemm_sp_relu_kernel.hpp"]
 
 # gfx950 only.  Packed fp32 ALU ops are switched off: the compiler otherwise
@@ -43,7 +44,8 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # copy offsets, whose reloads drain the copy pipeline every step; the VGPR
 # form of the matrix instructions leaves the main loop spill-free.
 EXTRA_FLAGS = {"inst_sp.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-               "inst_i16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+               "inst_i16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+               "probe_mfma16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _newer(target, deps):

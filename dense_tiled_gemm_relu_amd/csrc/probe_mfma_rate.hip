@@ -10,7 +10,9 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 on E2M1 data with unit E8M0 scales
 // (16-byte operands); kind 3: the same scaled MFMA on E4M3 data (32-byte
 // operands); kind 4: v_smfmac_f32_32x32x32_f16, the 2:4 sparse form (a 16-byte
-// compressed operand, a 32-byte dense one, a fixed valid index word).  The operands are the caller's random fp16 data, so the multiplier
+// compressed operand, a 32-byte dense one, a fixed valid index word); kind 5:
+// v_mfma_f32_16x16x32_f16 (16-byte operands), the same step as 64 MFMAs of
+// 16x16 blocks.  The operands are the caller's random data, so the multiplier
 // arrays toggle as they do in the GEMM; on MI355X this, not the instruction
 // rate, sets the shader clock.  Wave 0 of each workgroup records the shader
 // cycles (s_memtime) and 100 MHz reference ticks (s_memrealtime) of its loop.
@@ -119,6 +121,11 @@ k_smfmac_rate(const unsigned char* src, float* out, unsigned long long* ticks, i
 
 }  // namespace
 
+// kind 5 lives in probe_mfma16.hip (built with the matrix instructions in their
+// VGPR form, which keeps its 64 small accumulators in place)
+hipError_t launch_mfma16_rate(const unsigned char* src, float* out, unsigned long long* ticks,
+                              int blocks, int steps, hipStream_t stream);
+
 // src: at least blocks * 8 * 256 * OPB bytes of input data (OPB = 16 for
 // kind 0, fp16; 32 for kinds 1 and 3, E4M3; 16 for kind 2, packed E2M1; 32
 // for kind 4, fp16); out: blocks * 256 floats; ticks:
@@ -128,7 +135,7 @@ k_smfmac_rate(const unsigned char* src, float* out, unsigned long long* ticks, i
 extern "C" int probe_mfma_rate(const void* src, size_t src_bytes, void* out, void* ticks,
                                int blocks, int steps, int kind, void* stream)
 {
-    if (kind < 0 || kind > 4) return -1;
+    if (kind < 0 || kind > 5) return -1;
     const size_t opb = (kind == 1 || kind == 3 || kind == 4) ? 32 : 16;
     if (!src || !out || !ticks || blocks <= 0 || steps <= 0 ||
         src_bytes < (size_t)blocks * kOperandRegs * kThreads * opb)
@@ -147,8 +154,10 @@ extern "C" int probe_mfma_rate(const void* src, size_t src_bytes, void* out, voi
     else if (kind == 3)
         hipLaunchKernelGGL(k_mfma_rate<DT_MX_E4M3>, dim3(blocks), dim3(kThreads), 0, st, s,
                            (float*)out, (unsigned long long*)ticks, steps);
-    else
+    else if (kind == 4)
         hipLaunchKernelGGL(k_smfmac_rate, dim3(blocks), dim3(kThreads), 0, st, s, (float*)out,
                            (unsigned long long*)ticks, steps);
+    else
+        (void)launch_mfma16_rate(s, (float*)out, (unsigned long long*)ticks, blocks, steps, st);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }

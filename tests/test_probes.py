@@ -115,13 +115,13 @@ def test_unaligned_16_byte_loads(probe):
 
 
 @pytest.mark.parametrize("kind,opb,cycles", [(0, 16, 32), (1, 32, 64), (2, 16, 32), (3, 32, 64),
-                                              (4, 32, 32)],
-                         ids=["f16", "e4m3", "mx_e2m1", "mx_e4m3", "sparse_f16"])
+                                              (4, 32, 32), (5, 16, 32)],
+                         ids=["f16", "e4m3", "mx_e2m1", "mx_e4m3", "sparse_f16", "f16_16x16"])
 def test_mfma_rate_probe(probe, kind, opb, cycles):
     """The MFMA-only diagnostic (random operands, no memory traffic) runs, issues
     one 32x32x16 fp16 MFMA per 32 shader cycles (one 32x32x64 E4M3 MFMA per
-    64) per SIMD, and keeps its accumulators finite; size errors are rejected
-    before launch."""
+    64, two 16x16x32 fp16 MFMAs per 32) per SIMD, and keeps its accumulators
+    finite; size errors and unknown kinds are rejected before launch."""
     import torch
     lib = probe
     lib.probe_mfma_rate.restype = ctypes.c_int
@@ -132,9 +132,9 @@ def test_mfma_rate_probe(probe, kind, opb, cycles):
     if kind == 2:                                        # random E2M1 nibble pairs
         src = torch.randint(0, 256, (blocks * 8 * 256 * opb,), dtype=torch.uint8, device="cuda")
     else:
-        per_lane = opb // 2 if kind in (0, 4) else opb  # elements per operand per lane
+        per_lane = opb // 2 if kind in (0, 4, 5) else opb  # elements per operand per lane
         src = torch.empty(blocks * 8 * 256 * per_lane, dtype=torch.float32, device="cuda")
-        src = src.uniform_(-1, 1).to(torch.float16 if kind in (0, 4) else torch.float8_e4m3fn)
+        src = src.uniform_(-1, 1).to(torch.float16 if kind in (0, 4, 5) else torch.float8_e4m3fn)
     nbytes = src.numel() * src.element_size()
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     ticks = torch.zeros(2 * blocks, dtype=torch.int64, device="cuda")
@@ -142,7 +142,7 @@ def test_mfma_rate_probe(probe, kind, opb, cycles):
     assert lib.probe_mfma_rate(src.data_ptr(), nbytes - 1, out.data_ptr(),
                                ticks.data_ptr(), blocks, steps, kind, st) == -1
     assert lib.probe_mfma_rate(src.data_ptr(), nbytes, out.data_ptr(),
-                               ticks.data_ptr(), blocks, steps, 5, st) == -1
+                               ticks.data_ptr(), blocks, steps, 6, st) == -1
     assert lib.probe_mfma_rate(src.data_ptr(), nbytes, out.data_ptr(),
                                ticks.data_ptr(), blocks, steps, kind, st) == 0
     torch.cuda.synchronize()
