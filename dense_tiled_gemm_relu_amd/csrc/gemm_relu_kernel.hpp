@@ -1097,10 +1097,16 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
                     const uint32_t lsa = smem_addr + ld_stage * C::STAGE_BYTES;
                     const uint32_t lsb = lsa + C::A_BYTES;
                     const int rd_stage = (t + 1) % S;
-                    // stage t+1 has landed, and every wave is past its reads of
-                    // the buffer the copies below refill
+                    // stage t+1 has landed (this wave's copies, then the
+                    // barrier for the others'), and every wave is past its reads
+                    // of the buffer the copies below refill: those reads (stage
+                    // t-1, issued during step t-2) fed MFMAs of step t-1, so they
+                    // have completed.  No LDS fence: it would wait for this
+                    // wave's just-issued reads of stage t+1 as well.  The
+                    // memory clobber keeps the compiler from moving LDS accesses
+                    // across the barrier.
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::STEADY_ALLOWANCE));
-                    barrier_lds();
+                    asm volatile("s_barrier" ::: "memory");
                     static_for<0, 8>([&](auto r_tag) {
                         constexpr int r = decltype(r_tag)::value;
                         __builtin_amdgcn_sched_barrier(0);
