@@ -232,6 +232,20 @@ def gemm_relu_ref_matmul(A, B, M, N, K, dtype, transB=0, relu=True):
     return np.where(x > 0.0, x, 0.0)
 
 
+def gemm_absum_matmul(A, B, M, N, K, dtype, transB=0):
+    """S[i, j] = sum_k |a(i,k) b(k,j)| for every output, the scale of the
+    binary32 summation error bound, with numpy's binary64 matmul of the
+    decoded magnitudes as the summation step (a bound's scale, so its own
+    rounding does not matter).  For full-size problems."""
+    A = _bits(A, dtype).reshape(-1)
+    B = _bits(B, dtype).reshape(-1)
+    if A.size != M * K or B.size != K * N:
+        raise ValueError("operand sizes do not match M, N, K")
+    a = np.abs(decode(A, dtype).reshape(M, K))
+    b = np.abs(decode(B, dtype).reshape((N, K) if transB else (K, N)))
+    return a @ (b.T if transB else b)
+
+
 # ------------------------------------------------------ block-scaled (MX)
 def dec_e2m1(nibble):
     return _load().oracle_dec_e2m1(int(nibble))

@@ -240,6 +240,23 @@ def test_sampled_matches_full_and_absum():
         assert np.allclose(absum.reshape(M, N), S, rtol=1e-12, atol=0)
 
 
+def test_absum_matmul_form_matches_the_dot_products():
+    """The full-size absum (library matmul of decoded magnitudes) against the
+    per-position absum of the dot-product loop, and against the bound's
+    defining property S >= |sum|."""
+    M, N, K = 29, 33, 301
+    for transB, dtype in ((0, F16), (1, BF16), (1, F16)):
+        A, B = wl.make_inputs(M, N, K, dtype, transB, "uniform", 11)
+        S = oracle.gemm_absum_matmul(A, B, M, N, K, dtype, transB)
+        rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        _, absum = oracle.gemm_relu_ref_at(A, B, rows.ravel(), cols.ravel(), M, N, K,
+                                           dtype, transB)
+        assert S.shape == (M, N)
+        assert np.allclose(S, absum.reshape(M, N), rtol=1e-12, atol=0)
+        X = oracle.gemm_relu_ref(A, B, M, N, K, dtype, transB, relu=False)
+        assert np.all(S >= np.abs(X))
+
+
 def test_integer_inputs_are_exact_against_fractions():
     M, N, K = 7, 5, 300
     A, B = wl.make_inputs(M, N, K, F16, 0, "uniform", 3, int_values=True)
@@ -466,6 +483,54 @@ def test_mx_block_scale_pulls_out(fmt):
     SA0[:, 1] = 0                                  # block 1 scaled to 2^-127: negligible
     part0 = oracle.gemm_relu_mx_ref(A, SA0, B, SB, M, N, K, fmt, relu=False)
     assert np.allclose(bumped, full + (full - part0), rtol=0, atol=1e-30)
+
+
+@pytest.mark.parametrize("fmt", [MX_E4M3, MX_E5M2, MX_E2M1])
+def test_mx_sampled_matches_full_and_absum(fmt):
+    """The block-scaled oracle's position mode (the one full-size GPU checks
+    call) against its full mode, value for value at every position and at a
+    shuffled list with repeats; its absum against sum_k |xa a xb b| built here
+    from torch's float8 decoding (E4M3 / E5M2) or the OCP table (E2M1) and
+    2^(e - 127) scales, by numpy's binary64 matmul.  A NaN scale (e = 255)
+    makes its row's unclamped sums and absum NaN in both modes and nothing
+    else."""
+    import torch
+    rng = np.random.default_rng(53 + fmt)
+    M, N, K = 13, 11, 128
+    A, SA, B, SB = _random_mx(M, N, K, fmt, rng, scale_spread=5)
+    SA[4, 2] = 255
+    rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    rows, cols = rows.ravel(), cols.ravel()
+    perm = rng.permutation(np.concatenate([np.arange(M * N), rng.integers(0, M * N, 40)]))
+    for relu in (True, False):
+        full = oracle.gemm_relu_mx_ref(A, SA, B, SB, M, N, K, fmt, relu=relu)
+        v, absum = oracle.gemm_relu_mx_ref(A, SA, B, SB, M, N, K, fmt, relu=relu, rows=rows, cols=cols)
+        assert np.array_equal(v.reshape(M, N), full, equal_nan=True)
+        v2, absum2 = oracle.gemm_relu_mx_ref(A, SA, B, SB, M, N, K, fmt, relu=relu,
+                                             rows=rows[perm], cols=cols[perm])
+        assert np.array_equal(v2, full.reshape(-1)[perm], equal_nan=True)
+        assert np.array_equal(absum2, absum[perm], equal_nan=True)
+    assert np.all(np.isnan(full[4])) and not np.any(np.isnan(np.delete(full, 4, axis=0)))
+
+    def values(x):
+        if fmt == MX_E2M1:
+            nib = np.stack([x & 0xF, x >> 4], axis=-1).reshape(x.shape[0], -1)
+            mag = np.array(E2M1_SPEC)[nib & 7]
+            return np.where(nib & 8, -mag, mag)
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        f8 = torch.float8_e4m3fn if fmt == MX_E4M3 else torch.float8_e5m2
+        return t.view(f8).to(torch.float64).numpy()
+
+    def scaled(x, sx):
+        with np.errstate(invalid="ignore"):
+            scale = np.where(sx == 255, np.nan, np.ldexp(1.0, sx.astype(np.int64) - 127))
+        return values(x) * np.repeat(scale, 32, axis=1)
+
+    S = np.abs(scaled(A, SA)) @ np.abs(scaled(B, SB)).T
+    assert np.isnan(absum.reshape(M, N)[4]).all()
+    keep = np.arange(M) != 4
+    assert np.allclose(absum.reshape(M, N)[keep], S[keep], rtol=1e-12, atol=0)
+    assert np.all(absum.reshape(M, N)[keep] >= np.abs(full[keep]))
 
 
 def test_mx_rejects_partial_blocks():
