@@ -30,8 +30,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgemm_relu.so")
 PROBE_LIB_PATH = os.path.join(_PKG, "libgemm_relu_probe.so")
 
-EXPORTS = ("gemm_relu", "gemm_relu_strerror", "gemm_relu_plan", "gemm_relu_mx",
-           "gemm_relu_mx_plan", "gemm_relu_sp", "gemm_relu_sp_plan")
+EXPORTS = ("gemm_relu", "gemm_relu_strerror", "gemm_relu_configs", "gemm_relu_plan",
+           "gemm_relu_mx", "gemm_relu_mx_plan", "gemm_relu_sp", "gemm_relu_sp_plan")
 
 _lib = None
 
@@ -57,6 +57,8 @@ def library():
     lib.gemm_relu.restype = ctypes.c_int
     lib.gemm_relu_strerror.argtypes = [ctypes.c_int]
     lib.gemm_relu_strerror.restype = ctypes.c_char_p
+    lib.gemm_relu_configs.argtypes = []
+    lib.gemm_relu_configs.restype = ctypes.c_char_p
     lib.gemm_relu_plan.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int]
     lib.gemm_relu_plan.restype = ctypes.c_char_p
@@ -113,6 +115,11 @@ def gemm_relu(A, B, C, M, N, K, in_dtype, out_dtype, transB, stream=None):
     rc = gemm_relu_status(A, B, C, M, N, K, in_dtype, out_dtype, transB, stream)
     if rc != OK:
         raise GemmReluError(rc, gemm_relu_strerror(rc))
+
+
+def gemm_relu_configs():
+    """Names of the kernel configurations this build of the library holds."""
+    return library().gemm_relu_configs().decode().split(",")
 
 
 def gemm_relu_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB):

@@ -55,12 +55,22 @@ def _newer(target, deps):
     return any(os.path.getmtime(d) > t for d in deps)
 
 
+# GEMM_RELU_COMPARISON_CONFIGS=1 in the environment at build time also
+# compiles the comparison configurations (never chosen by plan selection;
+# selectable by name with GEMM_RELU_FORCE_CONFIG).  The default build leaves
+# them out.
+def _config_flags():
+    on = os.environ.get("GEMM_RELU_COMPARISON_CONFIGS", "") not in ("", "0")
+    return ["-DGEMM_RELU_COMPARISON_CONFIGS"] if on else []
+
+
 def _compile(src, force, verbose):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, h) for h in HEADERS] + \
         [os.path.join(INCLUDE, "gemm_relu.h")]
     if force or _newer(obj, deps):
-        cmd = [HIPCC] + HIP_FLAGS + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + HIP_FLAGS + _config_flags() + EXTRA_FLAGS.get(src, []) + \
+            ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -69,6 +69,33 @@ inline const ConfigInfo& config_info(int id)
     return table[id];
 }
 
+// Comparison configurations: variants measured against the ones plan selection
+// uses and never chosen by it (other stage counts and step depths, 8-wave
+// tiles, the bunched 16x16-block tile, the persistent tile loop and the
+// stream-K split; for block-scaled inputs the two-stage 256-wide tiles).  They
+// are compiled only when the library is built with
+// GEMM_RELU_COMPARISON_CONFIGS defined; otherwise GEMM_RELU_FORCE_CONFIG
+// cannot select them and the library has no path that allocates device memory.
+#ifdef GEMM_RELU_COMPARISON_CONFIGS
+inline constexpr bool kComparisonBuilt = true;
+#else
+inline constexpr bool kComparisonBuilt = false;
+#endif
+
+inline constexpr bool comparison_config(int id)
+{
+    return id == CFG_D256x256x64_S2 || id == CFG_D256x256x32_S4 || id == CFG_D256x256x32_S5 ||
+           id == CFG_D256x256x64_S2_16 || id == CFG_D256x256x32_S4_IP ||
+           id == CFG_D256x256x32_S4_ISK || id == CFG_D256x256x32_S4_W8I ||
+           id == CFG_D256x256x32_S5_W8I || id == CFG_D256x256x64_S2_W8 || id == CFG_D256x128x64_S2;
+}
+
+// Whether this build of the library holds kernels of configuration id.
+inline constexpr bool config_built(int id)
+{
+    return kComparisonBuilt || !comparison_config(id);
+}
+
 // K elements per step of a configuration whose 16-bit step is BK16 elements.
 // Block-scaled inputs count K in storage bytes (an E2M1 byte holds 2 elements).
 template <int IN, int BK16>
@@ -167,6 +194,17 @@ hipError_t launch_one(const KernelArgs& args, int grid, hipStream_t stream)
                            dim3(C::NTHREADS), params, 0, stream);
 }
 
+// The launcher of a comparison configuration: instantiated only in a build
+// that holds them.
+template <class C>
+LaunchFn comparison_launcher()
+{
+    if constexpr (kComparisonBuilt)
+        return &launch_one<C>;
+    else
+        return nullptr;
+}
+
 // One table per (input dtype, transB); defined in the instantiation units.
 LaunchFn launcher_f16_nn(int out_dt, int cfg);
 LaunchFn launcher_f16_nt(int out_dt, int cfg);
@@ -202,27 +240,27 @@ inline bool fp8_config(int cfg)
     {                                                                                      \
         switch (cfg) {                                                                     \
         case CFG_D256x256x64_S2:                                                           \
-            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2>::type>;     \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2>::type>(); \
         case CFG_D256x256x32_S4:                                                           \
-            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4>::type>;     \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4>::type>(); \
         case CFG_D256x256x32_S5:                                                           \
-            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S5>::type>;     \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S5>::type>(); \
         case CFG_D256x256x32_S4_I:                                                         \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I>::type>;   \
         case CFG_D256x256x64_S2_16:                                                        \
-            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_16>::type>;  \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_16>::type>(); \
         case CFG_D256x256x32_S4_I16:                                                       \
             return launcher_i16(IN, OUT, TB);                                              \
         case CFG_D256x256x32_S4_IP:                                                        \
-            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_IP>::type>;  \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_IP>::type>(); \
         case CFG_D256x256x32_S4_ISK:                                                       \
-            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_ISK>::type>; \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_ISK>::type>(); \
         case CFG_D256x256x32_S4_W8I:                                                       \
-            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_W8I>::type>; \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_W8I>::type>(); \
         case CFG_D256x256x32_S5_W8I:                                                       \
-            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S5_W8I>::type>; \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S5_W8I>::type>(); \
         case CFG_D256x256x64_S2_W8:                                                        \
-            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_W8>::type>;  \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_W8>::type>(); \
         case CFG_D128x128x64_S3:                                                           \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D128x128x64_S3>::type>;     \
         case CFG_D128x128x64_S2:                                                           \
@@ -262,7 +300,7 @@ inline bool fp8_config(int cfg)
         case CFG_D256x256x32_S4_I:                                                         \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I>::type>;   \
         case CFG_D256x256x32_S4_ISK:                                                       \
-            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_ISK>::type>; \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_ISK>::type>(); \
         case CFG_D128x128x64_S3:                                                           \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D128x128x64_S3>::type>;     \
         case CFG_D128x128x64_S2:                                                           \
@@ -303,11 +341,11 @@ inline bool fp8_config(int cfg)
         case CFG_D256x256x32_S4_I:                                                         \
             return &launch_one<typename CfgOf<IN, OUT, true, CFG_D256x256x32_S4_I>::type>; \
         case CFG_D256x256x64_S2:                                                           \
-            return &launch_one<typename CfgOf<IN, OUT, true, CFG_D256x256x64_S2>::type>;   \
+            return comparison_launcher<typename CfgOf<IN, OUT, true, CFG_D256x256x64_S2>::type>(); \
         case CFG_D128x128x64_S2:                                                           \
             return &launch_one<typename CfgOf<IN, OUT, true, CFG_D128x128x64_S2>::type>;   \
         case CFG_D256x128x64_S2:                                                           \
-            return &launch_one<typename CfgOf<IN, OUT, true, CFG_D256x128x64_S2>::type>;   \
+            return comparison_launcher<typename CfgOf<IN, OUT, true, CFG_D256x128x64_S2>::type>(); \
         default:                                                                           \
             return nullptr;                                                                \
         }                                                                                  \

@@ -12,6 +12,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <string>
 #include <vector>
 
 #include "configs.hpp"
@@ -242,6 +243,7 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     const bool sk_possible = sk_ok && sk_iters >= 2;
     auto usable = [&](int id) {
         return id != CFG_D256x128x64_S2 &&             // built for block-scaled inputs only
+               config_built(id) &&
                (id != CFG_D256x256x32_S4_ISK || sk_possible) &&
                direct_fits(id, N, K, transB) && (!fp8_input(in_dt) || fp8_config(id));
     };
@@ -338,7 +340,7 @@ Plan make_plan_mx(const void* A, const void* SA, const void* B, const void* SB, 
     auto usable = [&](int id) {
         return (id == CFG_D256x256x64_S2 || id == CFG_D256x128x64_S2 || id == CFG_D128x128x64_S2 ||
                 (id == CFG_D256x256x32_S4_I && lds_scales_fit)) &&
-               direct_fits(id, N, ks, 1);
+               config_built(id) && direct_fits(id, N, ks, 1);
     };
     // Estimated time per K, as for the other inputs: rounds of workgroups over
     // the CUs times the tile's area over its efficiency relative to the
@@ -502,6 +504,22 @@ extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64
         if (hipGetLastError() != hipSuccess) return GEMM_RELU_EHIP;
     }
     return GEMM_RELU_OK;
+}
+
+extern "C" const char* gemm_relu_configs(void)
+{
+    static const std::string names = [] {
+        std::string out;
+        for (int id = 0; id < CFG_COUNT; ++id)
+            if (config_built(id)) {
+                if (!out.empty()) out += ',';
+                out += config_info(id).name;
+            }
+        out += ',';
+        out += kSpConfigName;
+        return out;
+    }();
+    return names.c_str();
 }
 
 extern "C" const char* gemm_relu_strerror(int status)

@@ -11,8 +11,9 @@
 // thread-block rasterisation swizzle (panel of tile rows) for L2 reuse.
 //
 // The same kernel takes 8-bit inputs (OCP E4M3 / E5M2): the FP8 GEMM that
-// §4.1 of the first page lists among the kernels the DSL covers.  The pages
-// give it no scale factors, so it is the same definition over the 8-bit values.
+// §4.1 of page "TileLang：GPU/NPU 通用算子 DSL" lists among the kernels the
+// DSL covers.  The pages give it no scale factors, so it is the same
+// definition over the 8-bit values.
 //
 // What is specific to gfx950 here (none of it is on the pages):
 //   * v_mfma_f32_32x32x16_{f16,bf16}: each lane feeds 8 consecutive k of one

@@ -28,9 +28,10 @@ extern "C" {
 #define GEMM_RELU_F16  0 /* IEEE binary16 (inputs or output) */
 #define GEMM_RELU_BF16 1 /* bfloat16 (inputs or output) */
 #define GEMM_RELU_F32  2 /* IEEE binary32 (output only) */
-/* OCP 8-bit floating point (inputs only).  The first page's §4.1 lists an FP8
- * GEMM among the kernels the DSL covers but gives it no scale factors: the
- * product is the same definition over the exact values of the 8-bit inputs. */
+/* OCP 8-bit floating point (inputs only).  §4.1 of page "TileLang：GPU/NPU 通用
+ * 算子 DSL" lists an FP8 GEMM among the kernels the DSL covers but gives it no
+ * scale factors: the product is the same definition over the exact values of
+ * the 8-bit inputs. */
 #define GEMM_RELU_F8_E4M3 3 /* E4M3 ("FN"): bias 7, largest finite 448, no infinities */
 #define GEMM_RELU_F8_E5M2 4 /* E5M2: bias 15, IEEE-style infinities and NaNs */
 /* Block-scaled (OCP Microscaling) element formats, for gemm_relu_mx only. */
@@ -72,13 +73,14 @@ extern "C" {
  * nearest-even into out_dtype.
  *
  * Ownership: the caller owns A, B and C; the library keeps no pointer after the
- * call returns and allocates no device memory, except with the stream-K
- * comparison configuration (chosen only by name, GEMM_RELU_FORCE_CONFIG=
- * d256x256x32_s4_isk): its first call on a stream allocates and zeroes a
+ * call returns and allocates no device memory.  (A build made with
+ * GEMM_RELU_COMPARISON_CONFIGS defined also holds the stream-K comparison
+ * configuration, chosen only by name, GEMM_RELU_FORCE_CONFIG=
+ * d256x256x32_s4_isk: its first call on a stream allocates and zeroes a
  * 128 MiB workspace for that stream (fp32 partial tiles and arrival counters),
  * kept until the process ends.  Calls on one stream share it in stream order;
  * a call on a stream that is being captured into a graph and has no workspace
- * yet takes whole tiles instead.
+ * yet takes whole tiles instead.  The default build has no such path.)
  *
  * Execution: asynchronous on `stream`; the call returns after the launch.  A
  * device-side fault surfaces at the caller's next synchronisation.  With the
@@ -98,6 +100,14 @@ int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64
 const char* gemm_relu_strerror(int status);
 
 /*
+ * gemm_relu_configs — comma-separated names of the kernel configurations this
+ * build of the library holds (the names gemm_relu_plan, gemm_relu_mx_plan and
+ * gemm_relu_sp_plan return, and the values GEMM_RELU_FORCE_CONFIG accepts).
+ * Host-only, a static string, never NULL.
+ */
+const char* gemm_relu_configs(void);
+
+/*
  * gemm_relu_plan — name of the kernel configuration gemm_relu would launch for
  * these arguments, without touching the device ("none" when there is nothing
  * to launch, NULL when gemm_relu would return GEMM_RELU_EINVAL).  Host-only;
@@ -108,7 +118,8 @@ const char* gemm_relu_plan(const void* A, const void* B, const void* C, int64_t 
 
 /*
  * gemm_relu_mx — the block-scaled product: the "MXFP8 block-scaled GEMM" and
- * "CDNA4 MXFP4" items of the first page's §4.1 capability timeline, read as the
+ * "CDNA4 MXFP4" items of the §4.1 capability timeline of page "TileLang：GPU/NPU
+ * 通用算子 DSL", read as the
  * OCP Microscaling (MX) definition.  Every 32 consecutive elements of a row
  * along K share one E8M0 scale (2^(e - 127); e = 255 is NaN), and
  *
@@ -144,7 +155,8 @@ const char* gemm_relu_mx_plan(const void* A, const void* SA, const void* B, cons
 
 /*
  * gemm_relu_sp — the 2:4 structured-sparse product: the "2:4 structured-sparse
- * tensor core (T.gemm_sp)" item of the first page's §4.1 timeline, whose A
+ * tensor core (T.gemm_sp)" item of the §4.1 timeline of page "TileLang：GPU/NPU
+ * 通用算子 DSL", whose A
  * arrives compressed together with its metadata (page "从 TVM 到 TileLang…",
  * §四).  Every row of A is cut along K into groups of 4 consecutive elements
  * with at most two non-zeros; the caller passes them compressed:

@@ -44,6 +44,25 @@ def fp32_sum_bound(absum, ref, K, out_unit_roundoff):
     return K * 2.0 ** -24 * absum + out_unit_roundoff * np.abs(ref) + 2.0 ** -24
 
 
+# Comparison configurations: compiled only into a library built with
+# GEMM_RELU_COMPARISON_CONFIGS=1 (never chosen by plan selection).
+COMPARISON_CONFIGS = ("d256x256x64_s2", "d256x256x32_s4", "d256x256x32_s5", "d256x256x64_s2_16",
+                      "d256x256x32_s4_ip", "d256x256x32_s4_isk", "d256x256x32_s4_w8i",
+                      "d256x256x32_s5_w8i", "d256x256x64_s2_w8", "d256x128x64_s2")
+
+
+def built_configs(names):
+    """The configurations of `names` that the library in the tree holds: every
+    plan-selection configuration, and the comparison ones only in a build made
+    with them (asked of the library; none if it cannot be loaded)."""
+    try:
+        import dense_tiled_gemm_relu_amd as gr
+        have = set(gr.gemm_relu_configs())
+    except Exception:
+        have = set()
+    return [n for n in names if n not in COMPARISON_CONFIGS or n in have]
+
+
 # ------------------------------------------------------------------ GPU side
 def to_device(bits, dtype_code, shape):
     """Storage patterns (uint16 for fp16/bf16, uint8 for the 8-bit formats) ->

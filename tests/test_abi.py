@@ -9,6 +9,7 @@ import sys
 import pytest
 
 import dense_tiled_gemm_relu_amd as gr
+from tests.helpers import COMPARISON_CONFIGS, built_configs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -182,8 +183,8 @@ def test_mx_plan_selection(M, N, K, want, fmt):
     assert gr.gemm_relu_mx_plan(0, 0, 0, 0, C, 0, N, K, fmt, 0) == "none"
 
 
-@pytest.mark.parametrize("name", ["d256x256x32_s4_i", "d256x256x64_s2", "d256x128x64_s2",
-                                  "d128x128x64_s2"])
+@pytest.mark.parametrize("name", built_configs(["d256x256x32_s4_i", "d256x256x64_s2",
+                                                 "d256x128x64_s2", "d128x128x64_s2"]))
 def test_mx_forced_configuration(monkeypatch, name):
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", name)
     assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 8192, 8192, 8192, 7, 0) == name
@@ -235,7 +236,7 @@ def test_sp_plan():
     assert gr.gemm_relu_sp_plan(A, E_, B, C, 64, 8, (1 << 22) + 4, 0, 0, 1) == "unsupported"
 
 
-@pytest.mark.parametrize("name", ["d256x256x32_s4_ip", "d256x256x32_s4_i"])
+@pytest.mark.parametrize("name", built_configs(["d256x256x32_s4_ip", "d256x256x32_s4_i"]))
 def test_comparison_configurations_are_selectable(monkeypatch, name):
     """The persistent tile loop and the 32x32-block tile: forced by name for
     16-bit inputs, never chosen automatically for them (the 16x16-block tile
@@ -253,6 +254,35 @@ def test_16x16_tile_not_built_for_8bit_inputs(monkeypatch):
     assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 4, 0, 1) == "d256x256x32_s4_i"
 
 
+def test_configs_lists_the_plan_names():
+    """gemm_relu_configs names every configuration plan selection can return
+    (and, in a comparison build, the comparison ones too)."""
+    names = gr.gemm_relu_configs()
+    assert len(names) == len(set(names))
+    for want in ("d256x256x32_s4_i16", "d256x256x32_s4_i", "d128x128x64_s3", "d64x64x64_s4",
+                 "d64x32x128_s4", "d32x64x128_s4", "g128x128x64", "g64x64x64", "d128x128x64_s2",
+                 "sp256x256x64_s3"):
+        assert want in names
+    assert set(names) - set(COMPARISON_CONFIGS) <= set(names)
+
+
+def test_comparison_configurations_only_in_a_comparison_build(monkeypatch):
+    """Without the comparison configurations a forced one is not launched:
+    plan selection chooses as if it had not been named (and with them, it is)."""
+    names = set(gr.gemm_relu_configs())
+    cmp_built = set(COMPARISON_CONFIGS) & names
+    assert cmp_built in (set(), set(COMPARISON_CONFIGS))     # all or none
+    for name in ("d256x256x32_s4_isk", "d256x256x32_s4_ip", "d256x256x64_s2"):
+        monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", name)
+        got = gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0)
+        assert got == (name if cmp_built else "d256x256x32_s4_i16")
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x128x64_s2")
+    got = gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 8192, 8192, 8192, 7, 0)
+    assert got == ("d256x128x64_s2" if cmp_built else "d256x256x32_s4_i")
+
+
+@pytest.mark.skipif(not built_configs(["d256x256x32_s4_isk"]),
+                    reason="stream-K is a comparison configuration, not in this build")
 def test_streamk_selection(monkeypatch):
     """Stream-K (the 256x256 tile with its last round split along K) is
     selected by name only, for 16-bit and 8-bit inputs with at least two K

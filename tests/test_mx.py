@@ -8,7 +8,8 @@ import pytest
 import dense_tiled_gemm_relu_amd as gr
 import oracle
 import workloads as wl
-from tests.helpers import check_close, from_device, fp32_sum_bound, out_tensor, unit_roundoff
+from tests.helpers import (built_configs, check_close, from_device, fp32_sum_bound, out_tensor,
+                           unit_roundoff)
 
 pytestmark = pytest.mark.gpu
 
@@ -16,7 +17,7 @@ FMTS = [wl.MX_E4M3, wl.MX_E5M2, wl.MX_E2M1]
 # the interleaved four-stage tile stages scales in LDS by 16 blocks of a row,
 # so it serves K >= 512 only
 INTERLEAVED = "d256x256x32_s4_i"
-CONFIGS = [INTERLEAVED, "d256x256x64_s2", "d256x128x64_s2", "d128x128x64_s2"]
+CONFIGS = built_configs([INTERLEAVED, "d256x256x64_s2", "d256x128x64_s2", "d128x128x64_s2"])
 
 
 def _needs(cfg, K):
@@ -49,12 +50,12 @@ def run_mx(A, SA, B, SB, M, N, K, fmt, out_code, cfg=None, monkeypatch=None):
     return from_device(Cd)
 
 
-def int_mx(M, N, K, fmt, seed, scale_choices=(127,)):
-    """Integer elements in {-2..2} (exact in every format) and scales drawn
-    from scale_choices."""
+def int_mx(M, N, K, fmt, seed, scale_choices=(127,), top=2):
+    """Integer elements in {-top..top} (exact in every format) and scales
+    drawn from scale_choices."""
     rng = np.random.default_rng(seed)
-    a = rng.integers(-2, 3, size=(M, K)).astype(np.float64)
-    b = rng.integers(-2, 3, size=(N, K)).astype(np.float64)
+    a = rng.integers(-top, top + 1, size=(M, K)).astype(np.float64)
+    b = rng.integers(-top, top + 1, size=(N, K)).astype(np.float64)
     if fmt == wl.MX_E2M1:
         A, B = wl.pack_e2m1(wl.e2m1_codes(a)), wl.pack_e2m1(wl.e2m1_codes(b))
     else:
@@ -72,12 +73,12 @@ def int_mx(M, N, K, fmt, seed, scale_choices=(127,)):
                          ids=["tail32", "ragged", "long"])
 def test_mx_integer_unit_scales_bitexact(cfg, fmt, out_code, shape, monkeypatch):
     M, N, K = shape
-    A, SA, B, SB = int_mx(M, N, K, fmt, 900 + fmt)
-    if out_code == wl.BF16:                      # keep |C| inside bf16's exact integers
-        A, SA, B, SB = int_mx(M, N, 64, fmt, 901 + fmt)
-        K = 64
     _needs(cfg, K)
+    # a bf16 C holds every integer only up to 256: elements in {-1, 0, 1} keep
+    # |C| below it (about 4.5 standard deviations of sqrt(4K/9) at K = 1120)
+    A, SA, B, SB = int_mx(M, N, K, fmt, 900 + fmt, top=1 if out_code == wl.BF16 else 2)
     ref = oracle.gemm_relu_mx_ref(A, SA, B, SB, M, N, K, fmt)
+    assert np.abs(ref).max() < (256 if out_code == wl.BF16 else 2048)
     got = run_mx(A, SA, B, SB, M, N, K, fmt, out_code, cfg, monkeypatch)
     assert np.array_equal(got, ref)
     assert not np.any(np.signbit(got))

@@ -17,12 +17,16 @@ import pytest
 import dense_tiled_gemm_relu_amd as gr
 import oracle
 import workloads as wl
-from tests.helpers import (check_close, from_device, fp32_sum_bound, out_tensor, to_device,
-                           unit_roundoff)
-
-pytestmark = pytest.mark.gpu
+from tests.helpers import (built_configs, check_close, from_device, fp32_sum_bound, out_tensor,
+                           to_device, unit_roundoff)
 
 SK = "d256x256x32_s4_isk"
+
+# a comparison configuration: in the library only when it is built with
+# GEMM_RELU_COMPARISON_CONFIGS=1
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not built_configs([SK]),
+                                 reason="stream-K is a comparison configuration, not in this build")]
 
 
 @pytest.fixture(autouse=True)

@@ -98,7 +98,8 @@ WORKLOADS = {
                                          out_dtype=F16, transB=0, dist="uniform"),
     "gemm_relu_f16_64x8192x8192": dict(index=6, M=64, N=8192, K=8192, in_dtype=F16,
                                        out_dtype=F16, transB=0, dist="uniform"),
-    # the FP8 GEMM of the first page's capability list at the headline shape
+    # the FP8 GEMM of the capability list of page "TileLang：GPU/NPU 通用算子 DSL"
+    # (§4.1), at the headline shape
     "gemm_relu_f8e4m3_8192": dict(index=7, M=8192, N=8192, K=8192, in_dtype=F8E4M3,
                                   out_dtype=F16, transB=0, dist="uniform"),
     # block-scaled (gemm_relu_mx): the MXFP4 / MXFP8 of the same list, B stored (N, K)
