@@ -4,8 +4,14 @@ One step = one gemm_relu call (every stage of the hot path: tile rasterisation,
 global->LDS pipeline, MFMA contraction, ReLU, convert, store) over inputs
 already resident in HBM.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
+                    [--workload NAME] [--no-cpu-baseline]
+
+Before the W counted warm-up calls, calls of the same step run untimed for at
+least MS milliseconds (default 300; the line reports how many as
+settle.calls): the chip's power-managed clock falls within 0.2 s of idling
+and takes 50-100 ms of load to recover, so without it a short warm-up after
+the host-side input generation times the clock ramp, not the kernel.
     python bench.py --table      # one JSON line per workload (warm and cold L2/MALL)
     python bench.py --vendor     # the vendor GEMM (+ a separate ReLU) beside it, per workload
 
@@ -36,14 +42,24 @@ HBM_GBPS = 8000.0
 METRIC = "TFLOP/s and % of MI355X fp16 MFMA peak, fp16 GEMM+ReLU 8192³"
 KERNEL_SOURCES = ["dense_tiled_gemm_relu_amd/csrc/gemm_relu_kernel.hpp",
                   "dense_tiled_gemm_relu_amd/csrc/configs.hpp",
-                  "dense_tiled_gemm_relu_amd/csrc/gemm_relu_api.hip"]
+                  "dense_tiled_gemm_relu_amd/csrc/gemm_relu_api.hip",
+                  "dense_tiled_gemm_relu_amd/csrc/inst_i16.hip"]
+
+
+def _code_only(text):
+    """Source text without comments and blank space: a comment edit does not
+    change the kernel a counter summary was taken on."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
 
 
 def kernel_source_hash():
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -80,6 +96,51 @@ def measured_traffic(workload, launches_per_record=None):
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def measured_cycles(workload):
+    """Shader-clock cycles per launch (GRBM_GUI_ACTIVE of one XCD) from the
+    committed counter summary, if it was taken on the current kernel sources;
+    else None.  A launch takes the same number of cycles at any clock (measured:
+    the same count for 930 us and 797 us dispatches), so cycles / duration is
+    the clock the launch ran at."""
+    path = os.path.join(ROOT, "profiles", "cycles_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("cycles_per_launch")
+
+
+def ingest_cycles(workload, pmc_dir):
+    """GRBM_GUI_ACTIVE per launch of the GEMM kernel (sum of the XCD rows / 8)
+    and the launch durations from one rocprofv3 --pmc GRBM_GUI_ACTIVE
+    --kernel-trace run -> profiles/cycles_<workload>.json, stamped with the
+    kernel source hash."""
+    import csv
+    import glob
+    g = _pmc_per_dispatch(pmc_dir, "GRBM_GUI_ACTIVE", "gemm_relu_kernel")
+    dur = {}
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if "gemm_relu_kernel" in r["Kernel_Name"]:
+                dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    d = [dur[k] for k in sorted(dur)]
+    per_xcd = [x / 8.0 for x in g]
+    cyc = sorted(per_xcd)[len(per_xcd) // 2]
+    rec = {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+           "cycles_per_launch": int(cyc), "launches": len(per_xcd),
+           "cycles_min": int(min(per_xcd)), "cycles_max": int(max(per_xcd))}
+    if len(d) == len(per_xcd):
+        mhz = [c / t / 1e6 for c, t in zip(per_xcd, d)]
+        rec.update(clock_mhz_first=round(mhz[0]), clock_mhz_last=round(mhz[-1]),
+                   duration_us_first=round(d[0] * 1e6, 1), duration_us_last=round(d[-1] * 1e6, 1))
+    path = os.path.join(ROOT, "profiles", "cycles_%s.json" % workload)
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
 
 
 COPY_BYTES = 256 * 1024 * 1024
@@ -156,7 +217,7 @@ def cpu_baseline(w, A, B, target_s=15.0):
         R = int(min(M, max(R + 1, R * target_s / max(dt, 1e-3))))
     flops = 2.0 * R * N * K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "cpu_model": host_cpu()[0], "kind": "oracle",
             "sample": "rows 0..%d of A (%d x %d x %d multiply-adds of the %s workload, "
                       "binary64), %.2f s wall" % (R - 1, R, N, K, w["name"], dt)}
 
@@ -179,7 +240,7 @@ def cpu_baseline_mx(w, target_s=15.0):
     flops = 2.0 * R * N * K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s",
             "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count())),
-            "kind": "oracle",
+            "cpu_model": host_cpu()[0], "kind": "oracle",
             "sample": "rows 0..%d of A (%d x %d x %d block-scaled multiply-adds of the %s "
                       "workload, binary64), %.2f s wall" % (R - 1, R, N, K, w["name"], dt)}
 
@@ -203,7 +264,7 @@ def cpu_baseline_sp(w, target_s=15.0):
     flops = 2.0 * R * N * K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s",
             "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count())),
-            "kind": "oracle",
+            "cpu_model": host_cpu()[0], "kind": "oracle",
             "sample": "rows 0..%d of A (%d x %d x %d dense-equivalent multiply-adds of the %s "
                       "workload, binary64), %.2f s wall" % (R - 1, R, N, K, w["name"], dt)}
 
@@ -561,9 +622,13 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    # 200 calls: the power-limited clock settles within about 60-150 calls of
-    # the 8192^3 kernel (tens of milliseconds) and then holds steady
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    # Before the counted warm-up: calls of the same step for at least this
+    # long.  The power-managed clock drops within 0.2 s of idle and needs
+    # 50-100 ms of load to come back (measured: the first 10 calls of a fresh
+    # process average 1108 us, calls 60-400 about 798 us), so a short
+    # warm-up right after the host-side input generation would time the ramp.
+    ap.add_argument("--settle-ms", type=float, default=300.0)
     ap.add_argument("--workload", default="gemm_relu_f16_8192", choices=sorted(wl.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--table", action="store_true",
@@ -581,9 +646,15 @@ def main():
                     help="run only the plain copy used to scale HBM byte counters")
     ap.add_argument("--ingest-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"),
                     help="rocprofv3 --pmc output dirs -> profiles/traffic_<workload>.json")
+    ap.add_argument("--ingest-cycles", metavar="PMC_DIR",
+                    help="rocprofv3 --pmc GRBM_GUI_ACTIVE --kernel-trace output dir -> "
+                         "profiles/cycles_<workload>.json")
     args = ap.parse_args()
     if args.ingest_traffic:
         ingest_traffic(args.workload, *args.ingest_traffic)
+        return
+    if args.ingest_cycles:
+        ingest_cycles(args.workload, args.ingest_cycles)
         return
     if args.calibrate_copy:
         calibrate_copy()
@@ -624,6 +695,12 @@ def main():
     sparse = w.get("sparse", False)
     peak = peak_tflops(ic, sparse)
 
+    settle_calls, t_end = 0, time.perf_counter() + args.settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        step()
+        settle_calls += 1
+        if settle_calls % 8 == 0:
+            torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -659,6 +736,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "calls": settle_calls},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -670,6 +748,11 @@ def main():
                    "accumulate": "f32", "inputs": w["dist"], "tile_config": plan},
         "roofline": roofline(flops, nbytes, kernel_ms, peak, measured_traffic(args.workload)),
     }
+    cycles = measured_cycles(args.workload)
+    if cycles is not None:
+        out["clock"] = {"mhz": round(cycles / (kernel_ms * 1e-3) / 1e6),
+                        "source": "shader cycles per launch (GRBM_GUI_ACTIVE per XCD, "
+                                  "profiles/cycles_%s.json) / kernel_ms" % args.workload}
     ceiling = mfma_ceiling(gr, stream, kind=ceiling_kind(ic, sparse, plan))
     if ceiling is not None:
         out["mfma_ceiling"] = dict(ceiling, frac=round(achieved / ceiling["tflops"], 4))
