@@ -63,9 +63,10 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIB):
+    path = os.environ.get("ORACLE_LIB") or _build.LIB      # another build of oracle.c (sanitizers)
+    if path == _build.LIB and not os.path.exists(path):
         _build.build()
-    lib = ctypes.CDLL(_build.LIB)
+    lib = ctypes.CDLL(path)
     u16p = ctypes.POINTER(ctypes.c_uint16)
     f64p = ctypes.POINTER(ctypes.c_double)
     i64p = ctypes.POINTER(ctypes.c_int64)
