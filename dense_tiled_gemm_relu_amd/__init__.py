@@ -49,6 +49,10 @@ def library():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError("HIP library %s is not built; run __graft_entry__.build()" % LIB_PATH)
+    # PyTorch (the source of device memory and streams here) brings its own HIP
+    # runtime; loading it first makes the library bind to that same runtime
+    # instead of pulling a second copy into the process.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     i64 = ctypes.c_int64
     vp = ctypes.c_void_p

@@ -32,6 +32,7 @@ enum ConfigId : int {
     CFG_D32x64x128_S4,
     CFG_G128x128x64,
     CFG_G64x64x64,
+    CFG_D256x192x32_S4_I16,
     CFG_COUNT
 };
 
@@ -65,6 +66,7 @@ inline const ConfigInfo& config_info(int id)
         {"d32x64x128_s4", 32, 64, true},
         {"g128x128x64", 128, 128, false},
         {"g64x64x64", 64, 64, false},
+        {"d256x192x32_s4_i16", 256, 192, true},
     };
     return table[id];
 }
@@ -132,6 +134,13 @@ template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x64_S2
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I16> {
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 4, true, true, 16>;
 };
+// The same tile 192 columns wide (waves of 128 x 96, 8 x 6 blocks), for B
+// stored (N,K): the narrower last round of a two-region grid, where whole
+// 256x256 rounds leave a partial one (4096 x 7168: 256 tiles of 256 x 256,
+// then 256 of 256 x 192 instead of 192 more of 256 x 256).
+template <int IN, int OUT> struct CfgOf<IN, OUT, true, CFG_D256x192x32_S4_I16> {
+    using type = Cfg<IN, OUT, true, 256, 192, bk_of<IN, 32>, 2, 2, 4, true, true, 16>;
+};
 // The 32x32-block interleaved tile as a persistent kernel: at most one workgroup
 // per CU, each looping over its tiles (the Ascend version's T.Persistent).
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_IP> {
@@ -194,6 +203,15 @@ hipError_t launch_one(const KernelArgs& args, int grid, hipStream_t stream)
                            dim3(C::NTHREADS), params, 0, stream);
 }
 
+// A two-region grid: whole rounds of C1 tiles, then a round of C2 tiles.
+template <class C1, class C2>
+hipError_t launch_two(const KernelArgs& args, int grid, hipStream_t stream)
+{
+    void* params[] = {const_cast<KernelArgs*>(&args)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_relu_kernel_2r<C1, C2>), dim3(grid),
+                           dim3(C1::NTHREADS), params, 0, stream);
+}
+
 // The launcher of a comparison configuration: instantiated only in a build
 // that holds them.
 template <class C>
@@ -217,8 +235,12 @@ LaunchFn launcher_f8e5m2_nt(int out_dt, int cfg);
 LaunchFn launcher_mx_e4m3(int out_dt, int cfg);
 LaunchFn launcher_mx_e5m2(int out_dt, int cfg);
 LaunchFn launcher_mx_e2m1(int out_dt, int cfg);
-// the 16x16-block interleaved tile for a 16-bit input type (inst_i16.hip)
+// the 16x16-block interleaved tiles for a 16-bit input type (inst_i16.hip):
+// 256 x 256 (either B layout), 256 x 192 (B stored (N,K)), and the two-region
+// grid of both (B stored (N,K))
 LaunchFn launcher_i16(int in_dt, int out_dt, bool transB);
+LaunchFn launcher_i16_192(int in_dt, int out_dt);
+LaunchFn launcher_i16_2r(int in_dt, int out_dt);
 
 // Configurations built for 8-bit inputs: the ones plan selection can choose
 // (the 16-bit comparison variants are not instantiated for them).
@@ -251,6 +273,8 @@ inline bool fp8_config(int cfg)
             return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x64_S2_16>::type>(); \
         case CFG_D256x256x32_S4_I16:                                                       \
             return launcher_i16(IN, OUT, TB);                                              \
+        case CFG_D256x192x32_S4_I16:                                                       \
+            return TB ? launcher_i16_192(IN, OUT) : nullptr;                               \
         case CFG_D256x256x32_S4_IP:                                                        \
             return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_IP>::type>(); \
         case CFG_D256x256x32_S4_ISK:                                                       \

@@ -37,6 +37,8 @@ struct Env {
     int panel = 0;        // GEMM_RELU_PANEL=<tile rows>, 0 = default
     int nxcd = 8;         // GEMM_RELU_XCDS=<n>: 1 disables the XCD-aware tile remap
     int sk_units = 0;     // GEMM_RELU_SK_UNITS=<n>: stream-K units, 0 = one per CU
+    int split_cols = -1;  // GEMM_RELU_SPLIT_COLS=<c>: two-region grid with c 256-wide tile
+                          // columns first (0: never split); -1 = plan selection decides
 };
 
 // Debug and tuning switches, read on every call so a process can change them
@@ -57,6 +59,8 @@ Env env()
     if (x && x[0]) e.nxcd = std::atoi(x) > 0 ? std::atoi(x) : 1;
     const char* u = std::getenv("GEMM_RELU_SK_UNITS");
     if (u && u[0]) e.sk_units = std::max(0, std::atoi(u));
+    const char* c = std::getenv("GEMM_RELU_SPLIT_COLS");
+    if (c && c[0]) e.split_cols = std::max(0, std::atoi(c));
     return e;
 }
 
@@ -102,7 +106,13 @@ struct Plan {
     int cfg = -1;
     int tiles_m = 0, tiles_n = 0;
     int dp_tiles = 0, sk_units = 0;   // stream-K configurations
+    // two-region grid: cfg tiles over the first split columns, then cfg2
+    // (d256x192x32_s4_i16) tiles over the rest
+    int cfg2 = -1;
+    int tiles1 = 0, tiles_m2 = 0, tiles_n2 = 0, n_org2 = 0;
 };
+
+
 
 // ---- stream-K split (the 256x256 interleaved tile, selected by name only):
 // whole rounds of tiles over the CUs keep one workgroup per tile; the
@@ -196,6 +206,45 @@ bool direct_fits(int id, int64_t N, int64_t K, int transB)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+constexpr const char* kSplitName = "d256x256x32_s4_i16+d256x192x32_s4_i16";
+
+// ---- two-region grid (16-bit inputs, B stored (N,K)): when whole rounds of
+// 256x256 tiles over the CUs leave a partial round, the first `c` tile columns
+// (c * tiles_m = whole rounds) stay 256x256 and the remaining columns are cut
+// into 256x192 tiles, at most one round of them.  Measured efficiency of the
+// 256x192 tile per flop relative to 256x256 (kSplitEff) prices that round.
+constexpr double kSplitEff = 0.93;
+
+bool plan_split(Plan& p, int64_t M, int64_t N, int forced_cols)
+{
+    const int64_t tm = p.tiles_m, tn = p.tiles_n, tiles = tm * tn;
+    int64_t c = -1;
+    if (forced_cols >= 0) {
+        c = forced_cols;
+    } else {
+        const int64_t full = tiles / kNumCUs;
+        if (full < 1 || tiles % kNumCUs == 0 || (full * kNumCUs) % tm != 0) return false;
+        c = full * kNumCUs / tm;
+    }
+    if (c <= 0 || c >= tn) return false;
+    const int64_t n_org = c * 256, w2 = N - n_org;
+    const int64_t tn2 = ceil_div(w2, 192), tiles2 = ceil_div(M, 256) * tn2;
+    if (forced_cols < 0) {
+        const double plain = double(ceil_div(tiles, kNumCUs));
+        const double split = double(c * tm / kNumCUs) +
+                             double(ceil_div(tiles2, kNumCUs)) * (192.0 / 256.0) / kSplitEff;
+        if (split >= 0.95 * plain) return false;
+    }
+    if (c * tm + tiles2 > INT32_MAX) return false;
+    p.cfg2 = CFG_D256x192x32_S4_I16;
+    p.tiles1 = int(c * tm);
+    p.tiles_n = int(c);
+    p.tiles_m2 = int(ceil_div(M, 256));
+    p.tiles_n2 = int(tn2);
+    p.n_org2 = int(n_org);
+    return true;
+}
+
 Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
                int in_dt, int out_dt, int transB, const Env& e, bool sk_ok = true)
 {
@@ -243,6 +292,7 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     const bool sk_possible = sk_ok && sk_iters >= 2;
     auto usable = [&](int id) {
         return id != CFG_D256x128x64_S2 &&             // built for block-scaled inputs only
+               (id != CFG_D256x192x32_S4_I16 || transB) &&    // built for B stored (N,K) only
                config_built(id) &&
                (id != CFG_D256x256x32_S4_ISK || sk_possible) &&
                direct_fits(id, N, K, transB) && (!fp8_input(in_dt) || fp8_config(id));
@@ -282,6 +332,9 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
                 cfg = id;
         if (cfg < 0) cfg = tiles(CFG_G128x128x64) >= kNumCUs ? CFG_G128x128x64 : CFG_G64x64x64;
     }
+    // GEMM_RELU_SPLIT_COLS=<c> > 0 forces the two-region grid (on the 256x256
+    // tile) wherever it can be built
+    if (e.split_cols > 0 && transB && usable(CFG_D256x256x32_S4_I16)) cfg = CFG_D256x256x32_S4_I16;
     const int64_t tm = ceil_div(M, config_info(cfg).bm), tn = ceil_div(N, config_info(cfg).bn);
     if (tm * tn > lim) {
         p.status = GEMM_RELU_EUNSUPPORTED;
@@ -290,6 +343,12 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     p.cfg = cfg;
     p.tiles_m = int(tm);
     p.tiles_n = int(tn);
+    // a narrower last round for 16-bit inputs with B stored (N,K): chosen by
+    // the cost model unless a configuration was forced; GEMM_RELU_SPLIT_COLS
+    // forces (or, with 0, forbids) it
+    if (cfg == CFG_D256x256x32_S4_I16 && transB && e.split_cols != 0 &&
+        (e.split_cols > 0 || forced < 0))
+        plan_split(p, M, N, e.split_cols > 0 ? e.split_cols : -1);
     if (config_info(cfg).streamk) {
         const SkSplit sp = sk_split(tm * tn, sk_iters, e.sk_units);
         p.dp_tiles = sp.dp_tiles;
@@ -492,12 +551,21 @@ extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64
         args.sk_units = p.sk_units;
     }
 
-    LaunchFn fn = pick_launcher(in_dtype, out_dtype, transB, p.cfg);
+    LaunchFn fn = p.cfg2 >= 0 ? launcher_i16_2r(in_dtype, out_dtype)
+                              : pick_launcher(in_dtype, out_dtype, transB, p.cfg);
     if (!fn) return GEMM_RELU_EUNSUPPORTED;
     const int tiles = p.tiles_m * p.tiles_n;
-    const int grid = config_info(p.cfg).persistent ? std::min(tiles, kNumCUs)
-                     : config_info(p.cfg).streamk  ? p.dp_tiles + p.sk_units
-                                                   : tiles;
+    int grid = config_info(p.cfg).persistent ? std::min(tiles, kNumCUs)
+               : config_info(p.cfg).streamk  ? p.dp_tiles + p.sk_units
+                                             : tiles;
+    if (p.cfg2 >= 0) {
+        args.tiles1 = p.tiles1;
+        args.tiles_m2 = p.tiles_m2;
+        args.tiles_n2 = p.tiles_n2;
+        args.panel2 = panel < p.tiles_m2 ? panel : p.tiles_m2;
+        args.n_org2 = p.n_org2;
+        grid = p.tiles1 + p.tiles_m2 * p.tiles_n2;
+    }
     if (fn(args, grid, st) != hipSuccess) return GEMM_RELU_EHIP;
     if (e.sync) {
         if (hipStreamSynchronize(st) != hipSuccess) return GEMM_RELU_EHIP;
@@ -515,6 +583,8 @@ extern "C" const char* gemm_relu_configs(void)
                 if (!out.empty()) out += ',';
                 out += config_info(id).name;
             }
+        out += ',';
+        out += kSplitName;
         out += ',';
         out += kSpConfigName;
         return out;
@@ -541,7 +611,7 @@ extern "C" const char* gemm_relu_plan(const void* A, const void* B, const void* 
     if (p.status == GEMM_RELU_EINVAL) return nullptr;
     if (p.status != GEMM_RELU_OK) return "unsupported";
     if (p.empty) return "none";
-    return config_info(p.cfg).name;
+    return p.cfg2 >= 0 ? kSplitName : config_info(p.cfg).name;
 }
 
 extern "C" int gemm_relu_mx(const void* A, const void* SA, const void* B, const void* SB, void* C,

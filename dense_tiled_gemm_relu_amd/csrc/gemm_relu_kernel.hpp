@@ -79,6 +79,18 @@ struct KernelArgs {
     float* ws;
     unsigned* flags;
     int dp_tiles, sk_units;
+    // Two-region grids (a last round of narrower tiles): workgroups [0, tiles1)
+    // take the tiles_m x tiles_n tiles of the columns [0, n_org2); the rest take
+    // the tiles_m2 x tiles_n2 tiles of the second configuration over the
+    // columns [n_org2, N).  tiles1 is a multiple of nxcd.
+    int tiles1;
+    int tiles_m2, tiles_n2, panel2, n_org2;
+};
+
+// The tiles one configuration covers inside a launch: a grid of tiles_m x
+// tiles_n tiles whose first column starts at n_org.
+struct Region {
+    int tiles_m, tiles_n, panel, n_org;
 };
 
 // ------------------------------------------------------------------ helpers
@@ -332,7 +344,8 @@ struct Cfg {
     static constexpr int LOADS_PER_STAGE = A_PER_THREAD + B_PER_THREAD;  // vm ops per wave per stage
 
     static_assert(BM % (MB * WAVES_M) == 0 && BN % (MB * WAVES_N) == 0, "wave tiling");
-    static_assert(MB == 32 || TRANS_B || BN * EB >= 256, "16x16 blocks read (K,N) B rows of >= 16 chunks");
+    static_assert(MB == 32 || TRANS_B || (BN * EB) % 256 == 0,
+                  "16x16 blocks read (K,N) B rows of whole 16-chunk bank windows");
     static_assert(BK * EB == 64 || BK * EB == 128 || BK * EB == 256, "k-contiguous rows of 64, 128 or 256 bytes");
     static_assert(KSUB >= 1 && BK % In::KMF == 0, "whole MFMA k-steps per BK step");
     static_assert(KSUB % 2 == 0 || INTERLEAVE_, "an odd k-step count needs the step-parity tags of the interleaved loop");
@@ -360,8 +373,9 @@ struct Cfg {
     static constexpr int REGIONS = LOADS_PER_STAGE / KSUB;      // = copies per k-step
     static_assert(!INTERLEAVE || (DIRECT && STAGES >= 3), "interleave needs >= 3 direct stages");
     static_assert(!INTERLEAVE || (LOADS_PER_STAGE % KSUB == 0 && REGIONS >= 1 &&
-                                  NM % REGIONS == 0),
-                  "interleave: copies and MFMAs must split evenly over the regions");
+                                  (MB == 16 || NM % REGIONS == 0)),
+                  "interleave: copies split evenly over the k-steps (and, for 32x32 blocks, "
+                  "MFMAs over the regions; 16x16-block tiles take NM r / R .. NM (r+1) / R)");
     // Copies issued after the last copy of stage t+1 when the wave waits for it
     // (start of the last k-step of step t) in the steady state: the whole of
     // stages t+2 .. t+S-2 and the first KSUB-1 k-steps' share of stage t+S-1
@@ -468,7 +482,7 @@ struct SkState {
 template <class C>
 __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
                                                GR_LDS unsigned char* smem,
-                                               GR_LDS SkState* sk = nullptr)
+                                               GR_LDS SkState* sk, const Region& reg)
 {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::STAGES;
     constexpr int TM = C::TM, TN = C::TN, KSUB = C::KSUB;
@@ -484,7 +498,7 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     int tm, tn;
-    tile_coords(wg, args.tiles_m, args.tiles_n, args.panel, args.nxcd, tm, tn);
+    tile_coords(wg, reg.tiles_m, reg.tiles_n, reg.panel, args.nxcd, tm, tn);
     const int m0 = tm * BM;
     // (K,N) B on the direct path: the last tile column is moved back to end at N,
     // so every B chunk it copies lies inside its row.  The columns it shares with
@@ -492,8 +506,8 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
     // tile's first stored column): each element of C has one writer, so results
     // do not depend on which tile finishes last, even when the two tiles sum
     // their K range in different pieces.
-    const int n0 = (C::DIRECT && !C::TRANS_B) ? min(tn * BN, N - BN) : tn * BN;
-    const int n_own = tn * BN;
+    const int n_own = reg.n_org + tn * BN;
+    const int n0 = (C::DIRECT && !C::TRANS_B) ? min(n_own, N - BN) : n_own;
     // Direct path: K / BK full steps through the copy pipeline plus, if K % BK,
     // one register-staged tail step.  Register-staged path: ceil(K / BK) steps.
     // A stream-K piece: its full steps from kt0 on, and the tail step if it
@@ -1084,11 +1098,15 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
                 // one: B 0..3 after the first half, A blocks 2k, 2k+1 after
                 // region 4 + k, B 4..7 at the end.  Every read then has at
                 // least four regions (32 MFMAs) before its first use.
-                static_assert(TM == 8 && TN == 8 && KSUB == 1 && R == 8 && NM == 64 &&
-                                  C::LOADS_PER_STAGE == 8,
-                              "in-place 16x16 steps: 8 x 8 blocks, one copy per region");
+                // Narrower tiles (TN = 6: 256 x 192) keep the eight regions, with
+                // TN / 2 B blocks a half and one copy in each of the first
+                // LOADS_PER_STAGE regions.
+                static_assert(TM == 8 && TN % 2 == 0 && TN <= 8 && KSUB == 1 &&
+                                  C::LOADS_PER_STAGE <= 8,
+                              "in-place 16x16 steps: 8 x TN blocks, at most one copy per region");
                 constexpr int QA = TM * FRAG_CH;
                 constexpr int QB = C::TRANS_B ? FRAG_CH : TR_READS;     // reads per B block
+                constexpr int HB = TN / 2;                                // B blocks per half
                 for (; t < t_steady; ++t) {
                     const int ld_stage = (t + S - 1) % S;
                     const int ld_k0 = (t + S - 1) * BK;
@@ -1113,20 +1131,20 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
                         __builtin_amdgcn_sched_barrier(0);
                         if constexpr (r < APT)
                             dma16(ga, a_src[r], lsa + (r * C::NWAVES + wave) * 1024);
-                        else
+                        else if constexpr (r < C::LOADS_PER_STAGE)
                             dma16(gb, b_src[r - APT], lsb + ((r - APT) * C::NWAVES + wave) * 1024);
                         constexpr int half = r / 4, i0 = 2 * (r % 4);
 #pragma unroll
                         for (int di = 0; di < 2; ++di)
 #pragma unroll
-                            for (int jj = 0; jj < 4; ++jj) {
+                            for (int jj = 0; jj < HB; ++jj) {
                                 const int i = i0 + di;
-                                const int j = 4 * half + (di ? 3 - jj : jj);
+                                const int j = HB * half + (di ? HB - 1 - jj : jj);
                                 acc[i][j] = In::mfma(fr[0].b[j], fr[0].a[i], acc[i][j]);
                             }
                         if constexpr (r == 3 || r == 7) {
 #pragma unroll
-                            for (int q = QA + 4 * half * QB; q < QA + (4 * half + 4) * QB; ++q)
+                            for (int q = QA + HB * half * QB; q < QA + (HB * half + HB) * QB; ++q)
                                 read_op(rd_stage, 0, q, fr[0]);
                         }
                         if constexpr (r >= 4) {
@@ -1295,7 +1313,9 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
     constexpr int OB = OutTraits<C::OUT_DT>::bytes;
     constexpr bool STAGED = OB == 2 && BM * BN * 2 <= C::LDS_BYTES;
     constexpr int RB = BN * 2, RCH = BN / 8;          // staged: bytes and chunks per tile row
-    constexpr int XM = (RCH < 16 ? RCH : 16) - 1;
+    // chunk swizzle mask: the largest power of two <= 16 dividing RCH, less one
+    // (a row of 24 chunks XORs inside aligned groups of 8)
+    constexpr int XM = (RCH % 16 == 0 ? 16 : RCH % 8 == 0 ? 8 : RCH % 4 == 0 ? 4 : 1) - 1;
     auto put_group = [&](int i, int j, int q, const f32x4_t& x) {
         float v[4];
 #pragma unroll
@@ -1395,13 +1415,9 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
     }
     if constexpr (STAGED) {
         barrier_lds();
-        constexpr int ROWS_PER_PASS = C::NTHREADS / RCH;
-        static_assert(C::NTHREADS % RCH == 0 && BM % ROWS_PER_PASS == 0, "epilogue row passes");
-        const int cc = tid % RCH;
-#pragma unroll 4
-        for (int r = tid / RCH; r < BM; r += ROWS_PER_PASS) {
+        auto store_chunk = [&](int r, int cc) {
             const int m = m0 + r, n = n0 + 8 * cc;
-            if (m >= M || n >= N || n + 8 <= n_own) continue;
+            if (m >= M || n >= N || n + 8 <= n_own) return;
             const u32x4_t v = *reinterpret_cast<const GR_LDS u32x4_t*>(
                 smem + r * RB + ((cc ^ (r & XM)) << 4));
             unsigned short* dst = reinterpret_cast<unsigned short*>(args.C) + (size_t)m * N + n;
@@ -1415,6 +1431,18 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
                     if (n + e >= n_own && n + e < N)
                         dst[e] = (unsigned short)(v[e >> 1] >> (16 * (e & 1)));
             }
+        };
+        if constexpr (C::NTHREADS % RCH == 0) {
+            // whole rows per pass: thread tid keeps chunk tid % RCH
+            constexpr int ROWS_PER_PASS = C::NTHREADS / RCH;
+            static_assert(BM % ROWS_PER_PASS == 0, "epilogue row passes");
+            const int cc = tid % RCH;
+#pragma unroll 4
+            for (int r = tid / RCH; r < BM; r += ROWS_PER_PASS) store_chunk(r, cc);
+        } else {
+            static_assert((BM * RCH) % C::NTHREADS == 0, "epilogue chunk passes");
+#pragma unroll 4
+            for (int idx = tid; idx < BM * RCH; idx += C::NTHREADS) store_chunk(idx / RCH, idx % RCH);
         }
     }
 }
@@ -1495,19 +1523,45 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
                 sk->lo = lo + pc.kt1 - pc.kt0;
             }
             barrier_lds();
-            gemm_relu_tile<C>(args, sk->wg, smem, sk);
+            gemm_relu_tile<C>(args, sk->wg, smem, sk, Region{args.tiles_m, args.tiles_n, args.panel, 0});
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         }
     } else if constexpr (C::PERSISTENT) {
         const int total = args.tiles_m * args.tiles_n;
         for (int wg = blockIdx.x; wg < total; wg += gridDim.x) {
-            gemm_relu_tile<C>(args, wg, smem);
+            gemm_relu_tile<C>(args, wg, smem, nullptr, Region{args.tiles_m, args.tiles_n, args.panel, 0});
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             barrier_lds();
         }
     } else {
-        gemm_relu_tile<C>(args, blockIdx.x, smem);
+        gemm_relu_tile<C>(args, blockIdx.x, smem, nullptr,
+                          Region{args.tiles_m, args.tiles_n, args.panel, 0});
     }
+}
+
+// Whole-tile rounds with a narrower last round: the first tiles1 workgroups
+// (whole rounds of CUs) take C1 tiles over the columns [0, n_org2), the rest
+// take C2 tiles over [n_org2, N) — one round of narrower tiles instead of a
+// partly idle round of full ones.  No tile depends on another, so the two
+// kinds need no synchronisation; the dispatcher starts a C2 workgroup on each
+// CU as its last C1 workgroup retires.  This is the scheduling aim of the
+// T.Persistent form of page "TileLang：GPU/NPU 通用算子 DSL", §3.3 (every CU
+// busy to the end), reached with whole tiles instead of a tile loop.
+template <class C1, class C2>
+__global__ void __launch_bounds__(C1::NTHREADS, 1) gemm_relu_kernel_2r(KernelArgs args)
+{
+    static_assert(C1::NTHREADS == C2::NTHREADS && !C1::STREAMK && !C2::STREAMK &&
+                      !C1::PERSISTENT && !C2::PERSISTENT,
+                  "two-region grids: whole tiles of two configurations with one block size");
+    constexpr int LDS = C1::LDS_BYTES > C2::LDS_BYTES ? C1::LDS_BYTES : C2::LDS_BYTES;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[LDS];
+    GR_LDS unsigned char* smem = (GR_LDS unsigned char*)(smem_raw);
+    const int wg = blockIdx.x;
+    if (wg < args.tiles1)
+        gemm_relu_tile<C1>(args, wg, smem, nullptr, Region{args.tiles_m, args.tiles_n, args.panel, 0});
+    else
+        gemm_relu_tile<C2>(args, wg - args.tiles1, smem, nullptr,
+                           Region{args.tiles_m2, args.tiles_n2, args.panel2, args.n_org2});
 }
 
 }  // namespace gemm_relu_hip

@@ -1,5 +1,6 @@
 // Instantiations of the interleaved 256x256 tile with 16x16x32 MFMA blocks,
-// 16-bit inputs, both B layouts, every output type.  Kept apart from the other
+// 16-bit inputs, both B layouts, every output type; its 256x192 form and the
+// two-region grid of both for B stored (N,K).  Kept apart from the other
 // configurations because this unit is compiled with the matrix instructions in
 // their VGPR form, which keeps the 64 small accumulators in place.
 #include "configs.hpp"
@@ -21,6 +22,47 @@ LaunchFn launcher_i16(int in_dt, int out_dt, bool transB)
 {
     if (in_dt == DT_F16) return transB ? i16_out<DT_F16, true>(out_dt) : i16_out<DT_F16, false>(out_dt);
     if (in_dt == DT_BF16) return transB ? i16_out<DT_BF16, true>(out_dt) : i16_out<DT_BF16, false>(out_dt);
+    return nullptr;
+}
+
+template <int IN, int OUT>
+using Big = typename CfgOf<IN, OUT, true, CFG_D256x256x32_S4_I16>::type;
+template <int IN, int OUT>
+using Narrow = typename CfgOf<IN, OUT, true, CFG_D256x192x32_S4_I16>::type;
+
+template <int IN>
+static LaunchFn i16_192_out(int out_dt)
+{
+    switch (out_dt) {
+    case DT_F16: return &launch_one<Narrow<IN, DT_F16>>;
+    case DT_BF16: return &launch_one<Narrow<IN, DT_BF16>>;
+    case DT_F32: return &launch_one<Narrow<IN, DT_F32>>;
+    default: return nullptr;
+    }
+}
+
+template <int IN>
+static LaunchFn i16_2r_out(int out_dt)
+{
+    switch (out_dt) {
+    case DT_F16: return &launch_two<Big<IN, DT_F16>, Narrow<IN, DT_F16>>;
+    case DT_BF16: return &launch_two<Big<IN, DT_BF16>, Narrow<IN, DT_BF16>>;
+    case DT_F32: return &launch_two<Big<IN, DT_F32>, Narrow<IN, DT_F32>>;
+    default: return nullptr;
+    }
+}
+
+LaunchFn launcher_i16_192(int in_dt, int out_dt)
+{
+    if (in_dt == DT_F16) return i16_192_out<DT_F16>(out_dt);
+    if (in_dt == DT_BF16) return i16_192_out<DT_BF16>(out_dt);
+    return nullptr;
+}
+
+LaunchFn launcher_i16_2r(int in_dt, int out_dt)
+{
+    if (in_dt == DT_F16) return i16_2r_out<DT_F16>(out_dt);
+    if (in_dt == DT_BF16) return i16_2r_out<DT_BF16>(out_dt);
     return nullptr;
 }
 

@@ -83,7 +83,7 @@ def test_null_operands_allowed_when_K_is_zero():
 @pytest.mark.parametrize("M,N,K,transB,aligned,want", [
     (8192, 8192, 8192, 0, True, "d256x256x32_s4_i16"),
     (4096, 4096, 4096, 0, True, "d256x256x32_s4_i16"),
-    (4096, 7168, 4096, 1, True, "d256x256x32_s4_i16"),
+    (4096, 7168, 4096, 1, True, "d256x256x32_s4_i16+d256x192x32_s4_i16"),
     (256, 256, 256, 0, True, "d64x32x128_s4"),
     (64, 8192, 8192, 0, True, "d32x64x128_s4"),        # skinny: whole-line B rows, twice the workgroups of 64x64
     (32, 16384, 8192, 0, True, "d64x64x64_s4"),        # skinny, but 64x64 tiles fill the CUs
@@ -297,3 +297,31 @@ def test_streamk_selection(monkeypatch):
     assert gr.gemm_relu_plan(A, B, C, 512, 512, 128, 3, 0, 0) == "d256x256x32_s4_isk"
     assert gr.gemm_relu_plan(A, B, C, 512, 512, 64, 3, 0, 0) != "d256x256x32_s4_isk"
     assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 8192, 8192, 8192, 7, 0) == "d256x256x32_s4_i"
+
+
+SPLIT = "d256x256x32_s4_i16+d256x192x32_s4_i16"
+
+
+def test_two_region_grid_selection(monkeypatch):
+    """16-bit inputs with B stored (N,K): when whole rounds of 256x256 tiles
+    leave a partial round, the tile columns past those rounds are cut into
+    256x192 tiles (one launch, one narrower last round).  (K,N) B, whole
+    rounds, 8-bit inputs and forced configurations keep plain tiles;
+    GEMM_RELU_SPLIT_COLS forces or forbids the split."""
+    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == SPLIT
+    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 0, 0, 1) == SPLIT
+    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 0) == "d256x256x32_s4_i16"
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 1) == "d256x256x32_s4_i16"
+    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 3, 0, 1) == "d256x256x32_s4_i"
+    monkeypatch.setenv("GEMM_RELU_SPLIT_COLS", "0")
+    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == "d256x256x32_s4_i16"
+    monkeypatch.setenv("GEMM_RELU_SPLIT_COLS", "1")
+    assert gr.gemm_relu_plan(A, B, C, 512, 520, 64, 0, 0, 1) == SPLIT
+    assert gr.gemm_relu_plan(A, B, C, 512, 256, 64, 0, 0, 1) == "d256x256x32_s4_i16"
+    monkeypatch.delenv("GEMM_RELU_SPLIT_COLS")
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x256x32_s4_i16")
+    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == "d256x256x32_s4_i16"
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x192x32_s4_i16")
+    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == "d256x192x32_s4_i16"
+    # the 256x192 tile is built for B stored (N,K) only
+    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 0) == "d256x256x32_s4_i16"

@@ -20,11 +20,16 @@ from tests.helpers import (built_configs, check_close, from_device, fp32_sum_bou
 
 pytestmark = pytest.mark.gpu
 
+# the two-region grid (256x256 tiles over the first tile columns, 256x192 over
+# the rest), forced here with GEMM_RELU_SPLIT_COLS=1 (one 256-wide column first)
+SPLIT = "d256x256x32_s4_i16+d256x192x32_s4_i16"
+# built for 16-bit inputs with B stored (N,K) only
+NK_ONLY = {"d256x192x32_s4_i16", SPLIT}
 DIRECT = built_configs(["d256x256x64_s2", "d256x256x32_s4", "d256x256x32_s5", "d256x256x32_s4_i",
                         "d256x256x64_s2_16", "d256x256x32_s4_i16", "d256x256x32_s4_ip",
                         "d256x256x32_s4_isk", "d256x256x32_s4_w8i", "d256x256x32_s5_w8i",
                         "d256x256x64_s2_w8", "d128x128x64_s3", "d64x64x64_s4", "d64x32x128_s4",
-                        "d32x64x128_s4"])
+                        "d32x64x128_s4", "d256x192x32_s4_i16", SPLIT])
 STAGED = ["g128x128x64", "g64x64x64"]
 COMBOS = [(i, o) for i in (wl.F16, wl.BF16) for o in (wl.F16, wl.BF16, wl.F32)]
 
@@ -46,7 +51,13 @@ BN_OF = {"d256x256x64_s2": 256, "d256x256x32_s4": 256, "d256x256x32_s5": 256,
 
 def usable(cfg, N, transB, K=None, in_code=wl.F16):
     """Direct-copy configurations need a full tile of columns of a (K,N) B; the
-    stream-K one at least two K steps (32 elements, 64 for 8-bit inputs)."""
+    stream-K one at least two K steps (32 elements, 64 for 8-bit inputs); the
+    256x192 tile and the two-region grid B stored (N,K) (the grid also more
+    than one 256-wide column)."""
+    if cfg in NK_ONLY and not transB:
+        return False
+    if cfg == SPLIT and N <= 256:
+        return False
     if cfg == "d256x256x32_s4_isk" and K is not None:
         step = 64 if in_code in (wl.F8E4M3, wl.F8E5M2) else 32
         if -(-K // step) < 2:
@@ -57,8 +68,11 @@ def usable(cfg, N, transB, K=None, in_code=wl.F16):
 def run(A, B, M, N, K, in_code, out_code, transB, cfg=None, monkeypatch=None, poison=True):
     """Upload, call gemm_relu through the C-ABI, return exact binary64 values."""
     import torch
+    if cfg == SPLIT:
+        monkeypatch.setenv("GEMM_RELU_SPLIT_COLS", "1")
     if cfg is not None:
-        monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", cfg)
+        if cfg != SPLIT:
+            monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", cfg)
         Ad, Bd = to_device(A, in_code, (M, K)), to_device(B, in_code, wl.b_shape(M, N, K, transB))
         Cd = out_tensor(M, N, out_code, float("nan") if poison else 0.0)
         assert gr.gemm_relu_plan(Ad, Bd, Cd, M, N, K, in_code, out_code, transB) == cfg
@@ -88,6 +102,8 @@ def exact_limit(out_code):
 @pytest.mark.parametrize("transB", [0, 1])
 @pytest.mark.parametrize("shape", [(264, 520, 200), (301, 517, 203)], ids=["k8", "ragged"])
 def test_configs_integer_bitexact(cfg, in_code, out_code, transB, shape, monkeypatch):
+    if cfg in NK_ONLY and not transB:
+        pytest.skip("built for B stored (N,K) only")
     # several tiles in every direction plus M, N and K tails (K % BK != 0 in
     # both shapes; the ragged one has odd row lengths, so 2-byte-aligned rows)
     M, N, K = shape
@@ -104,6 +120,8 @@ def test_configs_integer_bitexact(cfg, in_code, out_code, transB, shape, monkeyp
                                               (wl.F16, wl.F32), (wl.BF16, wl.BF16)])
 @pytest.mark.parametrize("transB", [0, 1])
 def test_configs_uniform_tolerance(cfg, in_code, out_code, transB, monkeypatch):
+    if cfg in NK_ONLY and not transB:
+        pytest.skip("built for B stored (N,K) only")
     M, N, K = (331, 263, 461)
     A, B = wl.make_inputs(M, N, K, in_code, transB, "uniform", 200)
     got = run(A, B, M, N, K, in_code, out_code, transB, cfg, monkeypatch)
@@ -121,6 +139,8 @@ def test_configs_uniform_tolerance(cfg, in_code, out_code, transB, monkeypatch):
 def test_coded_mapping(cfg, transB, monkeypatch):
     """A selects one row of B per output row (A[i][pi(i)] = 1), and B's entries
     encode their position, so every output element names its source."""
+    if cfg in NK_ONLY and not transB:
+        pytest.skip("built for B stored (N,K) only")
     M, N, K = (203, 333, 269)
     rng = np.random.default_rng(3)
     pi = rng.permutation(K)[:M]
@@ -251,11 +271,13 @@ def test_tail_sweep_integer(M, N, K, transB):
 @pytest.mark.parametrize("M,N,K", [(1, 8, 8), (65, 72, 136), (33, 200, 520), (300, 16, 64),
                                    (70, 300, 24), (257, 263, 1), (5, 259, 37)])
 def test_tail_shapes_every_config(cfg, M, N, K, monkeypatch):
-    if not usable(cfg, N, 0, K, wl.BF16):
-        pytest.skip("needs a full tile of B columns (stream-K: two K steps)")
-    A, B = int_inputs(M, N, K, wl.BF16, 0, 400 + M, wl.F32)
-    ref = oracle.gemm_relu_ref(A, B, M, N, K, wl.BF16, 0)
-    got = run(A, B, M, N, K, wl.BF16, wl.F32, 0, cfg, monkeypatch)
+    tb = 1 if cfg in NK_ONLY else 0
+    if not usable(cfg, N, tb, K, wl.BF16):
+        pytest.skip("needs a full tile of B columns (stream-K: two K steps; two-region grid: "
+                    "two tile columns)")
+    A, B = int_inputs(M, N, K, wl.BF16, tb, 400 + M, wl.F32)
+    ref = oracle.gemm_relu_ref(A, B, M, N, K, wl.BF16, tb)
+    got = run(A, B, M, N, K, wl.BF16, wl.F32, tb, cfg, monkeypatch)
     assert np.array_equal(got, ref)
 
 
