@@ -455,12 +455,18 @@ def table(gr):
     """One JSON line per workload: median per-call kernel time over 5 trials of
     20 back-to-back calls (HIP events on the launch stream, after at least 10
     and at least TABLE_WARMUP_S seconds of warm-up calls),
-    and a cold-cache time (median of 20 calls, each after a 512 MiB write
+    and a cold-cache time (median of 20 calls, each after a 512 MiB read
     that evicts the 256 MiB MALL and the L2s)."""
     import statistics
     import torch
     stream = torch.cuda.current_stream()
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    # cache eviction for the cold times: a READ of 512 MiB, which leaves the
+    # 256 MiB MALL and the L2s holding clean lines of another buffer.  (Writing
+    # it instead leaves them dirty, and the timed kernel's misses then pay for
+    # their write-back: measured on the skinny 64x8192x8192 workload, 58 us
+    # after a 512 MiB write against 43 us after a 512 MiB read; a plain
+    # 134 MB streaming read, 52 against 26 us.)
+    flush = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     ceilings = {k: mfma_ceiling(gr, stream, kind=k) for k in (0, 1, 2, 3, 4, 5)}
     print(json.dumps({"mfma_ceiling": ceilings[0], "mfma_ceiling_fp8": ceilings[1],
                       "mfma_ceiling_mxfp4": ceilings[2], "mfma_ceiling_mxfp8": ceilings[3],
@@ -493,7 +499,7 @@ def table(gr):
             trials.append(e0.elapsed_time(e1) * 1e3 / 20)
         cold = []
         for i in range(20):
-            flush.fill_(float(i))
+            torch.sum(flush)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
