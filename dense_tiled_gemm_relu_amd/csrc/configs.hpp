@@ -33,6 +33,7 @@ enum ConfigId : int {
     CFG_G128x128x64,
     CFG_G64x64x64,
     CFG_D256x192x32_S4_I16,
+    CFG_D256x256x32_S4_I16P,
     CFG_COUNT
 };
 
@@ -67,13 +68,14 @@ inline const ConfigInfo& config_info(int id)
         {"g128x128x64", 128, 128, false},
         {"g64x64x64", 64, 64, false},
         {"d256x192x32_s4_i16", 256, 192, true},
+        {"d256x256x32_s4_i16p", 256, 256, true, true},
     };
     return table[id];
 }
 
 // Comparison configurations: variants measured against the ones plan selection
 // uses and never chosen by it (other stage counts and step depths, 8-wave
-// tiles, the bunched 16x16-block tile, the persistent tile loop and the
+// tiles, the bunched 16x16-block tile, the persistent tile loops and the
 // stream-K split; for block-scaled inputs the two-stage 256-wide tiles).  They
 // are compiled only when the library is built with
 // GEMM_RELU_COMPARISON_CONFIGS defined; otherwise GEMM_RELU_FORCE_CONFIG
@@ -89,7 +91,8 @@ inline constexpr bool comparison_config(int id)
     return id == CFG_D256x256x64_S2 || id == CFG_D256x256x32_S4 || id == CFG_D256x256x32_S5 ||
            id == CFG_D256x256x64_S2_16 || id == CFG_D256x256x32_S4_IP ||
            id == CFG_D256x256x32_S4_ISK || id == CFG_D256x256x32_S4_W8I ||
-           id == CFG_D256x256x32_S5_W8I || id == CFG_D256x256x64_S2_W8 || id == CFG_D256x128x64_S2;
+           id == CFG_D256x256x32_S5_W8I || id == CFG_D256x256x64_S2_W8 || id == CFG_D256x128x64_S2 ||
+           id == CFG_D256x256x32_S4_I16P;
 }
 
 // Whether this build of the library holds kernels of configuration id.
@@ -140,6 +143,13 @@ template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4
 // then 256 of 256 x 192 instead of 192 more of 256 x 256).
 template <int IN, int OUT> struct CfgOf<IN, OUT, true, CFG_D256x192x32_S4_I16> {
     using type = Cfg<IN, OUT, true, 256, 192, bk_of<IN, 32>, 2, 2, 4, true, true, 16>;
+};
+// The 16x16-block tile as a persistent kernel whose workgroups stream the K
+// steps of their tiles through one ring, fetching each next tile's first
+// steps during the current tile's last ones (16-bit inputs; M, N >= 256, K a
+// multiple of 32 with at least 4 steps).
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I16P> {
+    using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 4, true, true, 16, true>;
 };
 // The 32x32-block interleaved tile as a persistent kernel: at most one workgroup
 // per CU, each looping over its tiles (the Ascend version's T.Persistent).
@@ -240,6 +250,7 @@ LaunchFn launcher_mx_e2m1(int out_dt, int cfg);
 // grid of both (B stored (N,K))
 LaunchFn launcher_i16(int in_dt, int out_dt, bool transB);
 LaunchFn launcher_i16_192(int in_dt, int out_dt);
+LaunchFn launcher_i16p(int in_dt, int out_dt, bool transB);
 LaunchFn launcher_i16_2r(int in_dt, int out_dt);
 
 // Configurations built for 8-bit inputs: the ones plan selection can choose
@@ -275,6 +286,8 @@ inline bool fp8_config(int cfg)
             return launcher_i16(IN, OUT, TB);                                              \
         case CFG_D256x192x32_S4_I16:                                                       \
             return TB ? launcher_i16_192(IN, OUT) : nullptr;                               \
+        case CFG_D256x256x32_S4_I16P:                                                      \
+            return launcher_i16p(IN, OUT, TB);                                             \
         case CFG_D256x256x32_S4_IP:                                                        \
             return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_IP>::type>(); \
         case CFG_D256x256x32_S4_ISK:                                                       \

@@ -39,6 +39,8 @@ struct Env {
     int sk_units = 0;     // GEMM_RELU_SK_UNITS=<n>: stream-K units, 0 = one per CU
     int split_cols = -1;  // GEMM_RELU_SPLIT_COLS=<c>: two-region grid with c 256-wide tile
                           // columns first (0: never split); -1 = plan selection decides
+    int pgrid = 0;        // GEMM_RELU_PERSISTENT_GRID=<n>: workgroups of a persistent
+                          // configuration (0 = one per CU, at most one per tile)
 };
 
 // Debug and tuning switches, read on every call so a process can change them
@@ -61,6 +63,8 @@ Env env()
     if (u && u[0]) e.sk_units = std::max(0, std::atoi(u));
     const char* c = std::getenv("GEMM_RELU_SPLIT_COLS");
     if (c && c[0]) e.split_cols = std::max(0, std::atoi(c));
+    const char* pg = std::getenv("GEMM_RELU_PERSISTENT_GRID");
+    if (pg && pg[0]) e.pgrid = std::max(0, std::atoi(pg));
     return e;
 }
 
@@ -293,6 +297,9 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     auto usable = [&](int id) {
         return id != CFG_D256x128x64_S2 &&             // built for block-scaled inputs only
                (id != CFG_D256x192x32_S4_I16 || transB) &&    // built for B stored (N,K) only
+               // the persistent 16x16-block stream: whole 256x256 tiles inside
+               // the matrix, whole K steps, at least a full ring of them
+               (id != CFG_D256x256x32_S4_I16P || (M >= 256 && N >= 256 && K % 32 == 0 && K >= 128)) &&
                config_built(id) &&
                (id != CFG_D256x256x32_S4_ISK || sk_possible) &&
                direct_fits(id, N, K, transB) && (!fp8_input(in_dt) || fp8_config(id));
@@ -555,7 +562,7 @@ extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64
                               : pick_launcher(in_dtype, out_dtype, transB, p.cfg);
     if (!fn) return GEMM_RELU_EUNSUPPORTED;
     const int tiles = p.tiles_m * p.tiles_n;
-    int grid = config_info(p.cfg).persistent ? std::min(tiles, kNumCUs)
+    int grid = config_info(p.cfg).persistent ? std::min(tiles, e.pgrid > 0 ? e.pgrid : kNumCUs)
                : config_info(p.cfg).streamk  ? p.dp_tiles + p.sk_units
                                              : tiles;
     if (p.cfg2 >= 0) {

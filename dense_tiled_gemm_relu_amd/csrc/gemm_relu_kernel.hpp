@@ -1447,6 +1447,328 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
     }
 }
 
+// ------------------------------------------- persistent 16x16-block tiles
+// The T.Persistent form of page "TileLang：GPU/NPU 通用算子 DSL", §3.3, for the
+// 16x16-block tile: a grid of at most one workgroup per CU, workgroup w taking
+// tiles w, w + G, w + 2G, ... (G = grid, a multiple of the XCD count, so every
+// tile of a workgroup keeps the placement the one-tile-per-workgroup grid
+// gives it).  The K steps of a workgroup's tiles form one stream through the
+// stage ring: during the last S-1 steps of a tile the copies fetch the first
+// S-1 steps of the next tile, and the last step's in-place fragment reloads
+// read the next tile's first step, so the next tile starts without the
+// pipeline's fill latency.  C goes out straight from the accumulators (the
+// ring is busy with the next tile, so it cannot stage C), and the next tile's
+// MFMAs start while those stores drain.
+//
+// Every tile lies inside the matrix: the last tile row and column are moved
+// back to end at M and N, and each moved-back tile stores only the rows and
+// columns its neighbours do not own, so every element of C has one writer and
+// no copy is clamped.  Needs M, N >= 256 and K a multiple of 32 with at least
+// S steps (plan selection checks).
+template <class C>
+__device__ __forceinline__ void gemm_relu_i16_persistent(const KernelArgs& args,
+                                                         GR_LDS unsigned char* smem)
+{
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::STAGES;
+    constexpr int TM = C::TM, TN = C::TN;
+    constexpr int APT = C::A_PER_THREAD, BPT = C::B_PER_THREAD, LOADS = C::LOADS_PER_STAGE;
+    constexpr int ROW_CH = C::ROW_CH, NROW_CH = C::NROW_CH;
+    constexpr int EB = C::EB, FRAG_CH = C::FRAG_CH, TR_READS = C::TR_READS;
+    constexpr int MB = 16, NG = 4;
+    using In = typename C::In;
+    using Op = typename In::Op;
+    using Acc = typename In::Acc;
+    static_assert(C::MB == 16 && !C::MX && C::DIRECT && C::INTERLEAVE && C::KSUB == 1 && TM == 8 &&
+                      TN % 2 == 0 && TN <= 8 && LOADS <= 8 && !C::STREAMK,
+                  "persistent 16x16-block tile: 8 x TN blocks, one copy per region");
+
+    const int M = args.M, N = args.N, K = args.K;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nk = K / BK;
+    const int total = args.tiles_m * args.tiles_n;
+    const int G = gridDim.x;
+    int tile = blockIdx.x;
+    if (tile >= total) return;
+
+    // ---- copy geometry, the same for every tile (no clamped rows): slot q of
+    // a k-contiguous region holds row q / ROW_CH, chunk (q % ROW_CH) ^ swz;
+    // slot q of an n-contiguous B region holds k row q / NROW_CH.  Copy i of a
+    // lane covers the rows of copy 0 shifted by i passes; the swizzles repeat
+    // every 16 rows, so one per-lane offset (two for an n-contiguous B, whose
+    // passes are 8 rows) and a scalar shift per copy locate every chunk, which
+    // keeps the vector registers for the accumulators and fragments.
+    constexpr int RPP = C::NTHREADS / ROW_CH;       // k-contiguous rows per copy pass
+    constexpr int KPP = C::NTHREADS / NROW_CH;      // n-contiguous B rows per copy pass
+    constexpr int NPAT = C::TRANS_B || KPP >= 16 ? 1 : 16 / KPP;
+    static_assert(RPP % 16 == 0 && (C::TRANS_B || KPP % 16 == 0 || 16 % KPP == 0) && BPT % NPAT == 0,
+                  "copy passes align with the 16-row swizzle period");
+    auto krow_off = [&](int q) {
+        const int r = q / ROW_CH;
+        return (uint32_t)r * (uint32_t)K * (uint32_t)EB + (uint32_t)(((q % ROW_CH) ^ swz_krow<ROW_CH>(r)) * 16);
+    };
+    const uint32_t a_off = krow_off(tid);
+    uint32_t b_off[NPAT];
+#pragma unroll
+    for (int i = 0; i < NPAT; ++i) {
+        const int q = i * C::NTHREADS + tid;
+        if constexpr (C::TRANS_B) {
+            b_off[i] = krow_off(q);
+        } else {
+            const int k = q / NROW_CH;
+            b_off[i] = (uint32_t)k * (uint32_t)N * (uint32_t)EB +
+                       (uint32_t)(((q % NROW_CH) ^ swz_nrow<NROW_CH, In::TRK, MB>(k)) * 16);
+        }
+    }
+    const uint32_t smem_addr = lds_addr(smem);
+    // the tile's origin inside the matrix and the first row / column it owns
+    // (workgroup-uniform: kept in scalar registers, which the vector register
+    // file, full with accumulators and fragments, cannot spare)
+    auto origin = [&](int t, int& m0, int& n0, int& m_own, int& n_own) {
+        int tm, tn;
+        tile_coords(t, args.tiles_m, args.tiles_n, args.panel, args.nxcd, tm, tn);
+        m_own = __builtin_amdgcn_readfirstlane(tm * BM);
+        n_own = __builtin_amdgcn_readfirstlane(tn * BN);
+        m0 = __builtin_amdgcn_readfirstlane(min(m_own, M - BM));
+        n0 = __builtin_amdgcn_readfirstlane(min(n_own, N - BN));
+    };
+    auto a_base = [&](int m0) { return args.A + (size_t)m0 * (size_t)K * EB; };
+    auto b_base = [&](int n0) {
+        return C::TRANS_B ? args.B + (size_t)n0 * (size_t)K * EB : args.B + (size_t)n0 * EB;
+    };
+    // copy r (< LOADS) of K step u of the tile whose operands start at ga0, gb0,
+    // into ring stage st
+    auto copy_one = [&](const unsigned char* ga0, const unsigned char* gb0, int u, int st, int r) {
+        const uint32_t sa = smem_addr + st * C::STAGE_BYTES;
+        if (r < APT) {
+            dma16(ga0 + (size_t)u * BK * EB + (size_t)(r * RPP) * K * EB, a_off,
+                  sa + (r * C::NWAVES + wave) * 1024);
+        } else {
+            const int i = r - APT;
+            const unsigned char* gb =
+                C::TRANS_B ? gb0 + (size_t)u * BK * EB + (size_t)(i * RPP) * K * EB
+                           : gb0 + ((size_t)u * BK + (size_t)((i - i % NPAT) * KPP)) * (size_t)N * EB;
+            dma16(gb, b_off[i % NPAT], sa + C::A_BYTES + (i * C::NWAVES + wave) * 1024);
+        }
+    };
+
+    // ---- fragment reads (per lane, relative to a stage's A / B region)
+    const int wave_m = wave / C::WAVES_N, wave_n = wave % C::WAVES_N;
+    const int wm0 = wave_m * C::WM, wn0 = wave_n * C::WN;
+    const int lr = lane % MB, g = lane / MB;
+    uint32_t a_rd[FRAG_CH];
+#pragma unroll
+    for (int x = 0; x < FRAG_CH; ++x) {
+        const int r = wm0 + lr;
+        a_rd[x] = (uint32_t)(r * BK * EB + (((g * FRAG_CH + x) ^ swz_krow<ROW_CH>(r)) * 16));
+    }
+    constexpr int B_RD_T = C::TRANS_B ? FRAG_CH : TR_READS;
+    uint32_t b_rd[C::TRANS_B ? 1 : TN][B_RD_T];
+    if constexpr (C::TRANS_B) {
+#pragma unroll
+        for (int x = 0; x < FRAG_CH; ++x) {
+            const int r = wn0 + lr;
+            b_rd[0][x] = (uint32_t)(r * BK * EB + (((g * FRAG_CH + x) ^ swz_krow<ROW_CH>(r)) * 16));
+        }
+    } else {
+        // transpose reads: 16-lane group h = k group; lane i16 supplies k row
+        // 8 h + i16 / LPR (+ TRK t) and the 8 bytes of columns (i16 % LPR) 4 ..
+        constexpr int TRK = In::TRK, LPR = 16 / TRK;
+        const int h = lane >> 4, i16 = lane & 15;
+        const int kk = (In::KMF / NG) * h + i16 / LPR;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int t = 0; t < B_RD_T; ++t) {
+                const int n = wn0 + MB * j + (i16 % LPR) * (8 / EB);
+                const int k = kk + t * TRK;
+                const int phys = ((n * EB) >> 4) ^ swz_nrow<NROW_CH, TRK, MB>(k);
+                b_rd[j][t] = (uint32_t)(k * BN * EB + phys * 16 + ((n * EB) & 15));
+            }
+    }
+    struct Frags {
+        Op a[TM], b[TN];
+    };
+    Frags fr;
+    constexpr int QA = TM * FRAG_CH;
+    constexpr int QB = C::TRANS_B ? FRAG_CH : TR_READS;     // reads per B block
+    // read op q of the step held in ring stage st: A block q / FRAG_CH, then
+    // B block (q - QA) / QB
+    auto read_op = [&](int st, int q) {
+        const GR_LDS unsigned char* sa = smem + st * C::STAGE_BYTES;
+        const GR_LDS unsigned char* sb = sa + C::A_BYTES;
+        if (q < QA) {
+            const int i = q / FRAG_CH, x = q % FRAG_CH;
+            const u32x4_t v = lds_read_b128(sa + a_rd[x] + i * MB * BK * EB);
+            if (x == 0)
+                In::template set_chunk<0>(fr.a[i], v);
+            else
+                In::template set_chunk<1>(fr.a[i], v);
+        } else if constexpr (C::TRANS_B) {
+            const int j = (q - QA) / FRAG_CH, x = (q - QA) % FRAG_CH;
+            const u32x4_t v = lds_read_b128(sb + b_rd[0][x] + j * MB * BK * EB);
+            if (x == 0)
+                In::template set_chunk<0>(fr.b[j], v);
+            else
+                In::template set_chunk<1>(fr.b[j], v);
+        } else {
+            const int j = (q - QA) / TR_READS, t = (q - QA) % TR_READS;
+            In::set_tr(fr.b[j], t, sb + b_rd[j][t]);
+        }
+    };
+
+    Acc acc[TM][TN];
+    auto clear_acc = [&] {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < In::NACC; ++r) acc[i][j][r] = 0.0f;
+    };
+
+    // One K step: the MFMAs of the fragments in fr, with COPIES copies (of K
+    // step u of the tile at ga0, gb0, into stage ld_st) and, with READS, each
+    // fragment reloaded in place from stage rd_st after its last use (eight
+    // regions: A rows in pairs against B blocks 0 .. TN/2-1, then against the
+    // rest; B blocks after each half, A rows after their region of the second).
+    constexpr int HB = TN / 2;
+    auto step = [&](const unsigned char* ga0, const unsigned char* gb0, int u, int ld_st, int rd_st) {
+        static_for<0, 8>([&](auto r_tag) {
+            constexpr int r = decltype(r_tag)::value;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (r < LOADS) copy_one(ga0, gb0, u, ld_st, r);
+            constexpr int half = r / 4, i0 = 2 * (r % 4);
+#pragma unroll
+            for (int di = 0; di < 2; ++di)
+#pragma unroll
+                for (int jj = 0; jj < HB; ++jj) {
+                    const int i = i0 + di;
+                    const int j = HB * half + (di ? HB - 1 - jj : jj);
+                    acc[i][j] = In::mfma(fr.b[j], fr.a[i], acc[i][j]);
+                }
+            if constexpr (r == 3 || r == 7) {
+#pragma unroll
+                for (int q = QA + HB * half * QB; q < QA + (HB * half + HB) * QB; ++q) read_op(rd_st, q);
+            }
+            if constexpr (r >= 4) {
+#pragma unroll
+                for (int q = i0 * FRAG_CH; q < (i0 + 2) * FRAG_CH; ++q) read_op(rd_st, q);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    // Wait at the top of a step: this wave's copies of the next step have
+    // landed (one step's LOADS copies were issued after them; any C stores
+    // issued since are waited for as well), then every wave's have, and every
+    // wave is past its reads of the stage this step's copies refill (those
+    // reads fed the MFMAs of the step before).
+    auto top = [&] {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS));
+        asm volatile("s_barrier" ::: "memory");
+    };
+
+    // ---- epilogue: ReLU, convert, store from the accumulators.  Lane owns
+    // C[m][n .. n+3], m = m0 + wm0 + 16 i + lr, n = n0 + wn0 + 16 j + 4 g.
+    constexpr int OB = OutTraits<C::OUT_DT>::bytes;
+    auto store_tile = [&](int m0, int n0, int m_own, int n_own) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = m0 + wm0 + MB * i + lr;
+            if (m < m_own) continue;
+            unsigned char* crow = args.C + (size_t)m * (size_t)N * OB;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int n = n0 + wn0 + MB * j + 4 * g;
+                if (n + 4 <= n_own) continue;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = relu(acc[i][j][e]);
+                if constexpr (C::OUT_DT == DT_F32) {
+                    float* dst = reinterpret_cast<float*>(crow) + n;
+                    if (n >= n_own) {
+                        const u32x4_t w = {__builtin_bit_cast(unsigned, v[0]), __builtin_bit_cast(unsigned, v[1]),
+                                           __builtin_bit_cast(unsigned, v[2]), __builtin_bit_cast(unsigned, v[3])};
+                        __builtin_memcpy(dst, &w, 16);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e >= n_own) dst[e] = v[e];
+                    }
+                } else {
+                    unsigned short hv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) hv[e] = OutTraits<C::OUT_DT>::cvt(v[e]);
+                    unsigned short* dst = reinterpret_cast<unsigned short*>(crow) + n;
+                    if (n >= n_own) {
+                        const u32x2_t w = {hv[0] | ((unsigned)hv[1] << 16), hv[2] | ((unsigned)hv[3] << 16)};
+                        __builtin_memcpy(dst, &w, 8);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e >= n_own) dst[e] = hv[e];
+                    }
+                }
+            }
+        }
+    };
+
+    // ---- the stream: prologue of the first tile
+    int m0, n0, m_own, n_own;
+    origin(tile, m0, n0, m_own, n_own);
+    const unsigned char* ga0 = a_base(m0);
+    const unsigned char* gb0 = b_base(n0);
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+#pragma unroll
+        for (int r = 0; r < LOADS; ++r) copy_one(ga0, gb0, st, st, r);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((S - 2) * LOADS));
+    asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < C::NR; ++q) read_op(0, q);
+
+    uint32_t gbase = 0;     // stream position of the tile's first K step
+    for (;;) {
+        const int next = tile + G;
+        const bool has_next = next < total;
+        // After the workgroup's last tile the stream runs on into a copy of
+        // that tile's first steps, which nobody reads: one schedule for every
+        // tile (a separate ending made the register allocator spill).
+        int m1 = m0, n1 = n0, m1_own = m_own, n1_own = n_own;
+        if (has_next) origin(next, m1, n1, m1_own, n1_own);
+        const unsigned char* ga1 = a_base(m1);
+        const unsigned char* gb1 = b_base(n1);
+        clear_acc();
+        // steps whose copies fetch this tile's own steps
+        int t = 0;
+        for (; t < nk - (S - 1); ++t) {
+            top();
+            step(ga0, gb0, t + S - 1, (gbase + t + S - 1) % S, (gbase + t + 1) % S);
+        }
+        // the last S-1 steps fetch the next tile's first S-1 steps, and the
+        // last one reloads the fragments of the next tile's first step
+        for (; t < nk; ++t) {
+            top();
+            step(ga1, gb1, t + S - 1 - nk, (gbase + t + S - 1) % S, (gbase + t + 1) % S);
+        }
+        store_tile(m0, n0, m_own, n_own);
+        if (!has_next) {
+            // no copy may still be writing LDS when the workgroup retires
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            break;
+        }
+        tile = next;
+        m0 = m1;
+        n0 = n1;
+        m_own = m1_own;
+        n_own = n1_own;
+        ga0 = ga1;
+        gb0 = gb1;
+        gbase += nk;
+    }
+}
+
 // One workgroup per tile, or (persistent configurations, the T.Persistent form
 // of page "TileLang：GPU/NPU 通用算子 DSL", §3.3) a grid of at most one
 // workgroup per CU whose workgroups walk the tiles wg, wg + grid, ...: the
@@ -1526,6 +1848,8 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
             gemm_relu_tile<C>(args, sk->wg, smem, sk, Region{args.tiles_m, args.tiles_n, args.panel, 0});
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         }
+    } else if constexpr (C::PERSISTENT && C::MB == 16) {
+        gemm_relu_i16_persistent<C>(args, smem);
     } else if constexpr (C::PERSISTENT) {
         const int total = args.tiles_m * args.tiles_n;
         for (int wg = blockIdx.x; wg < total; wg += gridDim.x) {

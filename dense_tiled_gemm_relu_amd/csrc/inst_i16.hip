@@ -52,6 +52,24 @@ static LaunchFn i16_2r_out(int out_dt)
     }
 }
 
+template <int IN, bool TB>
+static LaunchFn i16p_out(int out_dt)
+{
+    switch (out_dt) {
+    case DT_F16: return comparison_launcher<typename CfgOf<IN, DT_F16, TB, CFG_D256x256x32_S4_I16P>::type>();
+    case DT_BF16: return comparison_launcher<typename CfgOf<IN, DT_BF16, TB, CFG_D256x256x32_S4_I16P>::type>();
+    case DT_F32: return comparison_launcher<typename CfgOf<IN, DT_F32, TB, CFG_D256x256x32_S4_I16P>::type>();
+    default: return nullptr;
+    }
+}
+
+LaunchFn launcher_i16p(int in_dt, int out_dt, bool transB)
+{
+    if (in_dt == DT_F16) return transB ? i16p_out<DT_F16, true>(out_dt) : i16p_out<DT_F16, false>(out_dt);
+    if (in_dt == DT_BF16) return transB ? i16p_out<DT_BF16, true>(out_dt) : i16p_out<DT_BF16, false>(out_dt);
+    return nullptr;
+}
+
 LaunchFn launcher_i16_192(int in_dt, int out_dt)
 {
     if (in_dt == DT_F16) return i16_192_out<DT_F16>(out_dt);

@@ -25,11 +25,14 @@ pytestmark = pytest.mark.gpu
 SPLIT = "d256x256x32_s4_i16+d256x192x32_s4_i16"
 # built for 16-bit inputs with B stored (N,K) only
 NK_ONLY = {"d256x192x32_s4_i16", SPLIT}
+# the persistent 16x16-block stream: whole 256x256 tiles (M, N >= 256), K a
+# multiple of 32 with at least 4 steps
+PSTREAM = "d256x256x32_s4_i16p"
 DIRECT = built_configs(["d256x256x64_s2", "d256x256x32_s4", "d256x256x32_s5", "d256x256x32_s4_i",
                         "d256x256x64_s2_16", "d256x256x32_s4_i16", "d256x256x32_s4_ip",
                         "d256x256x32_s4_isk", "d256x256x32_s4_w8i", "d256x256x32_s5_w8i",
                         "d256x256x64_s2_w8", "d128x128x64_s3", "d64x64x64_s4", "d64x32x128_s4",
-                        "d32x64x128_s4", "d256x192x32_s4_i16", SPLIT])
+                        "d32x64x128_s4", "d256x192x32_s4_i16", SPLIT, PSTREAM])
 STAGED = ["g128x128x64", "g64x64x64"]
 COMBOS = [(i, o) for i in (wl.F16, wl.BF16) for o in (wl.F16, wl.BF16, wl.F32)]
 
@@ -57,6 +60,8 @@ def usable(cfg, N, transB, K=None, in_code=wl.F16):
     if cfg in NK_ONLY and not transB:
         return False
     if cfg == SPLIT and N <= 256:
+        return False
+    if cfg == PSTREAM and (N < 256 or K is None or K % 32 or K < 128):
         return False
     if cfg == "d256x256x32_s4_isk" and K is not None:
         step = 64 if in_code in (wl.F8E4M3, wl.F8E5M2) else 32
@@ -104,6 +109,8 @@ def exact_limit(out_code):
 def test_configs_integer_bitexact(cfg, in_code, out_code, transB, shape, monkeypatch):
     if cfg in NK_ONLY and not transB:
         pytest.skip("built for B stored (N,K) only")
+    if cfg == PSTREAM:
+        pytest.skip("the persistent stream needs K a multiple of 32 (its own tests below)")
     # several tiles in every direction plus M, N and K tails (K % BK != 0 in
     # both shapes; the ragged one has odd row lengths, so 2-byte-aligned rows)
     M, N, K = shape
@@ -122,6 +129,8 @@ def test_configs_integer_bitexact(cfg, in_code, out_code, transB, shape, monkeyp
 def test_configs_uniform_tolerance(cfg, in_code, out_code, transB, monkeypatch):
     if cfg in NK_ONLY and not transB:
         pytest.skip("built for B stored (N,K) only")
+    if cfg == PSTREAM:
+        pytest.skip("the persistent stream needs K a multiple of 32 (its own tests below)")
     M, N, K = (331, 263, 461)
     A, B = wl.make_inputs(M, N, K, in_code, transB, "uniform", 200)
     got = run(A, B, M, N, K, in_code, out_code, transB, cfg, monkeypatch)
@@ -141,6 +150,8 @@ def test_coded_mapping(cfg, transB, monkeypatch):
     encode their position, so every output element names its source."""
     if cfg in NK_ONLY and not transB:
         pytest.skip("built for B stored (N,K) only")
+    if cfg == PSTREAM:
+        pytest.skip("the persistent stream needs K a multiple of 32 (its own tests below)")
     M, N, K = (203, 333, 269)
     rng = np.random.default_rng(3)
     pi = rng.permutation(K)[:M]
@@ -153,6 +164,89 @@ def test_coded_mapping(cfg, transB, monkeypatch):
     A, B = wl.encode(a, wl.F16), wl.encode(b, wl.F16)
     got = run(A, B, M, N, K, wl.F16, wl.F16, transB, cfg, monkeypatch)
     assert np.array_equal(got, np.maximum(bkn[pi, :], 0.0))
+
+
+# ------------------------------------------- the persistent 16x16 stream
+# Each workgroup runs the K steps of several tiles as one stream through the
+# stage ring (the next tile's first steps fetched during the current tile's
+# last ones); GEMM_RELU_PERSISTENT_GRID makes small problems give every
+# workgroup several tiles.  Shapes: one tile, whole tiles, moved-back last
+# tile row and column (M, N not multiples of 256), K of exactly one ring (4
+# steps) and long K.
+PSTREAM_SHAPES = [(256, 256, 128), (512, 768, 256), (777, 530, 160), (520, 1000, 1024), (300, 260, 4096)]
+need_pstream = pytest.mark.skipif(not built_configs([PSTREAM]),
+                                  reason="the persistent stream is a comparison configuration, not in this build")
+
+
+@need_pstream
+@pytest.mark.parametrize("M,N,K", PSTREAM_SHAPES)
+@pytest.mark.parametrize("grid", [1, 3, 8, 0])
+@pytest.mark.parametrize("transB", [0, 1])
+def test_persistent_stream_integer_bitexact(M, N, K, grid, transB, monkeypatch):
+    monkeypatch.setenv("GEMM_RELU_PERSISTENT_GRID", str(grid))
+    for in_code, out_code in ((wl.F16, wl.F16), (wl.BF16, wl.F32), (wl.F16, wl.BF16)):
+        A, B = int_inputs(M, N, K, in_code, transB, 1100 + M + K + grid, out_code)
+        ref = oracle.gemm_relu_ref(A, B, M, N, K, in_code, transB)
+        assert np.abs(ref).max() < exact_limit(out_code)
+        got = run(A, B, M, N, K, in_code, out_code, transB, PSTREAM, monkeypatch)
+        assert np.array_equal(got, ref)
+        assert not np.any(np.signbit(got))
+
+
+@need_pstream
+@pytest.mark.parametrize("transB", [0, 1])
+def test_persistent_stream_coded_mapping(transB, monkeypatch):
+    """Every output names its source row and column (as test_coded_mapping),
+    with three tiles per workgroup and moved-back edge tiles."""
+    monkeypatch.setenv("GEMM_RELU_PERSISTENT_GRID", "2")
+    M, N, K = (523, 777, 288)
+    rng = np.random.default_rng(5)
+    pi = rng.permutation(K)[:M] if M <= K else rng.integers(0, K, M)
+    a = np.zeros((M, K))
+    a[np.arange(M), pi] = 1.0
+    k = np.arange(K)[:, None]
+    j = np.arange(N)[None, :]
+    bkn = ((131 * k + 7 * j) % 5 - 2).astype(np.float64)
+    b = bkn.T if transB else bkn
+    A, B = wl.encode(a, wl.F16), wl.encode(b, wl.F16)
+    got = run(A, B, M, N, K, wl.F16, wl.F16, transB, PSTREAM, monkeypatch)
+    assert np.array_equal(got, np.maximum(bkn[pi, :], 0.0))
+
+
+@need_pstream
+@pytest.mark.parametrize("in_code,out_code", [(wl.F16, wl.F16), (wl.BF16, wl.F32)])
+@pytest.mark.parametrize("transB", [0, 1])
+def test_persistent_stream_uniform_tolerance(in_code, out_code, transB, monkeypatch):
+    monkeypatch.setenv("GEMM_RELU_PERSISTENT_GRID", "4")
+    M, N, K = (600, 700, 480)
+    A, B = wl.make_inputs(M, N, K, in_code, transB, "uniform", 1200)
+    got = run(A, B, M, N, K, in_code, out_code, transB, PSTREAM, monkeypatch)
+    ref = oracle.gemm_relu_ref(A, B, M, N, K, in_code, transB)
+    check_close(got, ref, K, out_code)
+    absum = oracle.gemm_absum_matmul(A, B, M, N, K, in_code, transB)
+    assert np.all(np.abs(got - ref) <= fp32_sum_bound(absum, ref, K, unit_roundoff(out_code)))
+
+
+@need_pstream
+def test_persistent_stream_repeats_and_guards(monkeypatch):
+    """Bit-identical results over calls and grid sizes; C's guard bands untouched."""
+    import torch
+    M, N, K = (777, 530, 320)
+    A, B = wl.make_inputs(M, N, K, wl.F16, 0, "uniform", 1300)
+    outs = []
+    for grid in (1, 5, 0, 0):
+        monkeypatch.setenv("GEMM_RELU_PERSISTENT_GRID", str(grid))
+        monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", PSTREAM)
+        Ad, Bd = to_device(A, wl.F16, (M, K)), to_device(B, wl.F16, (K, N))
+        buf = torch.full((M * N + 2048,), 7.0, dtype=torch.float16, device="cuda")
+        C = buf[1024:1024 + M * N].view(M, N)
+        assert gr.gemm_relu_plan(Ad, Bd, C, M, N, K, wl.F16, wl.F16, 0) == PSTREAM
+        gr.gemm_relu(Ad, Bd, C, M, N, K, wl.F16, wl.F16, 0)
+        torch.cuda.synchronize()
+        assert torch.all(buf[:1024] == 7.0) and torch.all(buf[1024 + M * N:] == 7.0)
+        outs.append(C.clone())
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
 
 
 # ----------------------------------------------------------- 8-bit inputs
@@ -272,6 +366,8 @@ def test_tail_sweep_integer(M, N, K, transB):
                                    (70, 300, 24), (257, 263, 1), (5, 259, 37)])
 def test_tail_shapes_every_config(cfg, M, N, K, monkeypatch):
     tb = 1 if cfg in NK_ONLY else 0
+    if cfg == PSTREAM:
+        pytest.skip("the persistent stream needs M, N >= 256 (its own tests below)")
     if not usable(cfg, N, tb, K, wl.BF16):
         pytest.skip("needs a full tile of B columns (stream-K: two K steps; two-region grid: "
                     "two tile columns)")
