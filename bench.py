@@ -340,10 +340,11 @@ def ceiling_kind(in_dtype, sparse=False, plan=None):
     return 1 if in_dtype in wl.FP8 else 0
 
 
-def workload_call(gr, name, stream):
+def workload_call(gr, name, stream, workspace=False):
     """(call, C tensor, tile config, algorithmic bytes) for one workload, its
-    inputs uploaded: plain ones through gemm_relu, block-scaled ones through
-    gemm_relu_mx."""
+    inputs uploaded: plain ones through gemm_relu (through gemm_relu_ws with a
+    zeroed workspace of gemm_relu_workspace_size bytes when `workspace`),
+    block-scaled ones through gemm_relu_mx."""
     import torch
     w = wl.WORKLOADS[name]
     M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
@@ -371,11 +372,19 @@ def workload_call(gr, name, stream):
     A, B = wl.workload_inputs(name)
     Ad = to_device(A, ic, (M, K))
     Bd = to_device(B, ic, wl.b_shape(M, N, K, tb))
+    nbytes = wl.elem_bytes(ic) * (M * K + K * N) + M * N * wl.elem_bytes(oc)
+    if workspace:
+        need = gr.gemm_relu_workspace_size(M, N, K, ic, oc, tb)
+        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+
+        def call():
+            gr.gemm_relu_ws(Ad, Bd, Cd, M, N, K, ic, oc, tb, ws, need, stream)
+        plan = gr.gemm_relu_ws_plan(Ad, Bd, Cd, M, N, K, ic, oc, tb, ws, need)
+        return call, Cd, plan, nbytes, (Ad, Bd, ws)
 
     def call():
         gr.gemm_relu(Ad, Bd, Cd, M, N, K, ic, oc, tb, stream)
     plan = gr.gemm_relu_plan(Ad, Bd, Cd, M, N, K, ic, oc, tb)
-    nbytes = wl.elem_bytes(ic) * (M * K + K * N) + M * N * wl.elem_bytes(oc)
     return call, Cd, plan, nbytes, (Ad, Bd)
 
 
@@ -455,8 +464,13 @@ def table(gr):
     """One JSON line per workload: median per-call kernel time over 5 trials of
     20 back-to-back calls (HIP events on the launch stream, after at least 10
     and at least TABLE_WARMUP_S seconds of warm-up calls),
-    and a cold-cache time (median of 20 calls, each after a 512 MiB read
-    that evicts the 256 MiB MALL and the L2s)."""
+    and a cold-cache time (each sample after a 512 MiB read that evicts the
+    256 MiB MALL and the L2s).  A kernel that follows an event record starts
+    some microseconds later than one that follows another kernel, so the cold
+    time is a difference: events around [a one-block fill kernel, the call]
+    less events around the fill kernel alone, medians of 20 samples each (the
+    single-call event time is reported beside it).  Plain workloads for which
+    gemm_relu_ws splits K get a second line, timed through it."""
     import statistics
     import torch
     stream = torch.cuda.current_stream()
@@ -472,10 +486,31 @@ def table(gr):
                       "mfma_ceiling_mxfp4": ceilings[2], "mfma_ceiling_mxfp8": ceilings[3],
                       "mfma_ceiling_sparse_f16": ceilings[4], "mfma_ceiling_f16_16x16": ceilings[5]}),
           flush=True)
+    tiny = torch.zeros(64, dtype=torch.float32, device="cuda")
+
+    def cold_sample(fn):
+        torch.sum(flush)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        tiny.fill_(1.0)
+        if fn is not None:
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    runs = []
     for name in sorted(wl.WORKLOADS, key=lambda n: wl.WORKLOADS[n]["index"]):
         w = wl.WORKLOADS[name]
+        runs.append((name, False))
+        if not w.get("mx") and not w.get("sparse") and gr.gemm_relu_workspace_size(
+                w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]) > 0:
+            runs.append((name, True))
+    for name, with_ws in runs:
+        w = wl.WORKLOADS[name]
         M, N, K, ic, oc, tb = w["M"], w["N"], w["K"], w["in_dtype"], w["out_dtype"], w["transB"]
-        call, Cd, plan, nbytes, keep = workload_call(gr, name, stream)
+        call, Cd, plan, nbytes, keep = workload_call(gr, name, stream, workspace=with_ws)
         ceiling = ceilings[ceiling_kind(ic, w.get("sparse", False), plan)]
         peak = peak_tflops(ic, w.get("sparse", False))
 
@@ -497,8 +532,10 @@ def table(gr):
             e1.record(stream)
             torch.cuda.synchronize()
             trials.append(e0.elapsed_time(e1) * 1e3 / 20)
-        cold = []
+        with_call, fill_only, raw = [], [], []
         for i in range(20):
+            with_call.append(cold_sample(call))
+            fill_only.append(cold_sample(None))
             torch.sum(flush)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -506,13 +543,14 @@ def table(gr):
             call()
             e1.record(stream)
             torch.cuda.synchronize()
-            cold.append(e0.elapsed_time(e1) * 1e3)
+            raw.append(e0.elapsed_time(e1) * 1e3)
         t = statistics.median(trials)
-        tc = statistics.median(cold)
+        tc = statistics.median(with_call) - statistics.median(fill_only)
         flops = 2.0 * M * N * K
         print(json.dumps({
             "workload": name, "M": M, "N": N, "K": K, "in": wl.DTYPE_NAMES[ic],
             "out": wl.DTYPE_NAMES[oc], "transB": tb,
+            "entry": "gemm_relu_ws" if with_ws else "gemm_relu",
             "tile_config": plan,
             "t_median_us": round(t, 2), "t_trials_us": [round(x, 2) for x in trials],
             "tflops": round(flops / t / 1e6, 1),
@@ -521,7 +559,9 @@ def table(gr):
                                     if ceiling else None),
             "algorithmic_GBps": round(nbytes / t / 1e3, 1),
             "pct_hbm": round(100 * nbytes / t / 1e3 / HBM_GBPS, 2),
-            "t_cold_median_us": round(tc, 2), "tflops_cold": round(flops / tc / 1e6, 1)}),
+            "t_cold_median_us": round(tc, 2), "tflops_cold": round(flops / tc / 1e6, 1),
+            "cold_GBps": round(nbytes / tc / 1e3, 1), "pct_hbm_cold": round(100 * nbytes / tc / 1e3 / HBM_GBPS, 2),
+            "t_cold_single_event_us": round(statistics.median(raw), 2)}),
             flush=True)
         del keep, Cd
 

@@ -31,6 +31,7 @@ LIB_PATH = os.path.join(_PKG, "libgemm_relu.so")
 PROBE_LIB_PATH = os.path.join(_PKG, "libgemm_relu_probe.so")
 
 EXPORTS = ("gemm_relu", "gemm_relu_strerror", "gemm_relu_configs", "gemm_relu_plan",
+           "gemm_relu_ws", "gemm_relu_workspace_size", "gemm_relu_ws_plan",
            "gemm_relu_mx", "gemm_relu_mx_plan", "gemm_relu_sp", "gemm_relu_sp_plan")
 
 _lib = None
@@ -66,6 +67,15 @@ def library():
     lib.gemm_relu_plan.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int]
     lib.gemm_relu_plan.restype = ctypes.c_char_p
+    u64 = ctypes.c_uint64
+    lib.gemm_relu_ws.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, vp, u64, vp]
+    lib.gemm_relu_ws.restype = ctypes.c_int
+    lib.gemm_relu_workspace_size.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.gemm_relu_workspace_size.restype = i64
+    lib.gemm_relu_ws_plan.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, vp, u64]
+    lib.gemm_relu_ws_plan.restype = ctypes.c_char_p
     lib.gemm_relu_mx.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp]
     lib.gemm_relu_mx.restype = ctypes.c_int
     lib.gemm_relu_mx_plan.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.c_int,
@@ -130,6 +140,39 @@ def gemm_relu_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB):
     """Configuration name gemm_relu would launch (None if the call is invalid)."""
     r = library().gemm_relu_plan(_addr(A), _addr(B), _addr(C), int(M), int(N), int(K),
                                  int(in_dtype), int(out_dtype), int(transB))
+    return None if r is None else r.decode()
+
+
+def gemm_relu_ws_status(A, B, C, M, N, K, in_dtype, out_dtype, transB, workspace, workspace_bytes,
+                        stream=None):
+    """Call the workspace C-ABI entry and return its status code (no exception)."""
+    return library().gemm_relu_ws(_addr(A), _addr(B), _addr(C), int(M), int(N), int(K),
+                                  int(in_dtype), int(out_dtype), int(transB), _addr(workspace),
+                                  int(workspace_bytes), _stream_handle(stream))
+
+
+def gemm_relu_ws(A, B, C, M, N, K, in_dtype, out_dtype, transB, workspace, workspace_bytes,
+                 stream=None):
+    """gemm_relu with a caller's device workspace (a tensor or raw address and
+    its size in bytes); raises GemmReluError on failure."""
+    rc = gemm_relu_ws_status(A, B, C, M, N, K, in_dtype, out_dtype, transB, workspace,
+                             workspace_bytes, stream)
+    if rc != OK:
+        raise GemmReluError(rc, gemm_relu_strerror(rc))
+
+
+def gemm_relu_workspace_size(M, N, K, in_dtype, out_dtype, transB):
+    """Workspace bytes gemm_relu_ws would use (0: no K split); negative status
+    for invalid arguments."""
+    return int(library().gemm_relu_workspace_size(int(M), int(N), int(K), int(in_dtype),
+                                                  int(out_dtype), int(transB)))
+
+
+def gemm_relu_ws_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB, workspace, workspace_bytes):
+    """Configuration name gemm_relu_ws would launch (None if the call is invalid)."""
+    r = library().gemm_relu_ws_plan(_addr(A), _addr(B), _addr(C), int(M), int(N), int(K),
+                                    int(in_dtype), int(out_dtype), int(transB), _addr(workspace),
+                                    int(workspace_bytes))
     return None if r is None else r.decode()
 
 

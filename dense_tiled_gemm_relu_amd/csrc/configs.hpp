@@ -34,6 +34,10 @@ enum ConfigId : int {
     CFG_G64x64x64,
     CFG_D256x192x32_S4_I16,
     CFG_D256x256x32_S4_I16P,
+    CFG_D64x128x64_S4_SPLITK,
+    CFG_D64x256x64_S3_SPLITK,
+    CFG_D64x128x128_S3_SPLITK,
+    CFG_D64x128x64_S3_SPLITK,
     CFG_COUNT
 };
 
@@ -43,6 +47,9 @@ struct ConfigInfo {
     bool direct;
     bool persistent = false;   // grid of min(tiles, CUs) workgroups looping over tiles
     bool streamk = false;      // whole-tile workgroups, then stream-K units (workspace)
+    bool splitk = false;       // every tile split along K: fp32 partials in a caller's workspace
+    int bk16 = 0;              // K-split configurations: K elements per step (16-bit inputs)
+    int per_cu = 1;            // K-split configurations: workgroups resident per CU
 };
 
 inline const ConfigInfo& config_info(int id)
@@ -69,6 +76,10 @@ inline const ConfigInfo& config_info(int id)
         {"g64x64x64", 64, 64, false},
         {"d256x192x32_s4_i16", 256, 192, true},
         {"d256x256x32_s4_i16p", 256, 256, true, true},
+        {"d64x128x64_s4_splitk", 64, 128, true, false, false, true, 64, 1},
+        {"d64x256x64_s3_splitk", 64, 256, true, false, false, true, 64, 1},
+        {"d64x128x128_s3_splitk", 64, 128, true, false, false, true, 128, 1},
+        {"d64x128x64_s3_splitk", 64, 128, true, false, false, true, 64, 2},
     };
     return table[id];
 }
@@ -92,7 +103,8 @@ inline constexpr bool comparison_config(int id)
            id == CFG_D256x256x64_S2_16 || id == CFG_D256x256x32_S4_IP ||
            id == CFG_D256x256x32_S4_ISK || id == CFG_D256x256x32_S4_W8I ||
            id == CFG_D256x256x32_S5_W8I || id == CFG_D256x256x64_S2_W8 || id == CFG_D256x128x64_S2 ||
-           id == CFG_D256x256x32_S4_I16P;
+           id == CFG_D256x256x32_S4_I16P || id == CFG_D64x256x64_S3_SPLITK ||
+           id == CFG_D64x128x128_S3_SPLITK || id == CFG_D64x128x64_S3_SPLITK;
 }
 
 // Whether this build of the library holds kernels of configuration id.
@@ -173,6 +185,27 @@ template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x64_S2
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D128x128x64_S3> {
     using type = Cfg<IN, OUT, TB, 128, 128, bk_of<IN, 64>, 2, 2, 3, true>;
+};
+// Skinny shapes with a workspace: 64 x 128 tiles (waves of 32 x 64), each
+// tile's K range cut into parts taken by separate workgroups, which publish
+// fp32 partial tiles; the last part of a tile to finish sums them, applies the
+// ReLU and stores C.  A part reads 256-byte pieces of many consecutive (K,N) B
+// rows, which HBM serves almost at the rate of contiguous reads, where
+// whole-K 64-column tiles read 128-byte pieces of every row.
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D64x128x64_S4_SPLITK> {
+    using type = Cfg<IN, OUT, TB, 64, 128, bk_of<IN, 64>, 2, 2, 4, true, false, 32, false, false, true>;
+};
+// Comparison variants of the K-split tile: 256 columns (512-byte row pieces),
+// 128-element steps, and a three-stage ring small enough for two workgroups
+// per CU.
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D64x256x64_S3_SPLITK> {
+    using type = Cfg<IN, OUT, TB, 64, 256, bk_of<IN, 64>, 2, 2, 3, true, false, 32, false, false, true>;
+};
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D64x128x128_S3_SPLITK> {
+    using type = Cfg<IN, OUT, TB, 64, 128, bk_of<IN, 128>, 2, 2, 3, true, false, 32, false, false, true>;
+};
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D64x128x64_S3_SPLITK> {
+    using type = Cfg<IN, OUT, TB, 64, 128, bk_of<IN, 64>, 2, 2, 3, true, false, 32, false, false, true>;
 };
 // Two-stage 128x128: the smaller tile of the block-scaled inputs.
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D128x128x64_S2> {
@@ -259,7 +292,9 @@ inline bool fp8_config(int cfg)
 {
     return cfg == CFG_D256x256x32_S4_I || cfg == CFG_D256x256x32_S4_ISK ||
            cfg == CFG_D128x128x64_S3 || cfg == CFG_D64x64x64_S4 || cfg == CFG_D32x64x128_S4 ||
-           cfg == CFG_D64x32x128_S4 || cfg == CFG_G128x128x64 || cfg == CFG_G64x64x64;
+           cfg == CFG_D64x32x128_S4 || cfg == CFG_G128x128x64 || cfg == CFG_G64x64x64 ||
+           cfg == CFG_D64x128x64_S4_SPLITK || cfg == CFG_D64x256x64_S3_SPLITK ||
+           cfg == CFG_D64x128x128_S3_SPLITK || cfg == CFG_D64x128x64_S3_SPLITK;
 }
 
 }  // namespace gemm_relu_hip
@@ -308,6 +343,14 @@ inline bool fp8_config(int cfg)
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x32x128_S4>::type>;      \
         case CFG_D32x64x128_S4:                                                            \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D32x64x128_S4>::type>;      \
+        case CFG_D64x128x64_S4_SPLITK:                                                     \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x128x64_S4_SPLITK>::type>; \
+        case CFG_D64x256x64_S3_SPLITK:                                                     \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D64x256x64_S3_SPLITK>::type>(); \
+        case CFG_D64x128x128_S3_SPLITK:                                                    \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D64x128x128_S3_SPLITK>::type>(); \
+        case CFG_D64x128x64_S3_SPLITK:                                                     \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D64x128x64_S3_SPLITK>::type>(); \
         case CFG_G128x128x64:                                                              \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_G128x128x64>::type>;        \
         case CFG_G64x64x64:                                                                \
@@ -348,6 +391,14 @@ inline bool fp8_config(int cfg)
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x32x128_S4>::type>;      \
         case CFG_D32x64x128_S4:                                                            \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D32x64x128_S4>::type>;      \
+        case CFG_D64x128x64_S4_SPLITK:                                                     \
+            return &launch_one<typename CfgOf<IN, OUT, TB, CFG_D64x128x64_S4_SPLITK>::type>; \
+        case CFG_D64x256x64_S3_SPLITK:                                                     \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D64x256x64_S3_SPLITK>::type>(); \
+        case CFG_D64x128x128_S3_SPLITK:                                                    \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D64x128x128_S3_SPLITK>::type>(); \
+        case CFG_D64x128x64_S3_SPLITK:                                                     \
+            return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D64x128x64_S3_SPLITK>::type>(); \
         case CFG_G128x128x64:                                                              \
             return &launch_one<typename CfgOf<IN, OUT, TB, CFG_G128x128x64>::type>;        \
         case CFG_G64x64x64:                                                                \

@@ -41,6 +41,8 @@ struct Env {
                           // columns first (0: never split); -1 = plan selection decides
     int pgrid = 0;        // GEMM_RELU_PERSISTENT_GRID=<n>: workgroups of a persistent
                           // configuration (0 = one per CU, at most one per tile)
+    int splitk_parts = 0; // GEMM_RELU_SPLITK_PARTS=<n>: K parts of a K-split plan
+                          // (0 = plan selection decides)
 };
 
 // Debug and tuning switches, read on every call so a process can change them
@@ -65,6 +67,8 @@ Env env()
     if (c && c[0]) e.split_cols = std::max(0, std::atoi(c));
     const char* pg = std::getenv("GEMM_RELU_PERSISTENT_GRID");
     if (pg && pg[0]) e.pgrid = std::max(0, std::atoi(pg));
+    const char* sp = std::getenv("GEMM_RELU_SPLITK_PARTS");
+    if (sp && sp[0]) e.splitk_parts = std::max(0, std::atoi(sp));
     return e;
 }
 
@@ -114,6 +118,10 @@ struct Plan {
     // (d256x192x32_s4_i16) tiles over the rest
     int cfg2 = -1;
     int tiles1 = 0, tiles_m2 = 0, tiles_n2 = 0, n_org2 = 0;
+    // K-split plan: `splits` parts of split_steps K steps per tile, ws_need
+    // bytes of workspace
+    int splits = 0, split_steps = 0;
+    uint64_t ws_need = 0;
 };
 
 
@@ -296,6 +304,7 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     const bool sk_possible = sk_ok && sk_iters >= 2;
     auto usable = [&](int id) {
         return id != CFG_D256x128x64_S2 &&             // built for block-scaled inputs only
+               !config_info(id).splitk &&               // needs a workspace (plan_splitk)
                (id != CFG_D256x192x32_S4_I16 || transB) &&    // built for B stored (N,K) only
                // the persistent 16x16-block stream: whole 256x256 tiles inside
                // the matrix, whole K steps, at least a full ring of them
@@ -362,6 +371,61 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
         p.sk_units = sp.units;
     }
     return p;
+}
+
+// ---- K split with a workspace (gemm_relu_ws).  Skinny shapes (M <= 64) whose
+// 64 x 128 tiles fill at most half the CUs: each tile's K steps are cut into
+// `splits` equal parts, one workgroup each, enough to give every CU a part,
+// with at least 8 steps a part.  With B stored (N,K) the workspace-free 32 x 64
+// tiles already read whole K runs of each B row; there the split is taken only
+// where those tiles would leave half the CUs idle (measured on MI355X, 64 x
+// 8192 x 8192 fp16 from cold HBM: (K,N) B 40.4 -> 32.1 us per call; (N,K) B
+// 34.1 -> 35.8 us, so not split).  GEMM_RELU_FORCE_CONFIG=d64x128x64_s4_splitk
+// takes it for any shape of at most kSplitkMaxTiles tiles (up to 16 parts);
+// GEMM_RELU_SPLITK_PARTS sets the part count.  Needs ws_need <= ws_bytes;
+// otherwise the plan is left as it is.
+// Workspace: kSplitkFlagBytes of arrival counters (one per tile, zero between
+// calls), then splits x tiles fp32 partial tiles.
+constexpr int kSplitkMaxParts = 16;
+constexpr int kSplitkMaxTiles = 1024;
+constexpr uint64_t kSplitkFlagBytes = 4 * kSplitkMaxTiles;
+
+bool plan_splitk(Plan& p, int64_t M, int64_t N, int64_t K, int in_dt, int transB, uint64_t ws_bytes,
+                 const Env& e)
+{
+    const bool forced = e.force_cfg >= 0 && config_info(e.force_cfg).splitk;
+    if (e.force_cfg >= 0 && !forced) return false;
+    const int id = forced ? e.force_cfg : int(CFG_D64x128x64_S4_SPLITK);
+    const ConfigInfo& ci = config_info(id);
+    if (ws_bytes == 0 || !config_built(id) || !direct_fits(id, N, K, transB)) return false;
+    const int64_t steps = ceil_div(K, fp8_input(in_dt) ? 2 * ci.bk16 : ci.bk16);
+    const int64_t tiles = ceil_div(M, ci.bm) * ceil_div(N, ci.bn);
+    const int64_t slots = int64_t(kNumCUs) * ci.per_cu;      // workgroups resident at once
+    int64_t parts = 0;
+    if (e.splitk_parts > 0 && (forced || M <= 64)) {
+        parts = e.splitk_parts;
+    } else if (forced) {
+        parts = std::max<int64_t>(2, std::min<int64_t>(kSplitkMaxParts, slots / tiles));
+    } else {
+        if (M > 64 || tiles * 2 > kNumCUs) return false;
+        if (transB && ceil_div(M, 32) * ceil_div(N, 64) * 2 > kNumCUs) return false;
+        parts = std::min<int64_t>({kSplitkMaxParts, slots / tiles, steps / 8});
+    }
+    parts = std::min<int64_t>({parts, steps, kSplitkMaxParts});
+    if (parts < 2) return false;
+    const int64_t split_steps = ceil_div(steps, parts);
+    const int64_t splits = ceil_div(steps, split_steps);     // every part non-empty
+    if (splits < 2 || tiles > kSplitkMaxTiles) return false;
+    const uint64_t need = kSplitkFlagBytes + uint64_t(splits) * uint64_t(tiles) * ci.bm * ci.bn * 4;
+    if (need > ws_bytes) return false;
+    p.cfg = id;
+    p.cfg2 = -1;
+    p.tiles_m = int(ceil_div(M, ci.bm));
+    p.tiles_n = int(ceil_div(N, ci.bn));
+    p.splits = int(splits);
+    p.split_steps = int(split_steps);
+    p.ws_need = need;
+    return true;
 }
 
 // ---- block-scaled (MX) inputs
@@ -516,13 +580,41 @@ LaunchFn pick_launcher(int in_dt, int out_dt, int transB, int cfg)
     }
 }
 
-}  // namespace
+// A caller's workspace: NULL or 0 bytes means none; otherwise 256-byte aligned
+// and disjoint from A, B and C.
+bool workspace_ok(const void* ws, uint64_t ws_bytes, const void* A, const void* B, const void* C,
+                  int64_t M, int64_t N, int64_t K, int in_dt, int out_dt)
+{
+    if (!ws || ws_bytes == 0) return true;
+    const uintptr_t uw = reinterpret_cast<uintptr_t>(ws);
+    if (uw & 255) return false;
+    const uint64_t in_bytes = uint64_t(elem_bytes(in_dt));
+    return !overlaps(uw, ws_bytes, reinterpret_cast<uintptr_t>(A), uint64_t(M) * uint64_t(K) * in_bytes) &&
+           !overlaps(uw, ws_bytes, reinterpret_cast<uintptr_t>(B), uint64_t(K) * uint64_t(N) * in_bytes) &&
+           !overlaps(uw, ws_bytes, reinterpret_cast<uintptr_t>(C),
+                     uint64_t(M) * uint64_t(N) * uint64_t(elem_bytes(out_dt)));
+}
 
-extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                         int in_dtype, int out_dtype, int transB, void* stream)
+// The plan of gemm_relu / gemm_relu_ws: the workspace-free choice, then a K
+// split where a workspace of ws_bytes allows one.
+Plan make_plan_ws(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K, int in_dt,
+                  int out_dt, int transB, const void* ws, uint64_t ws_bytes, const Env& e)
+{
+    Plan p = make_plan(A, B, C, M, N, K, in_dt, out_dt, transB, e);
+    if (p.status != GEMM_RELU_OK || p.empty) return p;
+    if (!workspace_ok(ws, ws_bytes, A, B, C, M, N, K, in_dt, out_dt)) {
+        p.status = GEMM_RELU_EINVAL;
+        return p;
+    }
+    if (ws && ws_bytes) plan_splitk(p, M, N, K, in_dt, transB, ws_bytes, e);
+    return p;
+}
+
+int run_gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K, int in_dtype,
+                  int out_dtype, int transB, void* workspace, uint64_t ws_bytes, void* stream)
 {
     const Env e = env();
-    Plan p = make_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB, e);
+    Plan p = make_plan_ws(A, B, C, M, N, K, in_dtype, out_dtype, transB, workspace, ws_bytes, e);
     if (p.status != GEMM_RELU_OK) return p.status;
     if (p.empty) return GEMM_RELU_OK;
     const int dev = check_device();
@@ -557,6 +649,12 @@ extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64
         args.dp_tiles = p.dp_tiles;
         args.sk_units = p.sk_units;
     }
+    if (p.splits > 0) {
+        args.flags = static_cast<unsigned*>(workspace);
+        args.ws = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + kSplitkFlagBytes);
+        args.splits = p.splits;
+        args.split_steps = p.split_steps;
+    }
 
     LaunchFn fn = p.cfg2 >= 0 ? launcher_i16_2r(in_dtype, out_dtype)
                               : pick_launcher(in_dtype, out_dtype, transB, p.cfg);
@@ -564,6 +662,7 @@ extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64
     const int tiles = p.tiles_m * p.tiles_n;
     int grid = config_info(p.cfg).persistent ? std::min(tiles, e.pgrid > 0 ? e.pgrid : kNumCUs)
                : config_info(p.cfg).streamk  ? p.dp_tiles + p.sk_units
+               : p.splits > 0                ? tiles * p.splits
                                              : tiles;
     if (p.cfg2 >= 0) {
         args.tiles1 = p.tiles1;
@@ -579,6 +678,41 @@ extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64
         if (hipGetLastError() != hipSuccess) return GEMM_RELU_EHIP;
     }
     return GEMM_RELU_OK;
+}
+
+bool codes_and_sizes_ok(int64_t M, int64_t N, int64_t K, int in_dt, int out_dt, int transB)
+{
+    const int64_t lim = INT32_MAX;
+    return M >= 0 && N >= 0 && K >= 0 && M <= lim && N <= lim && K <= lim &&
+           (in_dt == GEMM_RELU_F16 || in_dt == GEMM_RELU_BF16 || fp8_input(in_dt)) &&
+           (out_dt == GEMM_RELU_F16 || out_dt == GEMM_RELU_BF16 || out_dt == GEMM_RELU_F32) &&
+           (transB == 0 || transB == 1);
+}
+
+}  // namespace
+
+extern "C" int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                         int in_dtype, int out_dtype, int transB, void* stream)
+{
+    return run_gemm_relu(A, B, C, M, N, K, in_dtype, out_dtype, transB, nullptr, 0, stream);
+}
+
+extern "C" int gemm_relu_ws(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                            int in_dtype, int out_dtype, int transB, void* workspace,
+                            uint64_t workspace_bytes, void* stream)
+{
+    return run_gemm_relu(A, B, C, M, N, K, in_dtype, out_dtype, transB, workspace, workspace_bytes,
+                         stream);
+}
+
+extern "C" int64_t gemm_relu_workspace_size(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
+                                            int transB)
+{
+    if (!codes_and_sizes_ok(M, N, K, in_dtype, out_dtype, transB)) return GEMM_RELU_EINVAL;
+    if (M == 0 || N == 0) return 0;
+    Plan p;
+    if (!plan_splitk(p, M, N, K, in_dtype, transB, UINT64_MAX, env())) return 0;
+    return int64_t(p.ws_need);
 }
 
 extern "C" const char* gemm_relu_configs(void)
@@ -615,6 +749,18 @@ extern "C" const char* gemm_relu_plan(const void* A, const void* B, const void* 
                                       int transB)
 {
     const Plan p = make_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB, env());
+    if (p.status == GEMM_RELU_EINVAL) return nullptr;
+    if (p.status != GEMM_RELU_OK) return "unsupported";
+    if (p.empty) return "none";
+    return p.cfg2 >= 0 ? kSplitName : config_info(p.cfg).name;
+}
+
+extern "C" const char* gemm_relu_ws_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
+                                         int64_t K, int in_dtype, int out_dtype, int transB,
+                                         const void* workspace, uint64_t workspace_bytes)
+{
+    const Plan p = make_plan_ws(A, B, C, M, N, K, in_dtype, out_dtype, transB, workspace, workspace_bytes,
+                                env());
     if (p.status == GEMM_RELU_EINVAL) return nullptr;
     if (p.status != GEMM_RELU_OK) return "unsupported";
     if (p.empty) return "none";

@@ -85,6 +85,12 @@ struct KernelArgs {
     // columns [n_org2, N).  tiles1 is a multiple of nxcd.
     int tiles1;
     int tiles_m2, tiles_n2, panel2, n_org2;
+    // K-split configurations: workgroup w takes part s = w div T of tile
+    // w mod T (T = tiles_m tiles_n): the K steps [s split_steps, (s + 1)
+    // split_steps).  Its fp32 partial tile goes to slot s T + tile of ws (BM x
+    // BN floats each); flags holds one arrival counter per tile, zero between
+    // launches.
+    int splits, split_steps;
 };
 
 // The tiles one configuration covers inside a launch: a grid of tiles_m x
@@ -297,10 +303,11 @@ template <> struct OutTraits<DT_F32> {
 // ---------------------------------------------------------- configuration
 template <int IN_DT_, int OUT_DT_, bool TRANS_B_, int BM_, int BN_, int BK_, int WAVES_M_,
           int WAVES_N_, int STAGES_, bool DIRECT_, bool INTERLEAVE_ = false, int MB_ = 32,
-          bool PERSISTENT_ = false, bool STREAMK_ = false>
+          bool PERSISTENT_ = false, bool STREAMK_ = false, bool SPLITK_ = false>
 struct Cfg {
     static constexpr bool PERSISTENT = PERSISTENT_;   // tile loop over a grid of <= 1 per CU
     static constexpr bool STREAMK = STREAMK_;         // last round split along K
+    static constexpr bool SPLITK = SPLITK_;           // every tile split along K into fp32 partials
     static constexpr int IN_DT = IN_DT_, OUT_DT = OUT_DT_;
     static constexpr bool TRANS_B = TRANS_B_, DIRECT = DIRECT_, INTERLEAVE = INTERLEAVE_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
@@ -363,6 +370,8 @@ struct Cfg {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity of a gfx950 CU");
     static_assert(!STREAMK_ || (INTERLEAVE_ && !MX && !PERSISTENT_),
                   "stream-K: the interleaved pipeline, unscaled inputs");
+    static_assert(!SPLITK_ || (DIRECT_ && !INTERLEAVE_ && !MX && !PERSISTENT_ && !STREAMK_),
+                  "K split: the plain direct pipeline, unscaled inputs");
 
     // Interleaved direct pipeline: the LOADS_PER_STAGE copies of the stage
     // STAGES-1 ahead are spread over the KSUB k-steps of a BK step, one per
@@ -510,10 +519,13 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
     const int n0 = (C::DIRECT && !C::TRANS_B) ? min(n_own, N - BN) : n_own;
     // Direct path: K / BK full steps through the copy pipeline plus, if K % BK,
     // one register-staged tail step.  Register-staged path: ceil(K / BK) steps.
-    // A stream-K piece: its full steps from kt0 on, and the tail step if it
-    // ends the K range.
-    const int kt0 = C::STREAMK ? sk->pc.kt0 : 0;
-    const int nk = C::STREAMK ? min(sk->pc.kt1, K / BK) - kt0 : C::DIRECT ? K / BK : (K + BK - 1) / BK;
+    // A stream-K piece or a K-split part covers the steps [kt0, kt1) of
+    // ceil(K / BK): its full steps, and the tail step if it ends the K range.
+    const int ksteps = (K + BK - 1) / BK;
+    const int split = C::SPLITK ? (int)blockIdx.x / (reg.tiles_m * reg.tiles_n) : 0;
+    const int kt0 = C::STREAMK ? sk->pc.kt0 : C::SPLITK ? split * args.split_steps : 0;
+    const int kt1 = C::STREAMK ? sk->pc.kt1 : C::SPLITK ? min(ksteps, kt0 + args.split_steps) : ksteps;
+    const int nk = C::DIRECT ? max(0, min(kt1, K / BK) - kt0) : ksteps;
 
     // ---- loader geometry: this thread owns LDS slots q = i*NTHREADS + tid of
     // each stage region; a wave's 64 slots are contiguous (one 1 KiB DMA write).
@@ -1219,7 +1231,7 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
     if constexpr (C::DIRECT) {
         // K tail (K % BK != 0): one register-staged step with element-wise zero
         // fill past K, after every wave has left the copy ring.
-        if (C::STREAMK ? (K % BK != 0 && sk->pc.kt1 > K / BK) : K % BK != 0) {
+        if (K % BK != 0 && kt1 > K / BK) {
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             barrier_lds();
             if constexpr (C::MX) load_scales_tail(nk, sc_cur);
@@ -1296,6 +1308,94 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
                                    __HIP_MEMORY_SCOPE_AGENT);
             from_partials = true;
         }
+    }
+
+    // ---- K split: every part publishes its partial tile and counts itself in
+    // at the tile's counter; the last to arrive adds the parts in K order (its
+    // own from registers), so the sum is the same whichever part finishes
+    // last, and goes on to the epilogue with it.  Parts never wait for one
+    // another.  The partials are written and read as device-scope atomics
+    // (each coherent across the XCDs' separate L2 caches by itself), and a
+    // part counts itself in only once its stores have completed; so no L2
+    // write-back or invalidation is needed, which a release / acquire pair
+    // would do for the whole cache of every part's XCD.  Partial layout: value
+    // e of group v = (i TN + j) NQ + q of thread tid at float (4 v + e)
+    // NTHREADS + tid of the slot (each dword store of a wave is 256
+    // consecutive bytes).
+    if constexpr (C::SPLITK) {
+        constexpr int NQS = NACC / 4, NV = TM * TN * NQS;
+        const int tiles = reg.tiles_m * reg.tiles_n;
+        const int tile = (int)blockIdx.x - split * tiles;
+        auto slot = [&](int p) { return args.ws + ((size_t)(p * tiles + tile) * (BM * BN) + tid); };
+        float* own = slot(split);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < NQS; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        __hip_atomic_store(own + (((i * TN + j) * NQS + q) * 4 + e) * C::NTHREADS,
+                                           acc[i][j][4 * q + e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // this wave's stores have completed, then every wave's
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+        __shared__ int arrived;
+        if (tid == 0)
+            arrived = (int)__hip_atomic_fetch_add(args.flags + tile, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        barrier_lds();
+        if (arrived + 1 != args.splits) return;     // a later part completes the tile
+        if (tid == 0)
+            __hip_atomic_store(args.flags + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the other parts' tiles in groups of PB, all of a group's loads in
+        // flight together, then added in part order
+        constexpr int PB = 4;
+        f32x4_t sum[NV];
+        for (int p0 = 0; p0 < args.splits; p0 += PB) {
+            f32x4_t x[PB][NV];
+#pragma unroll
+            for (int u = 0; u < PB; ++u) {
+                const int p = p0 + u;
+                if (p < args.splits && p != split) {
+                    const float* sp = slot(p);
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            x[u][v][e] = __hip_atomic_load(sp + (4 * v + e) * C::NTHREADS, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < PB; ++u) {
+                const int p = p0 + u;
+                if (p < args.splits) {
+                    if (p == split) {
+#pragma unroll
+                        for (int i = 0; i < TM; ++i)
+#pragma unroll
+                            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                                for (int q = 0; q < NQS; ++q)
+                                    x[u][(i * TN + j) * NQS + q] =
+                                        f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                                acc[i][j][4 * q + 3]};
+                    }
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) sum[v] = p == 0 ? x[u][v] : sum[v] + x[u][v];
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < NQS; ++q)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = sum[(i * TN + j) * NQS + q][e];
     }
 
     // ---- epilogue: ReLU on the fp32 accumulators, convert, store.
@@ -1857,6 +1957,9 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_relu_kernel(KernelArgs ar
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
             barrier_lds();
         }
+    } else if constexpr (C::SPLITK) {
+        gemm_relu_tile<C>(args, (int)blockIdx.x % (args.tiles_m * args.tiles_n), smem, nullptr,
+                          Region{args.tiles_m, args.tiles_n, args.panel, 0});
     } else {
         gemm_relu_tile<C>(args, blockIdx.x, smem, nullptr,
                           Region{args.tiles_m, args.tiles_n, args.panel, 0});

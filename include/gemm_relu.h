@@ -96,6 +96,57 @@ extern "C" {
 int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
               int in_dtype, int out_dtype, int transB, void* stream);
 
+/*
+ * gemm_relu_ws — gemm_relu with a device workspace the caller provides, which
+ * lets the library split the K range of each output tile over several
+ * workgroups.  The product is that of gemm_relu (page "TileLang：GPU/NPU 通用算
+ * 子 DSL", §3.2); the fp32 accumulator of an output element is then formed in
+ * parts, each part a sum over a contiguous K range, and the parts are added in
+ * K order in fp32 before max(x, 0) and the rounding (the ReLU is never applied
+ * to a part: it does not distribute over the sum).
+ *
+ * Used for skinny shapes (M <= 64 with few output tiles), whose (K,N) B would
+ * otherwise be read as narrow column slabs, which HBM serves slowly: each part
+ * reads a contiguous run of many K rows instead.  Other shapes, or a workspace
+ * smaller than gemm_relu_workspace_size, run exactly as gemm_relu.
+ *
+ * Arguments as for gemm_relu, plus
+ *   workspace        device pointer, 256-byte aligned, disjoint from A, B and
+ *                    C; or NULL (no workspace: the call is gemm_relu).
+ *   workspace_bytes  its size in bytes (0: no workspace).
+ *
+ * Workspace contents: the first 4096 bytes are arrival counters of the split
+ * tiles.  They must be zero before the workspace's first use (hipMemset once
+ * after allocating it), and every call that splits leaves them zero again;
+ * the rest holds fp32 partial tiles during the call and is not read before it
+ * is written.  Calls that may run concurrently (other streams, or graphs
+ * replayed concurrently) need workspaces of their own; calls ordered on one
+ * stream may share one.  The library keeps no pointer to it.  The call
+ * allocates nothing, so it may be captured into a graph.
+ *
+ * Numerics as for gemm_relu; the summation order is fixed for given sizes, so
+ * repeated calls give the same bits.  Errors as for gemm_relu, plus EINVAL for
+ * a misaligned workspace or one that overlaps A, B or C.
+ */
+int gemm_relu_ws(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                 int in_dtype, int out_dtype, int transB, void* workspace,
+                 uint64_t workspace_bytes, void* stream);
+
+/*
+ * gemm_relu_workspace_size — bytes of workspace gemm_relu_ws would use for
+ * these sizes and types (0 when it would not split K; otherwise 4096 bytes of
+ * counters plus 32 KiB per 64 x 128 output tile and K part), or
+ * GEMM_RELU_EINVAL (negative) for invalid sizes or codes.  Host-only.
+ */
+int64_t gemm_relu_workspace_size(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
+                                 int transB);
+
+/* Configuration name gemm_relu_ws would launch with this workspace (as
+ * gemm_relu_plan; the workspace pointer is checked, never dereferenced). */
+const char* gemm_relu_ws_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
+                              int64_t K, int in_dtype, int out_dtype, int transB,
+                              const void* workspace, uint64_t workspace_bytes);
+
 /* Static message for a status code (never NULL). */
 const char* gemm_relu_strerror(int status);
 
