@@ -25,13 +25,14 @@ OK = 0
 EINVAL = -1
 EUNSUPPORTED = -2
 EHIP = -3
+ESCRATCH = -4
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgemm_relu.so")
 PROBE_LIB_PATH = os.path.join(_PKG, "libgemm_relu_probe.so")
 
 EXPORTS = ("gemm_relu", "gemm_relu_strerror", "gemm_relu_configs", "gemm_relu_plan",
-           "gemm_relu_ws", "gemm_relu_workspace_size", "gemm_relu_ws_plan",
+           "gemm_relu_ws", "gemm_relu_workspace_size", "gemm_relu_ws_plan", "gemm_relu_noalloc",
            "gemm_relu_mx", "gemm_relu_mx_plan", "gemm_relu_sp", "gemm_relu_sp_plan")
 
 _lib = None
@@ -71,6 +72,9 @@ def library():
     lib.gemm_relu_ws.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, vp, u64, vp]
     lib.gemm_relu_ws.restype = ctypes.c_int
+    lib.gemm_relu_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, vp]
+    lib.gemm_relu_noalloc.restype = ctypes.c_int
     lib.gemm_relu_workspace_size.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.gemm_relu_workspace_size.restype = i64
     lib.gemm_relu_ws_plan.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int,
@@ -157,6 +161,21 @@ def gemm_relu_ws(A, B, C, M, N, K, in_dtype, out_dtype, transB, workspace, works
     its size in bytes); raises GemmReluError on failure."""
     rc = gemm_relu_ws_status(A, B, C, M, N, K, in_dtype, out_dtype, transB, workspace,
                              workspace_bytes, stream)
+    if rc != OK:
+        raise GemmReluError(rc, gemm_relu_strerror(rc))
+
+
+def gemm_relu_noalloc_status(A, B, C, M, N, K, in_dtype, out_dtype, transB, stream=None):
+    """Call the no-allocation C-ABI entry and return its status code."""
+    return library().gemm_relu_noalloc(_addr(A), _addr(B), _addr(C), int(M), int(N), int(K),
+                                       int(in_dtype), int(out_dtype), int(transB),
+                                       _stream_handle(stream))
+
+
+def gemm_relu_noalloc(A, B, C, M, N, K, in_dtype, out_dtype, transB, stream=None):
+    """gemm_relu_ws with the library's own per-GPU scratch array as the
+    workspace (allocates nothing); raises GemmReluError on failure."""
+    rc = gemm_relu_noalloc_status(A, B, C, M, N, K, in_dtype, out_dtype, transB, stream)
     if rc != OK:
         raise GemmReluError(rc, gemm_relu_strerror(rc))
 

@@ -680,6 +680,34 @@ int run_gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, i
     return GEMM_RELU_OK;
 }
 
+// ---- gemm_relu_noalloc: the K-split workspace in a device array of the
+// library (one per GPU, held until the process ends) instead of the caller's.
+// Host code never passes the array's name to a kernel: its device address is
+// looked up once per device, with that device current.
+constexpr uint64_t kScratchBytes = uint64_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct ScratchAddr {
+    std::once_flag once;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchAddr g_scratch[kMaxDevices];
+
+void* scratch_address(int dev)
+{
+    ScratchAddr& s = g_scratch[dev];
+    std::call_once(s.once, [&] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+    return s.err == hipSuccess ? s.ptr : nullptr;
+}
+
+// Zeroes the arrival words at the start of the scratch (a kernel, so that a
+// captured graph holds no memset node).
+__global__ void __launch_bounds__(256) clear_words(unsigned* p, int n)
+{
+    for (int i = threadIdx.x; i < n; i += 256) p[i] = 0u;
+}
+
 bool codes_and_sizes_ok(int64_t M, int64_t N, int64_t K, int in_dt, int out_dt, int transB)
 {
     const int64_t lim = INT32_MAX;
@@ -703,6 +731,33 @@ extern "C" int gemm_relu_ws(const void* A, const void* B, void* C, int64_t M, in
 {
     return run_gemm_relu(A, B, C, M, N, K, in_dtype, out_dtype, transB, workspace, workspace_bytes,
                          stream);
+}
+
+extern "C" int gemm_relu_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                                 int in_dtype, int out_dtype, int transB, void* stream)
+{
+    const Env e = env();
+    const Plan p = make_plan(A, B, C, M, N, K, in_dtype, out_dtype, transB, e);
+    if (p.status != GEMM_RELU_OK) return p.status;
+    if (p.empty) return GEMM_RELU_OK;
+    Plan q = p;
+    if (!plan_splitk(q, M, N, K, in_dtype, transB, UINT64_MAX, e))
+        return run_gemm_relu(A, B, C, M, N, K, in_dtype, out_dtype, transB, nullptr, 0, stream);
+    if (q.ws_need > kScratchBytes) return GEMM_RELU_ESCRATCH;
+    const int dev = check_device();
+    if (dev != GEMM_RELU_OK) return dev;
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess) return GEMM_RELU_EHIP;
+    void* ws = scratch_address(d);
+    if (!ws) return GEMM_RELU_EHIP;
+    // the scratch keeps what the last call on this GPU left: start from
+    // zeroed arrival words
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    void* params[] = {&ws, const_cast<int*>(&kSplitkMaxTiles)};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(&clear_words), dim3(1), dim3(256), params, 0, st) !=
+        hipSuccess)
+        return GEMM_RELU_EHIP;
+    return run_gemm_relu(A, B, C, M, N, K, in_dtype, out_dtype, transB, ws, kScratchBytes, stream);
 }
 
 extern "C" int64_t gemm_relu_workspace_size(int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
@@ -740,6 +795,7 @@ extern "C" const char* gemm_relu_strerror(int status)
     case GEMM_RELU_EINVAL: return "invalid argument";
     case GEMM_RELU_EUNSUPPORTED: return "unsupported device or size";
     case GEMM_RELU_EHIP: return "HIP runtime error";
+    case GEMM_RELU_ESCRATCH: return "the K split needs more than the 16 MiB scratch of gemm_relu_noalloc";
     default: return "unknown status";
     }
 }

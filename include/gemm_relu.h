@@ -44,6 +44,7 @@ extern "C" {
 #define GEMM_RELU_EINVAL       -1 /* bad argument: size, pointer, code, overlap */
 #define GEMM_RELU_EUNSUPPORTED -2 /* valid request the library cannot run (device, size limits) */
 #define GEMM_RELU_EHIP         -3 /* a HIP runtime call or kernel launch failed */
+#define GEMM_RELU_ESCRATCH     -4 /* gemm_relu_noalloc: the request needs more scratch than it holds */
 
 /*
  * gemm_relu — C[i][j] = max( sum_k A[i][k] * opB[k][j], 0 ).
@@ -131,6 +132,25 @@ int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64
 int gemm_relu_ws(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                  int in_dtype, int out_dtype, int transB, void* workspace,
                  uint64_t workspace_bytes, void* stream);
+
+/*
+ * gemm_relu_noalloc — gemm_relu_ws for callers that cannot allocate device
+ * memory or bring a workspace (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a 16 MiB device array of
+ * the library, one per GPU, held until the process ends; the call allocates
+ * nothing.  Same arguments, results and errors as gemm_relu, plus
+ * GEMM_RELU_ESCRATCH when the K split the plan would take needs more than
+ * 16 MiB (gemm_relu_workspace_size bytes; never for plans chosen without a
+ * forced configuration, which need at most 8 MiB + 4 KiB).
+ *
+ * Every call on a GPU uses that GPU's one array, which keeps what the last call
+ * left: each call that splits first zeroes its arrival words (a small kernel on
+ * `stream`).  Calls that overlap on one GPU (other streams, concurrently
+ * replayed graphs) race on the array and give undefined results; calls ordered
+ * on one stream do not.
+ */
+int gemm_relu_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                      int in_dtype, int out_dtype, int transB, void* stream);
 
 /*
  * gemm_relu_workspace_size — bytes of workspace gemm_relu_ws would use for
