@@ -331,7 +331,7 @@ def ceiling_kind(in_dtype, sparse=False, plan=None):
     the 2:4 sparse fp16 form, 5 fp16 16x16x32 (the 16x16-block tiles)."""
     if sparse:
         return 4
-    if plan is not None and (plan.endswith("_i16") or plan.endswith("_16")):
+    if plan is not None and ("_i16" in plan or plan.endswith("_16")):
         return 5
     if in_dtype == wl.MX_E2M1:
         return 2

@@ -340,8 +340,8 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
         // The 256x256 tile: 16x16x32 MFMA blocks for 16-bit inputs, which on
         // random data the power-limited chip clocks higher than the 32x32x16
         // form (measured 5-8% faster per call at 4096^3 and 8192^3, the same
-        // bits); 8-bit inputs have only the 32x32x64 form here.
-        const int big = fp8_input(in_dt) ? CFG_D256x256x32_S4_I : CFG_D256x256x32_S4_I16;
+        // bits), with eight waves; 8-bit inputs have only the 32x32x64 form here.
+        const int big = fp8_input(in_dt) ? CFG_D256x256x32_S4_I : CFG_D256x256x32_S4_I16W8;
         for (int id : {big, int(CFG_D128x128x64_S3), int(CFG_D64x64x64_S4), int(CFG_D32x64x128_S4),
                        int(CFG_D64x32x128_S4)})
             if (usable(id) && (id != CFG_D32x64x128_S4 || skinny) && (cfg < 0 || cost(id) < cost(cfg)))
@@ -362,7 +362,7 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     // a narrower last round for 16-bit inputs with B stored (N,K): chosen by
     // the cost model unless a configuration was forced; GEMM_RELU_SPLIT_COLS
     // forces (or, with 0, forbids) it
-    if (cfg == CFG_D256x256x32_S4_I16 && transB && e.split_cols != 0 &&
+    if ((cfg == CFG_D256x256x32_S4_I16 || cfg == CFG_D256x256x32_S4_I16W8) && transB && e.split_cols != 0 &&
         (e.split_cols > 0 || forced < 0))
         plan_split(p, M, N, e.split_cols > 0 ? e.split_cols : -1);
     if (config_info(cfg).streamk) {

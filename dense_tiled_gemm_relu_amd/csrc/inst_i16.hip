@@ -70,6 +70,24 @@ LaunchFn launcher_i16p(int in_dt, int out_dt, bool transB)
     return nullptr;
 }
 
+template <int IN, bool TB>
+static LaunchFn i16w8_out(int out_dt)
+{
+    switch (out_dt) {
+    case DT_F16: return &launch_one<typename CfgOf<IN, DT_F16, TB, CFG_D256x256x32_S4_I16W8>::type>;
+    case DT_BF16: return &launch_one<typename CfgOf<IN, DT_BF16, TB, CFG_D256x256x32_S4_I16W8>::type>;
+    case DT_F32: return &launch_one<typename CfgOf<IN, DT_F32, TB, CFG_D256x256x32_S4_I16W8>::type>;
+    default: return nullptr;
+    }
+}
+
+LaunchFn launcher_i16w8(int in_dt, int out_dt, bool transB)
+{
+    if (in_dt == DT_F16) return transB ? i16w8_out<DT_F16, true>(out_dt) : i16w8_out<DT_F16, false>(out_dt);
+    if (in_dt == DT_BF16) return transB ? i16w8_out<DT_BF16, true>(out_dt) : i16w8_out<DT_BF16, false>(out_dt);
+    return nullptr;
+}
+
 LaunchFn launcher_i16_192(int in_dt, int out_dt)
 {
     if (in_dt == DT_F16) return i16_192_out<DT_F16>(out_dt);

@@ -81,16 +81,16 @@ def test_null_operands_allowed_when_K_is_zero():
 
 
 @pytest.mark.parametrize("M,N,K,transB,aligned,want", [
-    (8192, 8192, 8192, 0, True, "d256x256x32_s4_i16"),
-    (4096, 4096, 4096, 0, True, "d256x256x32_s4_i16"),
+    (8192, 8192, 8192, 0, True, "d256x256x32_s4_i16w8"),
+    (4096, 4096, 4096, 0, True, "d256x256x32_s4_i16w8"),
     (4096, 7168, 4096, 1, True, "d256x256x32_s4_i16+d256x192x32_s4_i16"),
     (256, 256, 256, 0, True, "d64x32x128_s4"),
     (64, 8192, 8192, 0, True, "d32x64x128_s4"),        # skinny: whole-line B rows, twice the workgroups of 64x64
     (32, 16384, 8192, 0, True, "d64x64x64_s4"),        # skinny, but 64x64 tiles fill the CUs
     (2048, 2048, 512, 0, True, "d128x128x64_s3"),
-    (4096, 7168, 4096, 0, True, "d256x256x32_s4_i16"),
-    (4097, 3001, 5003, 0, True, "d256x256x32_s4_i16"),  # ragged and 2-byte aligned rows
-    (4096, 4096, 4096, 0, False, "d256x256x32_s4_i16"), # 2-byte aligned base pointer
+    (4096, 7168, 4096, 0, True, "d256x256x32_s4_i16w8"),
+    (4097, 3001, 5003, 0, True, "d256x256x32_s4_i16w8"),  # ragged and 2-byte aligned rows
+    (4096, 4096, 4096, 0, False, "d256x256x32_s4_i16w8"), # 2-byte aligned base pointer
     (100, 100, 100, 0, True, "d64x32x128_s4"),
     (100, 24, 100, 0, True, "g64x64x64"),              # fewer than 32 columns of (K,N) B
     (100, 24, 100, 1, True, "d64x32x128_s4"),          # transposed B rows are clamped
@@ -200,7 +200,7 @@ def test_mx_interleaved_needs_16_scale_blocks_per_row(monkeypatch, fmt):
     assert gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 1024, 1024, 480, fmt, 0) == "d128x128x64_s2"
 
 
-@pytest.mark.parametrize("in_dtype,want", [(0, "d256x256x32_s4_i16"), (1, "d256x256x32_s4_i16"),
+@pytest.mark.parametrize("in_dtype,want", [(0, "d256x256x32_s4_i16w8"), (1, "d256x256x32_s4_i16w8"),
                                            (3, "d256x256x32_s4_i")])
 def test_mx_only_configuration_not_used_for_other_inputs(monkeypatch, in_dtype, want):
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x128x64_s2")
@@ -241,7 +241,7 @@ def test_comparison_configurations_are_selectable(monkeypatch, name):
     """The persistent tile loop and the 32x32-block tile: forced by name for
     16-bit inputs, never chosen automatically for them (the 16x16-block tile
     is); 8-bit inputs have no persistent build and take the 32x32 tile."""
-    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0) == "d256x256x32_s4_i16"
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0) == "d256x256x32_s4_i16w8"
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", name)
     assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0) == name
     assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 1, 2, 1) == name
@@ -259,7 +259,8 @@ def test_configs_lists_the_plan_names():
     (and, in a comparison build, the comparison ones too)."""
     names = gr.gemm_relu_configs()
     assert len(names) == len(set(names))
-    for want in ("d256x256x32_s4_i16", "d256x256x32_s4_i", "d128x128x64_s3", "d64x64x64_s4",
+    for want in ("d256x256x32_s4_i16w8", "d256x256x32_s4_i16", "d256x192x32_s4_i16",
+                 "d64x128x64_s4_splitk", "d256x256x32_s4_i", "d128x128x64_s3", "d64x64x64_s4",
                  "d64x32x128_s4", "d32x64x128_s4", "g128x128x64", "g64x64x64", "d128x128x64_s2",
                  "sp256x256x64_s3"):
         assert want in names
@@ -275,7 +276,7 @@ def test_comparison_configurations_only_in_a_comparison_build(monkeypatch):
     for name in ("d256x256x32_s4_isk", "d256x256x32_s4_ip", "d256x256x64_s2"):
         monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", name)
         got = gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 0)
-        assert got == (name if cmp_built else "d256x256x32_s4_i16")
+        assert got == (name if cmp_built else "d256x256x32_s4_i16w8")
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x128x64_s2")
     got = gr.gemm_relu_mx_plan(A, SA_, B, SB_, C, 8192, 8192, 8192, 7, 0)
     assert got == ("d256x128x64_s2" if cmp_built else "d256x256x32_s4_i")
@@ -310,11 +311,11 @@ def test_two_region_grid_selection(monkeypatch):
     GEMM_RELU_SPLIT_COLS forces or forbids the split."""
     assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == SPLIT
     assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 0, 0, 1) == SPLIT
-    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 0) == "d256x256x32_s4_i16"
-    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 1) == "d256x256x32_s4_i16"
+    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 0) == "d256x256x32_s4_i16w8"
+    assert gr.gemm_relu_plan(A, B, C, 8192, 8192, 8192, 0, 0, 1) == "d256x256x32_s4_i16w8"
     assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 3, 0, 1) == "d256x256x32_s4_i"
     monkeypatch.setenv("GEMM_RELU_SPLIT_COLS", "0")
-    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == "d256x256x32_s4_i16"
+    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == "d256x256x32_s4_i16w8"
     monkeypatch.setenv("GEMM_RELU_SPLIT_COLS", "1")
     assert gr.gemm_relu_plan(A, B, C, 512, 520, 64, 0, 0, 1) == SPLIT
     assert gr.gemm_relu_plan(A, B, C, 512, 256, 64, 0, 0, 1) == "d256x256x32_s4_i16"
@@ -324,4 +325,4 @@ def test_two_region_grid_selection(monkeypatch):
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x192x32_s4_i16")
     assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == "d256x192x32_s4_i16"
     # the 256x192 tile is built for B stored (N,K) only
-    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 0) == "d256x256x32_s4_i16"
+    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 0) == "d256x256x32_s4_i16w8"

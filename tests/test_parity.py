@@ -32,7 +32,7 @@ DIRECT = built_configs(["d256x256x64_s2", "d256x256x32_s4", "d256x256x32_s5", "d
                         "d256x256x64_s2_16", "d256x256x32_s4_i16", "d256x256x32_s4_ip",
                         "d256x256x32_s4_isk", "d256x256x32_s4_w8i", "d256x256x32_s5_w8i",
                         "d256x256x64_s2_w8", "d128x128x64_s3", "d64x64x64_s4", "d64x32x128_s4",
-                        "d32x64x128_s4", "d256x192x32_s4_i16", SPLIT, PSTREAM])
+                        "d32x64x128_s4", "d256x192x32_s4_i16", SPLIT, PSTREAM, "d256x256x32_s4_i16w8"])
 STAGED = ["g128x128x64", "g64x64x64"]
 COMBOS = [(i, o) for i in (wl.F16, wl.BF16) for o in (wl.F16, wl.BF16, wl.F32)]
 
@@ -46,6 +46,7 @@ def _gpu():
 
 BN_OF = {"d256x256x64_s2": 256, "d256x256x32_s4": 256, "d256x256x32_s5": 256,
          "d256x256x32_s4_i": 256, "d256x256x64_s2_16": 256, "d256x256x32_s4_i16": 256, "d256x256x32_s4_ip": 256,
+         "d256x256x32_s4_i16w8": 256,
          "d256x256x32_s4_isk": 256,
          "d256x256x32_s4_w8i": 256, "d256x256x32_s5_w8i": 256,
          "d256x256x64_s2_w8": 256, "d128x128x64_s3": 128, "d64x64x64_s4": 64,

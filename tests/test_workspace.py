@@ -87,7 +87,7 @@ def test_ws_plan_choice():
     # the square headline shape never splits
     a, b, c, w = fake_args(8192, 8192, 8192)
     assert gr.gemm_relu_ws_plan(a, b, c, 8192, 8192, 8192, wl.F16, wl.F16, 0, w,
-                                1 << 30) == "d256x256x32_s4_i16"
+                                1 << 30) == "d256x256x32_s4_i16w8"
 
 
 def test_ws_plan_rejects_bad_workspaces():
