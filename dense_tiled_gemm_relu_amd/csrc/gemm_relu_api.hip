@@ -23,7 +23,7 @@ using namespace gemm_relu_hip;
 
 namespace gemm_relu_hip {
 typedef hipError_t (*SpLaunchFn)(const SpArgs& args, int grid, hipStream_t stream);
-SpLaunchFn launcher_sp(int in_dt, int out_dt, int transB);   // inst_sp.hip
+SpLaunchFn launcher_sp(int in_dt, int out_dt, int transB, int variant);   // inst_sp.hip
 }
 
 namespace {
@@ -505,7 +505,9 @@ Plan make_plan_mx(const void* A, const void* SA, const void* B, const void* SB, 
 }
 
 // ---- 2:4 sparse A
-constexpr const char* kSpConfigName = "sp256x256x64_s3";
+// 2 x 4 waves (variant 1); the 2 x 2-wave variant 0 is a comparison build's, by name
+constexpr const char* kSpConfigName = "sp256x256x64_s3_w8";
+constexpr const char* kSpW4Name = "sp256x256x64_s3";
 constexpr int kSpTile = 256;
 
 Plan make_plan_sp(const void* As, const void* E, const void* B, const void* C, int64_t M,
@@ -551,7 +553,8 @@ Plan make_plan_sp(const void* As, const void* E, const void* B, const void* C, i
         p.status = GEMM_RELU_EUNSUPPORTED;
         return p;
     }
-    p.cfg = 0;
+    const char* f = std::getenv("GEMM_RELU_FORCE_CONFIG");
+    p.cfg = kComparisonBuilt && f && std::strcmp(f, kSpW4Name) == 0 ? 0 : 1;
     p.tiles_m = int(tm);
     p.tiles_n = int(tn);
     return p;
@@ -783,6 +786,10 @@ extern "C" const char* gemm_relu_configs(void)
         out += kSplitName;
         out += ',';
         out += kSpConfigName;
+        if (kComparisonBuilt) {
+            out += ',';
+            out += kSpW4Name;
+        }
         return out;
     }();
     return names.c_str();
@@ -896,7 +903,7 @@ extern "C" int gemm_relu_sp(const void* As, const void* E, const void* B, void* 
     args.panel = panel < p.tiles_m ? panel : p.tiles_m;
     args.nxcd = e.nxcd;
 
-    SpLaunchFn fn = launcher_sp(in_dtype, out_dtype, transB);
+    SpLaunchFn fn = launcher_sp(in_dtype, out_dtype, transB, p.cfg);
     if (!fn) return GEMM_RELU_EUNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (fn(args, p.tiles_m * p.tiles_n, st) != hipSuccess) return GEMM_RELU_EHIP;
@@ -915,5 +922,5 @@ extern "C" const char* gemm_relu_sp_plan(const void* As, const void* E, const vo
     if (p.status == GEMM_RELU_EINVAL) return nullptr;
     if (p.status != GEMM_RELU_OK) return "unsupported";
     if (p.empty) return "none";
-    return kSpConfigName;
+    return p.cfg == 1 ? kSpConfigName : kSpW4Name;
 }

@@ -62,11 +62,12 @@ __device__ __forceinline__ void dma4(const unsigned char* gbase, uint32_t voff, 
                  : "memory", "m0");
 }
 
-template <int IN_DT_, int OUT_DT_, bool TRANS_B_, int STAGES_ = 3> struct SpCfg {
+template <int IN_DT_, int OUT_DT_, bool TRANS_B_, int STAGES_ = 3, int WAVES_N_ = 2> struct SpCfg {
     static constexpr int IN_DT = IN_DT_, OUT_DT = OUT_DT_;
     static constexpr bool TRANS_B = TRANS_B_;
     static constexpr int BM = 256, BN = 256, BK = 64;           // BK in K (2 sparse k steps)
-    static constexpr int WAVES_M = 2, WAVES_N = 2, NWAVES = 4, NTHREADS = 256;
+    // 2 x 2 waves of 128 x 128, or 2 x 4 of 128 x 64 (two waves per SIMD)
+    static constexpr int WAVES_M = 2, WAVES_N = WAVES_N_, NWAVES = WAVES_M * WAVES_N, NTHREADS = 64 * NWAVES;
     static constexpr int STAGES = STAGES_;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N, TM = WM / 32, TN = WN / 32;
     static constexpr int KSUB = BK / 32;

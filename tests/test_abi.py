@@ -227,8 +227,8 @@ def test_sp_invalid_arguments(args):
 
 
 def test_sp_plan():
-    assert gr.gemm_relu_sp_plan(A, E_, B, C, 8192, 8192, 8192, 0, 0, 0) == "sp256x256x64_s3"
-    assert gr.gemm_relu_sp_plan(A, E_, B, C, 1, 1, 4, 1, 2, 1) == "sp256x256x64_s3"
+    assert gr.gemm_relu_sp_plan(A, E_, B, C, 8192, 8192, 8192, 0, 0, 0) == "sp256x256x64_s3_w8"
+    assert gr.gemm_relu_sp_plan(A, E_, B, C, 1, 1, 4, 1, 2, 1) == "sp256x256x64_s3_w8"
     assert gr.gemm_relu_sp_plan(A, E_, B, C, 0, 8, 8, 0, 0, 0) == "none"
     # B stored (K, N) needs a full tile of columns
     assert gr.gemm_relu_sp_plan(A, E_, B, C, 64, 255, 64, 0, 0, 0) == "unsupported"
@@ -262,7 +262,7 @@ def test_configs_lists_the_plan_names():
     for want in ("d256x256x32_s4_i16w8", "d256x256x32_s4_i16", "d256x192x32_s4_i16",
                  "d64x128x64_s4_splitk", "d256x256x32_s4_i", "d128x128x64_s3", "d64x64x64_s4",
                  "d64x32x128_s4", "d32x64x128_s4", "g128x128x64", "g64x64x64", "d128x128x64_s2",
-                 "sp256x256x64_s3"):
+                 "sp256x256x64_s3_w8"):
         assert want in names
     assert set(names) - set(COMPARISON_CONFIGS) <= set(names)
 

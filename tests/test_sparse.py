@@ -9,7 +9,8 @@ import pytest
 import dense_tiled_gemm_relu_amd as gr
 import oracle
 import workloads as wl
-from tests.helpers import check_close, from_device, fp32_sum_bound, out_tensor, unit_roundoff
+from tests.helpers import (built_configs, check_close, from_device, fp32_sum_bound, out_tensor,
+                           unit_roundoff)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,30 +27,37 @@ def _dev(x):
     return torch.from_numpy(np.ascontiguousarray(x).reshape(-1)).cuda()
 
 
-def run_sp(As, E, B, M, N, K, in_dtype, out_code, transB):
+SP = "sp256x256x64_s3_w8"
+# the plan's configuration (2 x 4 waves), and in a comparison build its 2 x 2-wave variant
+SP_CONFIGS = built_configs([SP, "sp256x256x64_s3"])
+
+
+def run_sp(As, E, B, M, N, K, in_dtype, out_code, transB, cfg=SP, monkeypatch=None):
     import torch
+    if cfg != SP:
+        monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", cfg)
     Ad, Ed, Bd = _dev(As), _dev(E), _dev(B)
     Cd = out_tensor(M, N, out_code)
-    assert gr.gemm_relu_sp_plan(Ad, Ed, Bd, Cd, M, N, K, in_dtype, out_code, transB) == \
-        "sp256x256x64_s3"
+    assert gr.gemm_relu_sp_plan(Ad, Ed, Bd, Cd, M, N, K, in_dtype, out_code, transB) == cfg
     gr.gemm_relu_sp(Ad, Ed, Bd, Cd, M, N, K, in_dtype, out_code, transB)
     torch.cuda.synchronize()
     return from_device(Cd)
 
 
+@pytest.mark.parametrize("cfg", SP_CONFIGS)
 @pytest.mark.parametrize("in_dtype", [wl.F16, wl.BF16])
 @pytest.mark.parametrize("out_code", [wl.F16, wl.BF16, wl.F32])
 @pytest.mark.parametrize("transB", [0, 1])
 @pytest.mark.parametrize("shape", [(256, 256, 64), (264, 520, 288), (301, 517, 200),
                                    (300, 300, 1100)],
                          ids=["one_tile", "tail32", "ragged", "long"])
-def test_sp_integer_bitexact(in_dtype, out_code, transB, shape):
+def test_sp_integer_bitexact(cfg, in_dtype, out_code, transB, shape, monkeypatch):
     M, N, K = shape
     if out_code == wl.BF16:
         K = 64 + 4 * (K % 3)                    # keep |C| inside bf16's exact integers
     As, E, B = wl.sp_inputs(M, N, K, in_dtype, transB, 70, int_values=True)
     ref = oracle.gemm_relu_sp_ref(As, E, B, M, N, K, in_dtype, transB)
-    got = run_sp(As, E, B, M, N, K, in_dtype, out_code, transB)
+    got = run_sp(As, E, B, M, N, K, in_dtype, out_code, transB, cfg, monkeypatch)
     assert np.array_equal(got, ref)
     assert not np.any(np.signbit(got))
 
