@@ -381,12 +381,15 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_sp_relu_kernel(SpArgs arg
 #pragma unroll
         for (int j = 0; j < TN; ++j) read_b(0, 0, j);
     }
-    // one step; STEADY: the stage S-1 ahead exists (no run-time checks)
-    auto step = [&](int t, auto steady_tag) {
+    // one step; STEADY: the stage S-1 ahead exists (no run-time checks).
+    // ring: the step's ring position, t mod S, as a compile-time constant in
+    // the unrolled steady loop (so that every LDS address of the step is a
+    // per-lane base plus a constant), or at run time
+    auto step = [&](int t, auto steady_tag, auto ring) {
         constexpr bool STEADY = decltype(steady_tag)::value;
-        const int stage = t % S;
+        const int stage = ring;
         const bool loads = STEADY || t + S - 1 < nk;
-        const int ld_stage = (t + S - 1) % S;
+        const int ld_stage = stage == 0 ? S - 1 : stage - 1;
 #pragma unroll
         for (int s = 0; s < KSUB; ++s) {
             int next_stage = -1, next_s = 0;
@@ -399,7 +402,7 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_sp_relu_kernel(SpArgs arg
                 else
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
                 barrier_lds();
-                next_stage = (t + 1) % S;
+                next_stage = stage + 1 == S ? 0 : stage + 1;
             }
             const AFrags& f = fa[s & 1];
 #pragma unroll
@@ -422,8 +425,11 @@ __global__ void __launch_bounds__(C::NTHREADS, 1) gemm_sp_relu_kernel(SpArgs arg
         }
     };
     const int t_steady = nk - (S - 1) > 0 ? nk - (S - 1) : 0;
-    for (int t = 0; t < t_steady; ++t) step(t, std::integral_constant<bool, true>{});
-    for (int t = t_steady; t < nk; ++t) step(t, std::integral_constant<bool, false>{});
+    int t = 0;
+    for (; t + S <= t_steady; t += S)
+        static_for<0, S>([&](auto r) { step(t + decltype(r)::value, std::integral_constant<bool, true>{}, r); });
+    for (; t < t_steady; ++t) step(t, std::integral_constant<bool, true>{}, t % S);
+    for (; t < nk; ++t) step(t, std::integral_constant<bool, false>{}, t % S);
     if (K % BK != 0) {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         barrier_lds();
