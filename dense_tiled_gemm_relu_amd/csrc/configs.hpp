@@ -39,6 +39,8 @@ enum ConfigId : int {
     CFG_D64x128x128_S3_SPLITK,
     CFG_D64x128x64_S3_SPLITK,
     CFG_D256x256x32_S4_I16W8,
+    CFG_D128x384x32_S4_I16W8,
+    CFG_D256x256x32_S4_I16W8SK,
     CFG_COUNT
 };
 
@@ -82,6 +84,8 @@ inline const ConfigInfo& config_info(int id)
         {"d64x128x128_s3_splitk", 64, 128, true, false, false, true, 128, 1},
         {"d64x128x64_s3_splitk", 64, 128, true, false, false, true, 64, 2},
         {"d256x256x32_s4_i16w8", 256, 256, true},
+        {"d128x384x32_s4_i16w8", 128, 384, true},
+        {"d256x256x32_s4_i16w8sk", 256, 256, true, false, true},
     };
     return table[id];
 }
@@ -106,7 +110,8 @@ inline constexpr bool comparison_config(int id)
            id == CFG_D256x256x32_S4_ISK || id == CFG_D256x256x32_S4_W8I ||
            id == CFG_D256x256x32_S5_W8I || id == CFG_D256x256x64_S2_W8 || id == CFG_D256x128x64_S2 ||
            id == CFG_D256x256x32_S4_I16P || id == CFG_D64x256x64_S3_SPLITK ||
-           id == CFG_D64x128x128_S3_SPLITK || id == CFG_D64x128x64_S3_SPLITK;
+           id == CFG_D64x128x128_S3_SPLITK || id == CFG_D64x128x64_S3_SPLITK ||
+           id == CFG_D128x384x32_S4_I16W8 || id == CFG_D256x256x32_S4_I16W8SK;
 }
 
 // Whether this build of the library holds kernels of configuration id.
@@ -170,6 +175,28 @@ template <int IN, int OUT> struct CfgOf<IN, OUT, true, CFG_D256x192x32_S4_I16> {
 // of 4096 x 7168 x 4096 bf16 4.7 %).
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I16W8> {
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 4, 4, true, true, 16>;
+};
+// Its narrower last round in a two-region grid (B stored (N,K); comparison
+// build): 128 x 384 tiles of eight waves side by side (waves of 128 x 48, 8 x 3
+// blocks), the same 128 KiB ring and one A and three B copies per thread a
+// step.  A 256 x 192 tile has no whole copy count over 512 threads (768 B
+// chunks a step); this one covers the same 49152 outputs.  Measured on
+// MI355X (bf16 4096 x 7168 x 4096, fp32 C, one box): the eight-wave grid
+// 187.7 us against the four-wave one's 182.4; its round runs at 0.74 of the
+// 256 x 256 tile's rate per flop (each A fragment is read by all eight waves).
+template <int IN, int OUT> struct CfgOf<IN, OUT, true, CFG_D128x384x32_S4_I16W8> {
+    using type = Cfg<IN, OUT, true, 128, 384, bk_of<IN, 32>, 1, 8, 4, true, true, 16>;
+};
+// The eight-wave tile with its last, partial round split along K (stream-K;
+// comparison build, gemm_relu_ws with GEMM_RELU_FORCE_CONFIG only): whole
+// rounds of one workgroup per tile, then one workgroup per CU taking an equal
+// share of the remaining tiles' K steps, with fp32 partials in the caller's
+// workspace.  Measured on MI355X (one box): 4097 x 3001 x 5003 195.4 us against
+// 125.5 for whole tiles (130.0 with one whole tile per unit, so the exchange of
+// the 256 KiB partials costs ~65 us: ~190 MiB of device-scope traffic at
+// ~3 TB/s), bf16 4096 x 7168 x 4096 219.7 against 182.4.
+template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I16W8SK> {
+    using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 4, 4, true, true, 16, false, true>;
 };
 template <int IN, int OUT, bool TB> struct CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_I16P> {
     using type = Cfg<IN, OUT, TB, 256, 256, bk_of<IN, 32>, 2, 2, 4, true, true, 16, true>;
@@ -290,13 +317,16 @@ LaunchFn launcher_mx_e4m3(int out_dt, int cfg);
 LaunchFn launcher_mx_e5m2(int out_dt, int cfg);
 LaunchFn launcher_mx_e2m1(int out_dt, int cfg);
 // the 16x16-block interleaved tiles for a 16-bit input type (inst_i16.hip):
-// 256 x 256 (either B layout), 256 x 192 (B stored (N,K)), and the two-region
-// grid of both (B stored (N,K))
+// 256 x 256 with four or eight waves (either B layout); 256 x 192 (four waves)
+// and 128 x 384 (eight waves) for B stored (N,K); and the two-region grids
+// (B stored (N,K)) whose narrower round is cfg2, one of those two
 LaunchFn launcher_i16(int in_dt, int out_dt, bool transB);
 LaunchFn launcher_i16_192(int in_dt, int out_dt);
+LaunchFn launcher_i16_384(int in_dt, int out_dt);
 LaunchFn launcher_i16p(int in_dt, int out_dt, bool transB);
 LaunchFn launcher_i16w8(int in_dt, int out_dt, bool transB);
-LaunchFn launcher_i16_2r(int in_dt, int out_dt);
+LaunchFn launcher_i16w8sk(int in_dt, int out_dt, bool transB);
+LaunchFn launcher_i16_2r(int in_dt, int out_dt, int cfg2);
 
 // Configurations built for 8-bit inputs: the ones plan selection can choose
 // (the 16-bit comparison variants are not instantiated for them).
@@ -337,6 +367,10 @@ inline bool fp8_config(int cfg)
             return launcher_i16p(IN, OUT, TB);                                             \
         case CFG_D256x256x32_S4_I16W8:                                                     \
             return launcher_i16w8(IN, OUT, TB);                                            \
+        case CFG_D256x256x32_S4_I16W8SK:                                                   \
+            return launcher_i16w8sk(IN, OUT, TB);                                          \
+        case CFG_D128x384x32_S4_I16W8:                                                     \
+            return TB ? launcher_i16_384(IN, OUT) : nullptr;                               \
         case CFG_D256x256x32_S4_IP:                                                        \
             return comparison_launcher<typename CfgOf<IN, OUT, TB, CFG_D256x256x32_S4_IP>::type>(); \
         case CFG_D256x256x32_S4_ISK:                                                       \

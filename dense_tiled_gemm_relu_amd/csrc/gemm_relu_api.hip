@@ -219,16 +219,26 @@ bool direct_fits(int id, int64_t N, int64_t K, int transB)
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr const char* kSplitName = "d256x256x32_s4_i16+d256x192x32_s4_i16";
+constexpr const char* kSplitName8 = "d256x256x32_s4_i16w8+d128x384x32_s4_i16w8";
 
 // ---- two-region grid (16-bit inputs, B stored (N,K)): when whole rounds of
 // 256x256 tiles over the CUs leave a partial round, the first `c` tile columns
 // (c * tiles_m = whole rounds) stay 256x256 and the remaining columns are cut
-// into 256x192 tiles, at most one round of them.  Measured efficiency of the
-// 256x192 tile per flop relative to 256x256 (kSplitEff) prices that round.
+// into narrower tiles of 3/4 the area, at most one round of them: 256x192
+// tiles of four waves, in a grid whose first region is the four-wave 256x256
+// tile, or (`eight`, only when forced) 128x384 tiles of eight waves behind the
+// eight-wave 256x256 tile.  Measured on MI355X (bf16 4096x7168x4096, fp32 C)
+// the four-wave grid takes 182.4 us, the eight-wave one 187.7 and eight-wave
+// whole tiles 186.4: the 128x384 round runs at 0.74 of the 256x256 tile's
+// rate per flop (each A fragment read by all eight waves), the 256x192 one at
+// 0.81.  kSplitEff prices that round.
 constexpr double kSplitEff = 0.93;
 
-bool plan_split(Plan& p, int64_t M, int64_t N, int forced_cols)
+bool plan_split(Plan& p, int64_t M, int64_t N, int forced_cols, bool eight)
 {
+    const int cfg2 = eight ? CFG_D128x384x32_S4_I16W8 : CFG_D256x192x32_S4_I16;
+    if (!config_built(cfg2)) return false;
+    const int64_t bm2 = config_info(cfg2).bm, bn2 = config_info(cfg2).bn;
     const int64_t tm = p.tiles_m, tn = p.tiles_n, tiles = tm * tn;
     int64_t c = -1;
     if (forced_cols >= 0) {
@@ -240,25 +250,27 @@ bool plan_split(Plan& p, int64_t M, int64_t N, int forced_cols)
     }
     if (c <= 0 || c >= tn) return false;
     const int64_t n_org = c * 256, w2 = N - n_org;
-    const int64_t tn2 = ceil_div(w2, 192), tiles2 = ceil_div(M, 256) * tn2;
+    const int64_t tn2 = ceil_div(w2, bn2), tiles2 = ceil_div(M, bm2) * tn2;
     if (forced_cols < 0) {
         const double plain = double(ceil_div(tiles, kNumCUs));
         const double split = double(c * tm / kNumCUs) +
-                             double(ceil_div(tiles2, kNumCUs)) * (192.0 / 256.0) / kSplitEff;
+                             double(ceil_div(tiles2, kNumCUs)) * (double(bm2 * bn2) / 65536.0) / kSplitEff;
         if (split >= 0.95 * plain) return false;
     }
     if (c * tm + tiles2 > INT32_MAX) return false;
-    p.cfg2 = CFG_D256x192x32_S4_I16;
+    p.cfg2 = cfg2;
     p.tiles1 = int(c * tm);
     p.tiles_n = int(c);
-    p.tiles_m2 = int(ceil_div(M, 256));
+    p.tiles_m2 = int(ceil_div(M, bm2));
     p.tiles_n2 = int(tn2);
     p.n_org2 = int(n_org);
     return true;
 }
 
+// ptrs = false: the choice for the sizes and codes alone (workspace queries),
+// with no operand pointers to check.
 Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
-               int in_dt, int out_dt, int transB, const Env& e, bool sk_ok = true)
+               int in_dt, int out_dt, int transB, const Env& e, bool sk_ok = true, bool ptrs = true)
 {
     Plan p;
     const int64_t lim = INT32_MAX;
@@ -280,19 +292,19 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     const uint64_t a_bytes = uint64_t(M) * uint64_t(K) * in_bytes;
     const uint64_t b_bytes = uint64_t(K) * uint64_t(N) * in_bytes;
     const uint64_t c_bytes = uint64_t(M) * uint64_t(N) * uint64_t(elem_bytes(out_dt));
-    if ((a_bytes && !A) || (b_bytes && !B) || !C) {
+    if (ptrs && ((a_bytes && !A) || (b_bytes && !B) || !C)) {
         p.status = GEMM_RELU_EINVAL;
         return p;
     }
-    if ((reinterpret_cast<uintptr_t>(A) & uintptr_t(in_bytes - 1)) ||
-        (reinterpret_cast<uintptr_t>(B) & uintptr_t(in_bytes - 1)) ||
-        (reinterpret_cast<uintptr_t>(C) & uintptr_t(elem_bytes(out_dt) - 1))) {
+    if (ptrs && ((reinterpret_cast<uintptr_t>(A) & uintptr_t(in_bytes - 1)) ||
+                 (reinterpret_cast<uintptr_t>(B) & uintptr_t(in_bytes - 1)) ||
+                 (reinterpret_cast<uintptr_t>(C) & uintptr_t(elem_bytes(out_dt) - 1)))) {
         p.status = GEMM_RELU_EINVAL;
         return p;
     }
     const uintptr_t ua = reinterpret_cast<uintptr_t>(A), ub = reinterpret_cast<uintptr_t>(B),
                     uc = reinterpret_cast<uintptr_t>(C);
-    if (overlaps(uc, c_bytes, ua, a_bytes) || overlaps(uc, c_bytes, ub, b_bytes)) {
+    if (ptrs && (overlaps(uc, c_bytes, ua, a_bytes) || overlaps(uc, c_bytes, ub, b_bytes))) {
         p.status = GEMM_RELU_EINVAL;
         return p;
     }
@@ -305,12 +317,14 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     auto usable = [&](int id) {
         return id != CFG_D256x128x64_S2 &&             // built for block-scaled inputs only
                !config_info(id).splitk &&               // needs a workspace (plan_splitk)
-               (id != CFG_D256x192x32_S4_I16 || transB) &&    // built for B stored (N,K) only
+               ((id != CFG_D256x192x32_S4_I16 && id != CFG_D128x384x32_S4_I16W8) ||
+                transB) &&                              // built for B stored (N,K) only
                // the persistent 16x16-block stream: whole 256x256 tiles inside
                // the matrix, whole K steps, at least a full ring of them
                (id != CFG_D256x256x32_S4_I16P || (M >= 256 && N >= 256 && K % 32 == 0 && K >= 128)) &&
                config_built(id) &&
                (id != CFG_D256x256x32_S4_ISK || sk_possible) &&
+               id != CFG_D256x256x32_S4_I16W8SK &&      // needs a workspace (plan_streamk)
                direct_fits(id, N, K, transB) && (!fp8_input(in_dt) || fp8_config(id));
     };
     // Estimated time of a direct configuration, per K: rounds of workgroups
@@ -348,9 +362,11 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
                 cfg = id;
         if (cfg < 0) cfg = tiles(CFG_G128x128x64) >= kNumCUs ? CFG_G128x128x64 : CFG_G64x64x64;
     }
-    // GEMM_RELU_SPLIT_COLS=<c> > 0 forces the two-region grid (on the 256x256
-    // tile) wherever it can be built
-    if (e.split_cols > 0 && transB && usable(CFG_D256x256x32_S4_I16)) cfg = CFG_D256x256x32_S4_I16;
+    // GEMM_RELU_SPLIT_COLS=<c> > 0 forces the two-region grid wherever it can
+    // be built: behind the four-wave 256x256 tile, or behind the eight-wave one
+    // when that is the forced configuration
+    if (e.split_cols > 0 && transB && usable(CFG_D256x256x32_S4_I16) && forced != CFG_D256x256x32_S4_I16W8)
+        cfg = CFG_D256x256x32_S4_I16;
     const int64_t tm = ceil_div(M, config_info(cfg).bm), tn = ceil_div(N, config_info(cfg).bn);
     if (tm * tn > lim) {
         p.status = GEMM_RELU_EUNSUPPORTED;
@@ -364,7 +380,8 @@ Plan make_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N
     // forces (or, with 0, forbids) it
     if ((cfg == CFG_D256x256x32_S4_I16 || cfg == CFG_D256x256x32_S4_I16W8) && transB && e.split_cols != 0 &&
         (e.split_cols > 0 || forced < 0))
-        plan_split(p, M, N, e.split_cols > 0 ? e.split_cols : -1);
+        plan_split(p, M, N, e.split_cols > 0 ? e.split_cols : -1,
+                   e.split_cols > 0 && forced == CFG_D256x256x32_S4_I16W8);
     if (config_info(cfg).streamk) {
         const SkSplit sp = sk_split(tm * tn, sk_iters, e.sk_units);
         p.dp_tiles = sp.dp_tiles;
@@ -424,6 +441,42 @@ bool plan_splitk(Plan& p, int64_t M, int64_t N, int64_t K, int in_dt, int transB
     p.tiles_n = int(ceil_div(N, ci.bn));
     p.splits = int(splits);
     p.split_steps = int(split_steps);
+    p.ws_need = need;
+    return true;
+}
+
+// ---- stream-K with a workspace (gemm_relu_ws; the eight-wave tile's
+// comparison configuration, taken only when GEMM_RELU_FORCE_CONFIG names it):
+// whole rounds keep one workgroup per tile and the rest of the tiles' K steps
+// are shared equally by one workgroup per CU, or GEMM_RELU_SK_UNITS of them.
+// Each split tile has an arrival counter in the workspace's first 4096 bytes;
+// the fp32 partials follow, two 256 KiB slots per unit.  Measured on MI355X
+// it loses to whole tiles wherever it applies (the exchange of 256 KiB
+// partials through device-coherent memory costs more than the partly empty
+// last round), so plan selection never takes it.
+constexpr uint64_t kSkSlotFloats = 256 * 256;
+
+bool plan_streamk(Plan& p, int64_t M, int64_t N, int64_t K, int in_dt, int transB, uint64_t ws_bytes,
+                  const Env& e)
+{
+    const int id = CFG_D256x256x32_S4_I16W8SK;
+    if (e.force_cfg != id) return false;
+    if (ws_bytes == 0 || fp8_input(in_dt) || !config_built(id) || !direct_fits(id, N, K, transB)) return false;
+    const int64_t tiles = ceil_div(M, 256) * ceil_div(N, 256);
+    const int64_t iters = ceil_div(K, 32);
+    const int64_t rest = tiles % kNumCUs;
+    if (rest == 0 || tiles > INT32_MAX) return false;
+    const SkSplit sp = sk_split(tiles, iters, e.sk_units);
+    if (sp.units < 1) return false;
+    if (rest > int64_t(kSplitkFlagBytes / 4)) return false;
+    const uint64_t need = kSplitkFlagBytes + 2 * uint64_t(sp.units) * kSkSlotFloats * 4;
+    if (need > ws_bytes) return false;
+    p.cfg = id;
+    p.cfg2 = -1;
+    p.tiles_m = int(ceil_div(M, 256));
+    p.tiles_n = int(ceil_div(N, 256));
+    p.dp_tiles = sp.dp_tiles;
+    p.sk_units = sp.units;
     p.ws_need = need;
     return true;
 }
@@ -609,7 +662,8 @@ Plan make_plan_ws(const void* A, const void* B, const void* C, int64_t M, int64_
         p.status = GEMM_RELU_EINVAL;
         return p;
     }
-    if (ws && ws_bytes) plan_splitk(p, M, N, K, in_dt, transB, ws_bytes, e);
+    if (ws && ws_bytes && !plan_splitk(p, M, N, K, in_dt, transB, ws_bytes, e))
+        plan_streamk(p, M, N, K, in_dt, transB, ws_bytes, e);
     return p;
 }
 
@@ -624,7 +678,9 @@ int run_gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, i
     if (dev != GEMM_RELU_OK) return dev;
     hipStream_t st = static_cast<hipStream_t>(stream);
     unsigned char* ws = nullptr;
-    if (config_info(p.cfg).streamk) {
+    if (config_info(p.cfg).streamk && p.ws_need > 0) {
+        ws = static_cast<unsigned char*>(workspace);       // the caller's (plan_streamk)
+    } else if (config_info(p.cfg).streamk) {
         int d = 0;
         if (hipGetDevice(&d) != hipSuccess) return GEMM_RELU_EHIP;
         ws = sk_workspace(d, st);
@@ -648,7 +704,7 @@ int run_gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, i
     args.KB = 0;
     if (config_info(p.cfg).streamk) {
         args.flags = reinterpret_cast<unsigned*>(ws);
-        args.ws = reinterpret_cast<float*>(ws + kSkFlagBytes);
+        args.ws = reinterpret_cast<float*>(ws + (p.ws_need > 0 ? kSplitkFlagBytes : kSkFlagBytes));
         args.dp_tiles = p.dp_tiles;
         args.sk_units = p.sk_units;
     }
@@ -659,7 +715,7 @@ int run_gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, i
         args.split_steps = p.split_steps;
     }
 
-    LaunchFn fn = p.cfg2 >= 0 ? launcher_i16_2r(in_dtype, out_dtype)
+    LaunchFn fn = p.cfg2 >= 0 ? launcher_i16_2r(in_dtype, out_dtype, p.cfg2)
                               : pick_launcher(in_dtype, out_dtype, transB, p.cfg);
     if (!fn) return GEMM_RELU_EUNSUPPORTED;
     const int tiles = p.tiles_m * p.tiles_n;
@@ -768,8 +824,12 @@ extern "C" int64_t gemm_relu_workspace_size(int64_t M, int64_t N, int64_t K, int
 {
     if (!codes_and_sizes_ok(M, N, K, in_dtype, out_dtype, transB)) return GEMM_RELU_EINVAL;
     if (M == 0 || N == 0) return 0;
+    const Env e = env();
     Plan p;
-    if (!plan_splitk(p, M, N, K, in_dtype, transB, UINT64_MAX, env())) return 0;
+    if (plan_splitk(p, M, N, K, in_dtype, transB, UINT64_MAX, e)) return int64_t(p.ws_need);
+    // stream-K (forced only) on top of what plan selection takes without one
+    p = make_plan(nullptr, nullptr, nullptr, M, N, K, in_dtype, out_dtype, transB, e, true, false);
+    if (!plan_streamk(p, M, N, K, in_dtype, transB, UINT64_MAX, e)) return 0;
     return int64_t(p.ws_need);
 }
 
@@ -784,6 +844,10 @@ extern "C" const char* gemm_relu_configs(void)
             }
         out += ',';
         out += kSplitName;
+        if (config_built(CFG_D128x384x32_S4_I16W8)) {
+            out += ',';
+            out += kSplitName8;
+        }
         out += ',';
         out += kSpConfigName;
         if (kComparisonBuilt) {
@@ -807,6 +871,12 @@ extern "C" const char* gemm_relu_strerror(int status)
     }
 }
 
+static const char* plan_name(const Plan& p)
+{
+    if (p.cfg2 < 0) return config_info(p.cfg).name;
+    return p.cfg2 == CFG_D128x384x32_S4_I16W8 ? kSplitName8 : kSplitName;
+}
+
 extern "C" const char* gemm_relu_plan(const void* A, const void* B, const void* C, int64_t M,
                                       int64_t N, int64_t K, int in_dtype, int out_dtype,
                                       int transB)
@@ -815,7 +885,7 @@ extern "C" const char* gemm_relu_plan(const void* A, const void* B, const void* 
     if (p.status == GEMM_RELU_EINVAL) return nullptr;
     if (p.status != GEMM_RELU_OK) return "unsupported";
     if (p.empty) return "none";
-    return p.cfg2 >= 0 ? kSplitName : config_info(p.cfg).name;
+    return plan_name(p);
 }
 
 extern "C" const char* gemm_relu_ws_plan(const void* A, const void* B, const void* C, int64_t M, int64_t N,
@@ -827,7 +897,7 @@ extern "C" const char* gemm_relu_ws_plan(const void* A, const void* B, const voi
     if (p.status == GEMM_RELU_EINVAL) return nullptr;
     if (p.status != GEMM_RELU_OK) return "unsupported";
     if (p.empty) return "none";
-    return p.cfg2 >= 0 ? kSplitName : config_info(p.cfg).name;
+    return plan_name(p);
 }
 
 extern "C" int gemm_relu_mx(const void* A, const void* SA, const void* B, const void* SB, void* C,

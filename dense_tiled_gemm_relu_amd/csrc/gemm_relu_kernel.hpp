@@ -1110,15 +1110,17 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
                 // one: B 0..3 after the first half, A blocks 2k, 2k+1 after
                 // region 4 + k, B 4..7 at the end.  Every read then has at
                 // least four regions (32 MFMAs) before its first use.
-                // Narrower tiles (TN = 6: 256 x 192) keep the eight regions, with
-                // TN / 2 B blocks a half and one copy in each of the first
-                // LOADS_PER_STAGE regions.
-                static_assert(TM == 8 && TN % 2 == 0 && TN <= 8 && KSUB == 1 &&
+                // Narrower tiles (TN = 6: 256 x 192; TN = 3: waves of 128 x 48)
+                // keep the eight regions, with TN / 2 B blocks in the first half
+                // and the rest in the second, and one copy in each of the first
+                // LOADS_PER_STAGE regions.  With TN = 3 every read still has
+                // at least three regions (six MFMAs) before its first use.
+                static_assert(TM == 8 && TN >= 2 && TN <= 8 && KSUB == 1 &&
                                   C::LOADS_PER_STAGE <= 8,
                               "in-place 16x16 steps: 8 x TN blocks, at most one copy per region");
                 constexpr int QA = TM * FRAG_CH;
                 constexpr int QB = C::TRANS_B ? FRAG_CH : TR_READS;     // reads per B block
-                constexpr int HB = TN / 2;                                // B blocks per half
+                constexpr int HB0 = TN / 2, HB1 = TN - HB0;               // B blocks per half
                 for (; t < t_steady; ++t) {
                     const int ld_stage = (t + S - 1) % S;
                     const int ld_k0 = (t + S - 1) * BK;
@@ -1146,17 +1148,18 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
                         else if constexpr (r < C::LOADS_PER_STAGE)
                             dma16(gb, b_src[r - APT], lsb + ((r - APT) * C::NWAVES + wave) * 1024);
                         constexpr int half = r / 4, i0 = 2 * (r % 4);
+                        constexpr int j0 = half ? HB0 : 0, hb = half ? HB1 : HB0;
 #pragma unroll
                         for (int di = 0; di < 2; ++di)
 #pragma unroll
-                            for (int jj = 0; jj < HB; ++jj) {
+                            for (int jj = 0; jj < hb; ++jj) {
                                 const int i = i0 + di;
-                                const int j = HB * half + (di ? HB - 1 - jj : jj);
+                                const int j = j0 + (di ? hb - 1 - jj : jj);
                                 acc[i][j] = In::mfma(fr[0].b[j], fr[0].a[i], acc[i][j]);
                             }
                         if constexpr (r == 3 || r == 7) {
 #pragma unroll
-                            for (int q = QA + HB * half * QB; q < QA + (HB * half + HB) * QB; ++q)
+                            for (int q = QA + j0 * QB; q < QA + (j0 + hb) * QB; ++q)
                                 read_op(rd_stage, 0, q, fr[0]);
                         }
                         if constexpr (r >= 4) {
@@ -1270,39 +1273,41 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
     // tile from the sum of all of them, read back in piece order.  (Summing
     // from memory leaves the accumulators to the matrix instructions alone:
     // vector adds into them make the compiler split them over both register
-    // files and shuffle them every main-loop step.)
+    // files and shuffle them every main-loop step.)  As for the K split below,
+    // the partials are written and read as device-scope atomics and a piece
+    // counts itself in only once its stores have completed, so no L2
+    // write-back or invalidation is needed.  Partial layout: value e of group
+    // v = (i TN + j) NQ + q of thread tid at float (4 v + e) NTHREADS + tid of
+    // the slot (each dword store of a wave is 256 consecutive bytes).
     constexpr int NQ = NACC / 4;                 // 4-float groups per block
     bool from_partials = false;
-    // partial layout: group v = (i TN + j) NQ + q of thread tid at float4 index
-    // v NTHREADS + tid (each wave writes and reads whole 1 KiB lines)
     auto slot_of = [&](int p) {
         const GR_LDS SkPiece* pc = &sk->pc;
         const int s = p == 0 ? pc->slot0 : 2 * (pc->first + p);
-        return reinterpret_cast<f32x4_t*>(args.ws + (size_t)s * (BM * BN)) + tid;
+        return args.ws + (size_t)s * (BM * BN) + tid;
     };
     if constexpr (C::STREAMK) {
         const GR_LDS SkPiece* pc = &sk->pc;
         if (pc->count > 1) {
-            f32x4_t* own = slot_of(pc->pos);
+            float* own = slot_of(pc->pos);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
-                    for (int q = 0; q < NQ; ++q) {
-                        const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                           acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                        own[((i * TN + j) * NQ + q) * C::NTHREADS] = v;
-                    }
-            // every wave's stores reach device scope before the count is taken
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-            __builtin_amdgcn_s_barrier();
+                    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            __hip_atomic_store(own + (((i * TN + j) * NQ + q) * 4 + e) * C::NTHREADS,
+                                               acc[i][j][4 * q + e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // this wave's stores have completed, then every wave's
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            asm volatile("s_barrier" ::: "memory");
             if (tid == 0)
                 sk->arrived = (int)__hip_atomic_fetch_add(args.flags + pc->tile, 1u, __ATOMIC_RELAXED,
                                                           __HIP_MEMORY_SCOPE_AGENT);
             barrier_lds();
             if (sk->arrived + 1 != pc->count) return;     // a later piece completes the tile
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             if (tid == 0)
                 __hip_atomic_store(args.flags + pc->tile, 0u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
@@ -1487,17 +1492,22 @@ __device__ __forceinline__ void gemm_relu_tile(const KernelArgs& args, int wg,
             constexpr int NV = TM * TN * NQ, VB = 16;
             static_assert(NV % VB == 0, "partial load batches");
             const int count = sk->pc.count;
+            auto load_batch = [&](int p, int c, f32x4_t* x) {
+                const float* sp = slot_of(p);
+#pragma unroll
+                for (int k = 0; k < VB; ++k)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        x[k][e] = __hip_atomic_load(sp + (4 * (c + k) + e) * C::NTHREADS, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+            };
 #pragma unroll
             for (int c = 0; c < NV; c += VB) {
-                const f32x4_t* s0 = slot_of(0);
                 f32x4_t sum[VB];
-#pragma unroll
-                for (int k = 0; k < VB; ++k) sum[k] = s0[(c + k) * C::NTHREADS];
+                load_batch(0, c, sum);
                 for (int p = 1; p < count; ++p) {
-                    const f32x4_t* sp = slot_of(p);
                     f32x4_t x[VB];
-#pragma unroll
-                    for (int k = 0; k < VB; ++k) x[k] = sp[(c + k) * C::NTHREADS];
+                    load_batch(p, c, x);
 #pragma unroll
                     for (int k = 0; k < VB; ++k) sum[k] += x[k];
                 }

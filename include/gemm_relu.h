@@ -109,7 +109,11 @@ int gemm_relu(const void* A, const void* B, void* C, int64_t M, int64_t N, int64
  * Used for skinny shapes (M <= 64 with few output tiles), whose (K,N) B would
  * otherwise be read as narrow column slabs, which HBM serves slowly: each part
  * reads a contiguous run of many K rows instead.  Other shapes, or a workspace
- * smaller than gemm_relu_workspace_size, run exactly as gemm_relu.
+ * smaller than gemm_relu_workspace_size, run exactly as gemm_relu.  (A library
+ * built with the comparison configurations also splits the last, partial
+ * round of 256x256 tiles this way when GEMM_RELU_FORCE_CONFIG names
+ * d256x256x32_s4_i16w8sk: the same workspace layout, two 256 KiB partial
+ * tiles per workgroup of that round.)
  *
  * Arguments as for gemm_relu, plus
  *   workspace        device pointer, 256-byte aligned, disjoint from A, B and

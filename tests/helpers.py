@@ -50,7 +50,8 @@ COMPARISON_CONFIGS = ("d256x256x64_s2", "d256x256x32_s4", "d256x256x32_s5", "d25
                       "d256x256x32_s4_ip", "d256x256x32_s4_isk", "d256x256x32_s4_w8i",
                       "d256x256x32_s5_w8i", "d256x256x64_s2_w8", "d256x128x64_s2",
                       "d256x256x32_s4_i16p", "d64x256x64_s3_splitk", "d64x128x128_s3_splitk",
-                      "d64x128x64_s3_splitk", "sp256x256x64_s3")
+                      "d64x128x64_s3_splitk", "sp256x256x64_s3", "d128x384x32_s4_i16w8",
+                      "d256x256x32_s4_i16w8+d128x384x32_s4_i16w8", "d256x256x32_s4_i16w8sk")
 
 
 def built_configs(names):

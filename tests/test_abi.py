@@ -260,6 +260,7 @@ def test_configs_lists_the_plan_names():
     names = gr.gemm_relu_configs()
     assert len(names) == len(set(names))
     for want in ("d256x256x32_s4_i16w8", "d256x256x32_s4_i16", "d256x192x32_s4_i16",
+                 "d256x256x32_s4_i16+d256x192x32_s4_i16",
                  "d64x128x64_s4_splitk", "d256x256x32_s4_i", "d128x128x64_s3", "d64x64x64_s4",
                  "d64x32x128_s4", "d32x64x128_s4", "g128x128x64", "g64x64x64", "d128x128x64_s2",
                  "sp256x256x64_s3_w8"):
@@ -301,14 +302,19 @@ def test_streamk_selection(monkeypatch):
 
 
 SPLIT = "d256x256x32_s4_i16+d256x192x32_s4_i16"
+SPLIT8 = "d256x256x32_s4_i16w8+d128x384x32_s4_i16w8"
 
 
 def test_two_region_grid_selection(monkeypatch):
     """16-bit inputs with B stored (N,K): when whole rounds of 256x256 tiles
     leave a partial round, the tile columns past those rounds are cut into
-    256x192 tiles (one launch, one narrower last round).  (K,N) B, whole
-    rounds, 8-bit inputs and forced configurations keep plain tiles;
-    GEMM_RELU_SPLIT_COLS forces or forbids the split."""
+    narrower tiles of 3/4 the area (one launch, one narrower last round):
+    256x192 four-wave tiles behind the four-wave 256x256 tile, or, when the
+    eight-wave 256x256 tile is forced, 128x384 eight-wave tiles behind it (a
+    comparison configuration).  (K,N) B, whole rounds, 8-bit inputs and forced
+    configurations keep plain tiles; GEMM_RELU_SPLIT_COLS forces or forbids
+    the split."""
+    eight = bool(built_configs([SPLIT8]))
     assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == SPLIT
     assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 0, 0, 1) == SPLIT
     assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 0) == "d256x256x32_s4_i16w8"
@@ -319,10 +325,20 @@ def test_two_region_grid_selection(monkeypatch):
     monkeypatch.setenv("GEMM_RELU_SPLIT_COLS", "1")
     assert gr.gemm_relu_plan(A, B, C, 512, 520, 64, 0, 0, 1) == SPLIT
     assert gr.gemm_relu_plan(A, B, C, 512, 256, 64, 0, 0, 1) == "d256x256x32_s4_i16"
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x256x32_s4_i16w8")
+    assert gr.gemm_relu_plan(A, B, C, 512, 520, 64, 0, 0, 1) == (SPLIT8 if eight else "d256x256x32_s4_i16w8")
+    assert gr.gemm_relu_plan(A, B, C, 512, 256, 64, 0, 0, 1) == "d256x256x32_s4_i16w8"
     monkeypatch.delenv("GEMM_RELU_SPLIT_COLS")
+    assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == "d256x256x32_s4_i16w8"
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x256x32_s4_i16")
     assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == "d256x256x32_s4_i16"
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x192x32_s4_i16")
     assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == "d256x192x32_s4_i16"
+    if eight:
+        monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d128x384x32_s4_i16w8")
+        assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 1) == "d128x384x32_s4_i16w8"
+        # the narrower tiles are built for B stored (N,K) only
+        assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 0) == "d256x256x32_s4_i16w8"
+    monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", "d256x192x32_s4_i16")
     # the 256x192 tile is built for B stored (N,K) only
     assert gr.gemm_relu_plan(A, B, C, 4096, 7168, 4096, 1, 2, 0) == "d256x256x32_s4_i16w8"

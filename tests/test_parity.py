@@ -20,11 +20,15 @@ from tests.helpers import (built_configs, check_close, from_device, fp32_sum_bou
 
 pytestmark = pytest.mark.gpu
 
-# the two-region grid (256x256 tiles over the first tile columns, 256x192 over
-# the rest), forced here with GEMM_RELU_SPLIT_COLS=1 (one 256-wide column first)
+# the two-region grids (256x256 tiles over the first tile columns, narrower
+# tiles over the rest), forced here with GEMM_RELU_SPLIT_COLS=1 (one 256-wide
+# column first): four waves with 256x192 tiles, or eight waves with 128x384
+# ones (GEMM_RELU_FORCE_CONFIG names the eight-wave 256x256 tile)
 SPLIT = "d256x256x32_s4_i16+d256x192x32_s4_i16"
+SPLIT8 = "d256x256x32_s4_i16w8+d128x384x32_s4_i16w8"
+SPLITS = {SPLIT: None, SPLIT8: "d256x256x32_s4_i16w8"}
 # built for 16-bit inputs with B stored (N,K) only
-NK_ONLY = {"d256x192x32_s4_i16", SPLIT}
+NK_ONLY = {"d256x192x32_s4_i16", "d128x384x32_s4_i16w8", SPLIT, SPLIT8}
 # the persistent 16x16-block stream: whole 256x256 tiles (M, N >= 256), K a
 # multiple of 32 with at least 4 steps
 PSTREAM = "d256x256x32_s4_i16p"
@@ -32,7 +36,8 @@ DIRECT = built_configs(["d256x256x64_s2", "d256x256x32_s4", "d256x256x32_s5", "d
                         "d256x256x64_s2_16", "d256x256x32_s4_i16", "d256x256x32_s4_ip",
                         "d256x256x32_s4_isk", "d256x256x32_s4_w8i", "d256x256x32_s5_w8i",
                         "d256x256x64_s2_w8", "d128x128x64_s3", "d64x64x64_s4", "d64x32x128_s4",
-                        "d32x64x128_s4", "d256x192x32_s4_i16", SPLIT, PSTREAM, "d256x256x32_s4_i16w8"])
+                        "d32x64x128_s4", "d256x192x32_s4_i16", SPLIT, PSTREAM, "d256x256x32_s4_i16w8",
+                        "d128x384x32_s4_i16w8", SPLIT8])
 STAGED = ["g128x128x64", "g64x64x64"]
 COMBOS = [(i, o) for i in (wl.F16, wl.BF16) for o in (wl.F16, wl.BF16, wl.F32)]
 
@@ -60,7 +65,7 @@ def usable(cfg, N, transB, K=None, in_code=wl.F16):
     than one 256-wide column)."""
     if cfg in NK_ONLY and not transB:
         return False
-    if cfg == SPLIT and N <= 256:
+    if cfg in SPLITS and N <= 256:
         return False
     if cfg == PSTREAM and (N < 256 or K is None or K % 32 or K < 128):
         return False
@@ -74,11 +79,12 @@ def usable(cfg, N, transB, K=None, in_code=wl.F16):
 def run(A, B, M, N, K, in_code, out_code, transB, cfg=None, monkeypatch=None, poison=True):
     """Upload, call gemm_relu through the C-ABI, return exact binary64 values."""
     import torch
-    if cfg == SPLIT:
+    if cfg in SPLITS:
         monkeypatch.setenv("GEMM_RELU_SPLIT_COLS", "1")
     if cfg is not None:
-        if cfg != SPLIT:
-            monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", cfg)
+        force = SPLITS.get(cfg, cfg)
+        if force is not None:
+            monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", force)
         Ad, Bd = to_device(A, in_code, (M, K)), to_device(B, in_code, wl.b_shape(M, N, K, transB))
         Cd = out_tensor(M, N, out_code, float("nan") if poison else 0.0)
         assert gr.gemm_relu_plan(Ad, Bd, Cd, M, N, K, in_code, out_code, transB) == cfg

@@ -59,7 +59,7 @@ def test_workspace_size_of_the_skinny_workload():
 
 @pytest.mark.parametrize("M,N,K", [(8192, 8192, 8192), (128, 8192, 8192), (64, 8192, 256),
                                    (64, 100, 8192), (0, 64, 64), (64, 0, 64), (64, 8192, 0),
-                                   (4096, 7168, 4096)])
+                                   (4096, 7168, 4096), (4096, 4096, 4096)])
 def test_no_split_where_it_does_not_pay(M, N, K):
     """Large M, many tiles, short K, N below one (K,N) tile, empty: no split."""
     assert gr.gemm_relu_workspace_size(M, N, K, wl.F16, wl.F16, 0) == 0
