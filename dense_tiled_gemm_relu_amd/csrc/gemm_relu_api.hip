@@ -175,6 +175,11 @@ std::vector<SkWorkspace> g_ws;
 
 unsigned char* sk_workspace(int dev, hipStream_t st)
 {
+    // never under graph capture, even where the stream already has one: a
+    // captured graph replayed on another stream would share it with this one
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return nullptr;
     std::lock_guard<std::mutex> lk(g_ws_mu);
     int on_dev = 0;
     for (const SkWorkspace& w : g_ws) {
@@ -182,9 +187,6 @@ unsigned char* sk_workspace(int dev, hipStream_t st)
         on_dev += w.dev == dev;
     }
     if (on_dev >= kSkMaxPerDevice) return nullptr;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
-        return nullptr;
     // Relaxed capture mode for this thread around the allocation, so that a
     // graph capture in global mode on another thread is not invalidated by it.
     void* p = nullptr;

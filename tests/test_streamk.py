@@ -151,9 +151,10 @@ def test_streamk_two_streams(monkeypatch):
 
 
 def test_streamk_graph_capture(monkeypatch):
-    """Under capture on a stream with no workspace yet the call takes whole
-    tiles (nothing is allocated); once an eager call has set the workspace up,
-    a captured stream-K launch replays correctly, eager calls in between."""
+    """Under capture the call takes whole tiles (nothing is allocated, and no
+    per-stream workspace is shared with the graph), also once an eager call on
+    that stream has set one up; the captured launch replays correctly, eager
+    stream-K calls in between."""
     import torch
     monkeypatch.setenv("GEMM_RELU_FORCE_CONFIG", SK)
     monkeypatch.setenv("GEMM_RELU_SK_UNITS", "13")
