@@ -73,3 +73,38 @@ def test_matches_where_nothing_splits():
     got, want, plan = _pair(300, 260, 520, 1, 820)
     assert plan != SPLITK
     assert np.array_equal(got, want)
+
+
+@pytest.mark.gpu
+def test_captured_and_replayed():
+    """Captured into a graph (after an eager call has looked up the scratch's
+    address on this GPU) and replayed, with eager calls of another shape on
+    the same scratch and stream in between: every result as gemm_relu_ws's."""
+    import torch
+    M, N, K = 64, 4096, 8192
+    A = wl.uniform((M, K), 830, wl.F16)
+    B = wl.uniform((K, N), 831, wl.F16)
+    Ad, Bd = to_device(A, wl.F16, (M, K)), to_device(B, wl.F16, (K, N))
+    want, _, plan = _pair(M, N, K, 0, 830)
+    assert plan == SPLITK
+    M2, N2, K2 = 40, 2048, 4096
+    want2, _, _ = _pair(M2, N2, K2, 0, 840)
+    A2 = wl.uniform((M2, K2), 840, wl.F16)
+    B2 = wl.uniform((K2, N2), 841, wl.F16)
+    A2d, B2d = to_device(A2, wl.F16, (M2, K2)), to_device(B2, wl.F16, (K2, N2))
+    Cd, C2d = out_tensor(M, N, wl.F16, float("nan")), out_tensor(M2, N2, wl.F16, float("nan"))
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        gr.gemm_relu_noalloc(Ad, Bd, Cd, M, N, K, wl.F16, wl.F16, 0, s)
+    for _ in range(3):
+        with torch.cuda.stream(s):
+            Cd.fill_(float("nan"))
+            g.replay()
+            C2d.fill_(float("nan"))
+            gr.gemm_relu_noalloc(A2d, B2d, C2d, M2, N2, K2, wl.F16, wl.F16, 0, s)
+        s.synchronize()
+        assert np.array_equal(from_device(Cd), want)
+        assert np.array_equal(from_device(C2d), want2)
+    del g
