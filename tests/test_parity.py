@@ -384,6 +384,26 @@ def test_tail_shapes_every_config(cfg, M, N, K, monkeypatch):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("transB", [0, 1])
+def test_k_beyond_32_bit_copy_offsets(transB):
+    """K past 2^22: a tile's rows of A span more than 2^32 bytes of copy
+    offsets, so the plan takes the register-staged tile (64-bit addressing);
+    every output bit-exact (elements in {-1, 0, 1}: every partial sum below
+    2^24, exact in fp32)."""
+    M, N, K = 64, 64, (1 << 22) + 72
+    A = wl.integers((M, K), 1600 + transB, wl.F16, -1, 1)
+    B = wl.integers(wl.b_shape(M, N, K, transB), 1700 + transB, wl.F16, -1, 1)
+    Ad, Bd = to_device(A, wl.F16, (M, K)), to_device(B, wl.F16, wl.b_shape(M, N, K, transB))
+    Cd = out_tensor(M, N, wl.F32, float("nan"))
+    assert gr.gemm_relu_plan(Ad, Bd, Cd, M, N, K, wl.F16, wl.F32, transB).startswith("g")
+    gr.gemm_relu(Ad, Bd, Cd, M, N, K, wl.F16, wl.F32, transB)
+    import torch
+    torch.cuda.synchronize()
+    got = from_device(Cd)
+    del Ad, Bd
+    assert np.array_equal(got, oracle.gemm_relu_ref_matmul(A, B, M, N, K, wl.F16, transB))
+
+
 @pytest.mark.parametrize("off_a,off_b,off_c", [(1, 0, 0), (0, 1, 0), (0, 0, 1), (1, 3, 5)])
 @pytest.mark.parametrize("transB", [0, 1])
 def test_unaligned_pointers(off_a, off_b, off_c, transB):
